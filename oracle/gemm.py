@@ -1,0 +1,86 @@
+"""FP64 reference for the scaled FP8 GEMM and its tolerance.
+
+Test infrastructure only (see the package docstring).
+
+[MPT] §横断的知見 "FP8 への拡張": Transformer Engine runs only the GEMMs in FP8.
+[MPT] §横断的知見 "HPC ソルバーとの目的の分岐": tensor cores accumulate in FP32.
+The layer's output is Y = (Xq . Wq^T) / (sx * sw): the FP8 operands are decoded,
+multiplied and summed, and the inverse scales dequantise the sum. Here both
+operands are K-contiguous: A[m x k], B[n x k], C = A . B^T.
+
+Every product of two FP8 values is exact in float64 (at most 4 x 4 significant
+bits) and the float64 sum's error, at most (K-1) * 2**-53 * sum|a*b|, is far
+below the tolerance, so the float64 result stands for the exact one.
+
+Tolerance for a BF16 output y (widened to float64):
+    |y - y_ref| <= 2**-7 * |y_ref| + 1e-6 * sum_k |a_k * b_k|
+with a_k, b_k the dequantised operands (decoded code times inverse scale).
+2**-7 is BF16's epsilon ([MPT] §定義 precision table lists BF16's relative
+error as about 1e-2); the second term absorbs FP32 accumulation.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codec import _fmt, decode_table
+
+
+def _dec(codes, fmt) -> np.ndarray:
+    return decode_table(_fmt(fmt))[np.asarray(codes, dtype=np.uint8)]
+
+
+def gemm_ref(a_codes, a_fmt, b_codes, b_fmt, a_scale_inv, b_scale_inv) -> np.ndarray:
+    """y_ref = (dec(A) . dec(B)^T) * a_scale_inv * b_scale_inv, float64."""
+    A = _dec(a_codes, a_fmt)
+    B = _dec(b_codes, b_fmt)
+    return (A @ B.T) * float(a_scale_inv) * float(b_scale_inv)
+
+
+def gemm_abs_ref(a_codes, a_fmt, b_codes, b_fmt, a_scale_inv, b_scale_inv) -> np.ndarray:
+    """sum_k |a_k * b_k| for every output entry (the accumulation term of the bound)."""
+    A = np.abs(_dec(a_codes, a_fmt))
+    B = np.abs(_dec(b_codes, b_fmt))
+    return (A @ B.T) * abs(float(a_scale_inv)) * abs(float(b_scale_inv))
+
+
+def gemm_entry(a_codes, a_fmt, b_codes, b_fmt, a_scale_inv, b_scale_inv, i, j):
+    """One output entry and its bound term, for sampled checks at full size."""
+    a = _dec(np.asarray(a_codes)[i], a_fmt)
+    b = _dec(np.asarray(b_codes)[j], b_fmt)
+    sa, sb = float(a_scale_inv), float(b_scale_inv)
+    return float(np.dot(a, b)) * sa * sb, float(np.dot(np.abs(a), np.abs(b))) * abs(sa) * abs(sb)
+
+
+def gemm_bound(y_ref, abs_ref) -> np.ndarray:
+    return 2.0 ** -7 * np.abs(y_ref) + 1e-6 * np.asarray(abs_ref)
+
+
+def bf16_bits_to_f64(y_bits) -> np.ndarray:
+    y = np.asarray(y_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return y.view(np.float32).astype(np.float64)
+
+
+def gemm_check(y_bits, y_ref, abs_ref):
+    """Grade BF16 output bits against the reference.
+
+    Returns (ok, worst) where worst is the largest |y - y_ref| / bound over the
+    finite entries. Non-finite references (NaN or Inf codes among the operands)
+    must be matched exactly in kind.
+    """
+    y = bf16_bits_to_f64(y_bits)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    fin = np.isfinite(y_ref)
+    ok = True
+    if (~fin).any():
+        yr, yy = y_ref[~fin], y[~fin]
+        same = (np.isnan(yr) & np.isnan(yy)) | (yr == yy)
+        ok = bool(same.all())
+    bound = gemm_bound(y_ref[fin], np.asarray(abs_ref, dtype=np.float64)[fin])
+    err = np.abs(y[fin] - y_ref[fin])
+    if err.size == 0:
+        return ok, 0.0
+    if not np.isfinite(err).all():
+        return False, float("inf")
+    ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max())
+    return ok and worst <= 1.0, worst

@@ -1,0 +1,125 @@
+"""Pins for the oracle's FP64 GEMM and its tolerance.
+
+The checks use exact integer arithmetic on the codes' bit fields, Python
+integers, and a brute-force triple loop, so that a transposed operand, a wrong
+index, a dropped term or a wrong scale in the oracle fails one of them.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle.codec import FMT
+from oracle.gemm import (bf16_bits_to_f64, gemm_abs_ref, gemm_check, gemm_entry, gemm_ref)
+
+
+def _finite_codes(rng, shape, name):
+    top = FMT[name].max_code
+    c = rng.integers(0, top + 1, shape, dtype=np.int64)
+    sign = rng.integers(0, 2, shape, dtype=np.int64) << 7
+    return (c | sign).astype(np.uint8)
+
+
+def _int_value(code: int, name: str) -> int:
+    """Value of a finite code as an integer multiple of its format's smallest subnormal.
+
+    Written from the fields with integer arithmetic only: subnormal m, normal
+    (2**M + m) * 2**(e - 1).
+    """
+    f = FMT[name]
+    s = -1 if code & 0x80 else 1
+    e = (code >> f.man_bits) & ((1 << f.exp_bits) - 1)
+    m = code & ((1 << f.man_bits) - 1)
+    if e == 0:
+        return s * m
+    return s * (((1 << f.man_bits) + m) << (e - 1))
+
+
+UNIT = {"e4m3": Fraction(1, 2 ** 9), "e5m2": Fraction(1, 2 ** 16)}
+
+
+def test_e4m3_gemm_is_exact_integer_gemm():
+    rng = np.random.default_rng(0)
+    A = _finite_codes(rng, (37, 200), "e4m3")
+    B = _finite_codes(rng, (45, 200), "e4m3")
+    lut = np.array([_int_value(c, "e4m3") if (c & 0x7F) <= 0x7E else 0 for c in range(256)], np.int64)
+    exact = lut[A] @ lut[B].T                       # int64: |sum| < 2**50
+    ref = gemm_ref(A, "e4m3", B, "e4m3", 1.0, 1.0)
+    assert np.array_equal(ref, exact.astype(np.float64) * 2.0 ** -18)
+    assert np.array_equal(exact.astype(np.float64) * 2.0 ** -18, exact * 2.0 ** -18)
+
+
+def test_e5m2_by_e4m3_matches_python_integers():
+    rng = np.random.default_rng(1)
+    A = _finite_codes(rng, (5, 33), "e5m2")
+    B = _finite_codes(rng, (7, 33), "e4m3")
+    sa, sb = np.float32(0.375), np.float32(3.0)
+    ref = gemm_ref(A, "e5m2", B, "e4m3", sa, sb)
+    for i in range(5):
+        for j in range(7):
+            acc = sum(_int_value(int(A[i, k]), "e5m2") * _int_value(int(B[j, k]), "e4m3") for k in range(33))
+            want = Fraction(acc) * UNIT["e5m2"] * UNIT["e4m3"] * Fraction(0.375) * Fraction(3.0)
+            assert abs(Fraction(ref[i, j]) - want) <= abs(want) * Fraction(1, 2 ** 50)
+
+
+def test_triple_loop_non_square():
+    rng = np.random.default_rng(2)
+    from oracle.codec import decode
+    A = _finite_codes(rng, (3, 11), "e5m2")
+    B = _finite_codes(rng, (4, 11), "e4m3")
+    ref = gemm_ref(A, "e5m2", B, "e4m3", 2.0, 0.5)
+    for i in range(3):
+        for j in range(4):
+            s = 0.0
+            for k in range(11):
+                s += decode(A[i, k], "e5m2") * decode(B[j, k], "e4m3")
+            assert ref[i, j] == pytest.approx(s, rel=1e-15, abs=1e-300)
+            r, b = gemm_entry(A, "e5m2", B, "e4m3", 2.0, 0.5, i, j)
+            assert r == pytest.approx(ref[i, j], rel=1e-15, abs=1e-300)
+
+
+def _to_bf16_bits(y: np.ndarray) -> np.ndarray:
+    """Round float64 values to BF16 (via float32) for the tolerance checks."""
+    u = y.astype(np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def test_tolerance_accepts_rounded_and_rejects_wrong_results():
+    rng = np.random.default_rng(3)
+    K = 512
+    A = _finite_codes(rng, (16, K), "e4m3")
+    B = _finite_codes(rng, (24, K), "e4m3")
+    sa, sb = np.float32(1 / 64), np.float32(1 / 32)
+    ref = gemm_ref(A, "e4m3", B, "e4m3", sa, sb)
+    absr = gemm_abs_ref(A, "e4m3", B, "e4m3", sa, sb)
+    ok, worst = gemm_check(_to_bf16_bits(ref), ref, absr)
+    assert ok and worst < 0.6
+    # dropping the last k term
+    ref_drop = gemm_ref(A[:, :-1], "e4m3", B[:, :-1], "e4m3", sa, sb)
+    big = np.abs(ref - ref_drop) > 2 * (2.0 ** -7 * np.abs(ref) + 1e-6 * absr)
+    assert big.any()
+    assert not gemm_check(_to_bf16_bits(ref_drop), ref, absr)[0]
+    # transposed operand pairing (B . A^T has a different shape; use a square case)
+    Bs = _finite_codes(rng, (16, K), "e4m3")
+    ref_s = gemm_ref(A, "e4m3", Bs, "e4m3", sa, sb)
+    abs_s = gemm_abs_ref(A, "e4m3", Bs, "e4m3", sa, sb)
+    assert not gemm_check(_to_bf16_bits(ref_s.T), ref_s, abs_s)[0]
+    # a wrong scale (one inverse scale applied twice)
+    assert not gemm_check(_to_bf16_bits(ref * float(sa)), ref, absr)[0]
+    # sign flip
+    assert not gemm_check(_to_bf16_bits(-ref), ref, absr)[0]
+
+
+def test_nan_codes_propagate_and_are_graded():
+    A = np.array([[0x7F, 0x38]], np.uint8)      # NaN, 1.0 (E4M3)
+    B = np.array([[0x38, 0x38]], np.uint8)
+    ref = gemm_ref(A, "e4m3", B, "e4m3", 1.0, 1.0)
+    assert np.isnan(ref).all()
+    nan_bits = np.array([[0x7FC0]], np.uint16)
+    absr = gemm_abs_ref(A, "e4m3", B, "e4m3", 1.0, 1.0)
+    assert gemm_check(nan_bits, ref, absr)[0]
+    assert not gemm_check(np.array([[0x3F80]], np.uint16), ref, absr)[0]
+
+
+def test_bf16_output_widening():
+    assert bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0000], np.uint16)).tolist() == [1.0, -2.0, 0.0]
