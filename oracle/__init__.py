@@ -37,17 +37,19 @@ test under tests/):
   * encode rounds to nearest, ties to even, and saturates: every |v| >= fmax,
     +-Inf included, maps to the largest finite code of that sign; NaN maps to
     sign | 0x7F; FP8 subnormals are produced; a zero result keeps its sign;
+  * the sign of a NaN product x * s is sign(x) xor sign(s) (IEEE 754 leaves
+    it open);
   * OCP variants: E4M3 has bias 7, no infinities and one NaN code per sign;
     E5M2 has bias 15 and IEEE-style Inf/NaN;
   * amax is max |x| in fp32; any NaN gives the canonical NaN 0x7FC00000.
 """
 from .codec import (FMT, FP8Format, decode, decode_table, encode, encode_scalar,
                     bf16_to_f32)
-from .recipe import (amax, cast, DelayedScaling, max_nan, update_scale)
+from .recipe import (amax, cast, DelayedScaling, max_nan, primed_scale, update_scale)
 from .gemm import gemm_ref, gemm_abs_ref, gemm_bound, gemm_check, gemm_entry
 
 __all__ = [
     "FMT", "FP8Format", "decode", "decode_table", "encode", "encode_scalar", "bf16_to_f32",
-    "amax", "cast", "DelayedScaling", "max_nan", "update_scale",
+    "amax", "cast", "DelayedScaling", "max_nan", "primed_scale", "update_scale",
     "gemm_ref", "gemm_abs_ref", "gemm_bound", "gemm_check", "gemm_entry",
 ]

@@ -48,10 +48,23 @@ def amax(x, dtype: str = "f32") -> np.float32:
 
 
 def cast(x, scale, fmt, dtype: str = "f32") -> np.ndarray:
-    """q = enc(fp32(x) * s): one binary32 multiply (round to nearest even), then one FP8 rounding."""
+    """q = enc(fp32(x) * s): one binary32 multiply (round to nearest even), then one FP8 rounding.
+
+    IEEE 754 leaves the sign of a NaN result open; it is read here as the sign
+    the product would have, sign(x) xor sign(s), so a NaN product's code is
+    0x7F with that sign.
+    """
     xf = _as_f32(x, dtype)
-    prod = xf * np.float32(scale)        # numpy float32 multiply: IEEE binary32, RNE, no flushing
-    return encode(prod, fmt)
+    s = np.float32(scale)
+    with np.errstate(invalid="ignore", over="ignore"):
+        prod = xf * s                    # numpy float32 multiply: IEEE binary32, RNE, no flushing
+    q = encode(prod, fmt)
+    nan = np.isnan(prod)
+    if nan.any():
+        sx = (np.ascontiguousarray(xf).view(np.uint32) >> np.uint32(31)).astype(np.uint8)
+        ss = np.uint8(int(np.array([s], np.float32).view(np.uint32)[0]) >> 31)
+        q[nan] = np.uint8(0x7F) | ((sx[nan] ^ ss) << np.uint8(7))
+    return q
 
 
 def update_scale(history: np.ndarray, scale: np.float32, scale_inv: np.float32,

@@ -229,3 +229,17 @@ def test_max_nan():
     assert max_nan([]) == 0.0
     assert bits(max_nan([np.float32(1), CANONICAL_NAN])) == 0x7FC00000
     assert max_nan([F32(-1), F32(2)]) == 2.0
+
+
+def test_nan_product_sign_rule():
+    """A NaN product's code carries sign(x) xor sign(s); Inf * 0 and NaN scales included."""
+    neg_nan = np.array([0xFFC00000], np.uint32).view(np.float32)[0]
+    x = np.array([np.nan, neg_nan, np.inf, -np.inf, 1.0, -2.0], F32)
+    q = cast(x, F32(0.0), "e4m3")
+    assert q.tolist() == [0x7F, 0xFF, 0x7F, 0xFF, 0x00, 0x80]
+    q = cast(x, F32(-0.0), "e5m2")
+    assert q.tolist() == [0xFF, 0x7F, 0xFF, 0x7F, 0x80, 0x00]
+    q = cast(x, F32(np.nan), "e4m3")
+    assert q.tolist() == [0x7F, 0xFF, 0x7F, 0xFF, 0x7F, 0xFF]
+    q = cast(x, F32(-2.0), "e4m3")
+    assert q.tolist() == [0xFF, 0x7F, 0xFE, 0x7E, 0xC0, 0x48]
