@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-tensor-scaled FP8 linear layer's hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: the
+fused amax+cast of X and of W with the delayed scales, the scaled FP8 GEMM
+into BF16, and the two scale updates, all through the C-ABI library. The
+default workload is the 7B-class MLP up-projection (X[4096x4096] BF16 with
+0.1% outliers x20, W[11008x4096] BF16 N(0, 0.02); GEMM M=4096, N=11008,
+K=4096; amax history 1024, margin 0).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mlp7b_up_fwd]
+
+Prints one JSON line. `value` is the step's GEMM FLOPs divided by the
+measured step time (TFLOP/s, higher is better); `roofline` describes the
+dominant kernel (the GEMM) from HIP events recorded around every launch in the
+timed region; `components` gives the cast kernels' GB/s against HBM;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # dense
+PEAK_FP8_MFMA_TFLOPS = 5000.0   # dense
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mlp7b_up_fwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, min_seconds: float = 10.0):
+    """The oracle's whole step (amax, cast, FP64 GEMM, update) on the workload, repeated
+    until at least min_seconds of CPU work have been timed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    g = w.gemms[0]
+    x, wt = inp["X"], inp["W"]
+    reps, total = 0, 0.0
+    while total < min_seconds and reps < 20:
+        t0 = time.perf_counter()
+        rx = oracle.DelayedScaling("e4m3", w.history_len, w.margin)
+        rw = oracle.DelayedScaling("e4m3", w.history_len, w.margin)
+        qx = rx.cast_step(x, "bf16")
+        qw = rw.cast_step(wt, "bf16")
+        y = oracle.gemm_ref(qx, "e4m3", qw, "e4m3", rx.scale_inv, rw.scale_inv)
+        rx.update()
+        rw.update()
+        total += time.perf_counter() - t0
+        reps += 1
+        del y
+    flops = 2.0 * g.m * g.n * g.k
+    return {"value": flops * reps / total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full oracle steps (amax, cast of X and W, FP64 GEMM {g.m}x{g.n}x{g.k}, "
+                      f"update) in {total:.1f} s; elementwise stages single-threaded, BLAS on {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); every box has one MI355X and this "
+              "path does not shard across GPUs.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import fp8_mixed_precision_cast_amd as fp8
+    from fp8_mixed_precision_cast_amd.linear import plan_from_workload
+
+    w = wl.BY_NAME[args.workload]
+    if w.steps != 1:
+        raise SystemExit("bench.py times the single-step workloads")
+    info = fp8.fp8mp_device_info()
+    inp = wl.load(w.name)
+    dinp = {k: torch.from_numpy(v.view("int16")).cuda() for k, v in inp.items()}
+    plan = plan_from_workload(w)
+    stream = torch.cuda.current_stream()
+    plan.prime(dinp)
+    for _ in range(args.warmup):
+        plan.step(dinp)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record(stream)
+        plan.cast_all(dinp)
+        e[1].record(stream)
+        plan.gemm_all()
+        e[2].record(stream)
+        plan.update_all()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    step_s = (t1 - t0) / K
+    cast_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    upd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+
+    flops = plan.gemm_flops()
+    n_gemm = len(plan.gemms)
+    gemm_launch_ms = gemm_ms / n_gemm
+    flops_per_launch = flops / n_gemm
+    gemm_tflops = flops_per_launch / (gemm_launch_ms * 1e-3) / 1e12
+    cast_bytes = plan.cast_bytes(dinp)
+    cast_gbps = cast_bytes / (cast_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            t = json.load(f)
+        traffic = t.get(w.name, {}).get("gemm_bytes_per_launch")
+
+    g = w.gemms[0]
+    out = {
+        "metric": "FP8 scaled-GEMM TFLOP/s (7B MLP shape) + amax/cast GB/s, % of roofline",
+        "value": round(flops / step_s / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 operands; bf16 MFMA (exact on FP8 values), f32 accumulate, bf16 out",
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": g.m, "n": g.n, "k": g.k, "x": "bf16 N(0,1)+0.1% x20",
+                   "w": "bf16 N(0,0.02)", "history_len": w.history_len, "margin": w.margin,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_MFMA_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "gemm_fp8_kernel (bf16 MFMA on widened FP8)",
+                     "frac_of_fp8_mfma_peak": round(gemm_tflops / PEAK_FP8_MFMA_TFLOPS, 4)},
+        "components": {
+            "gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(gemm_tflops, 2),
+            "cast_ms": round(cast_ms, 4), "cast_bytes": cast_bytes, "cast_gbps": round(cast_gbps, 1),
+            "cast_frac_of_hbm": round(cast_gbps / PEAK_HBM_GBPS, 4),
+            "scale_update_ms": round(upd_ms, 4),
+        },
+        "device": info,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

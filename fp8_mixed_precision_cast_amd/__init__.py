@@ -1,0 +1,193 @@
+"""Python binding of libfp8mp: the per-tensor-scaled FP8 linear layer on gfx950.
+
+Argument marshalling only. Every step of the path runs in the HIP library
+(``libfp8mp.so``, built in-tree by ``fp8_mixed_precision_cast_amd.build``);
+torch supplies device memory and the current stream. The functions carry the
+C-ABI names and raise ``Fp8mpError`` on any non-OK status. There is no CPU
+fallback: without the built library, importing the binding's entry points
+raises.
+
+Tensors:
+  * sources: 2-D float32 or bfloat16 (or int16/uint16 BF16 bit patterns), unit
+    column stride; the row stride is the leading dimension;
+  * FP8 codes: uint8 tensors; scales, inverse scales and amax: float32 tensors
+    (their first element is used; a history's first element is its amax slot);
+  * GEMM output: bfloat16 (or int16/uint16) tensor.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+__all__ = [
+    "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
+    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8mp_status_string",
+    "fp8mp_device_info", "exported_symbols", "DelayedScalingState",
+]
+
+E4M3, E5M2 = 0, 1
+F32, BF16 = 0, 1
+FORMATS = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+_lib = None
+
+
+class Fp8mpError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {fp8mp_status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfp8mp.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfp8mp.so from this package directory (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fp8_mixed_precision_cast_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.fp8_amax_cast.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, i64, vp, i64, vp, vp]
+    lib.fp8_amax_cast.restype = ctypes.c_int
+    lib.fp8_scale_update.argtypes = [vp, i32, ctypes.c_int, i32, vp, vp, vp]
+    lib.fp8_scale_update.restype = ctypes.c_int
+    lib.fp8_scaled_gemm.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp,
+                                    i64, vp]
+    lib.fp8_scaled_gemm.restype = ctypes.c_int
+    lib.fp8mp_status_string.argtypes = [ctypes.c_int]
+    lib.fp8mp_status_string.restype = ctypes.c_char_p
+    lib.fp8mp_device_info.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+    lib.fp8mp_device_info.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> list:
+    """Function names declared in include/fp8mp.h."""
+    with open(os.path.join(_ROOT, "include", "fp8mp.h")) as f:
+        text = f.read()
+    return re.findall(r"^\s*(?:fp8mp_status|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def fp8mp_status_string(status: int) -> str:
+    return load_library().fp8mp_status_string(int(status)).decode()
+
+
+def fp8mp_device_info() -> str:
+    buf = ctypes.create_string_buffer(256)
+    st = load_library().fp8mp_device_info(buf, 256)
+    if st != 0:
+        raise Fp8mpError(st, "fp8mp_device_info")
+    return buf.value.decode()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(getattr(stream, "cuda_stream", stream))
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(st: int, call: str) -> None:
+    if st != 0:
+        raise Fp8mpError(st, call)
+
+
+def _src_dtype(x) -> int:
+    import torch
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    raise TypeError(f"source dtype {x.dtype} is not float32 or bfloat16")
+
+
+def _rows_ld(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.shape[0], t.shape[1], max(t.stride(0), t.shape[1])
+
+
+def fp8_amax_cast(x, fmt, scale=None, q=None, q_t=None, amax=None, stream=None) -> None:
+    """One pass over x: *amax = max(*amax, max|x|), q = enc(x*scale), q_t = q^T."""
+    rows, cols, ld_x = _rows_ld(x, "x")
+    ld_q = _rows_ld(q, "q")[2] if q is not None else 0
+    ld_qt = _rows_ld(q_t, "q_t")[2] if q_t is not None else 0
+    if q is not None and tuple(q.shape) != (rows, cols):
+        raise ValueError("q must be rows x cols")
+    if q_t is not None and tuple(q_t.shape) != (cols, rows):
+        raise ValueError("q_t must be cols x rows")
+    st = load_library().fp8_amax_cast(_ptr(x), _src_dtype(x), rows, cols, ld_x, FORMATS[fmt], _ptr(scale),
+                                      _ptr(q), ld_q, _ptr(q_t), ld_qt, _ptr(amax), _stream(stream))
+    _check(st, "fp8_amax_cast")
+
+
+def fp8_scale_update(history, fmt, margin, scale, scale_inv, stream=None) -> None:
+    """Delayed-scaling update of (scale, scale_inv) from history, then roll the history."""
+    st = load_library().fp8_scale_update(_ptr(history), int(history.numel()), FORMATS[fmt], int(margin),
+                                         _ptr(scale), _ptr(scale_inv), _stream(stream))
+    _check(st, "fp8_scale_update")
+
+
+def fp8_scaled_gemm(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None) -> None:
+    """c = (a . b^T) * a_scale_inv * b_scale_inv; a[m,k], b[n,k] uint8 codes; c[m,n] BF16."""
+    m, k, lda = _rows_ld(a, "a")
+    n, kb, ldb = _rows_ld(b, "b")
+    if kb != k:
+        raise ValueError("a and b must share k")
+    mc, nc, ldc = _rows_ld(c, "c")
+    if (mc, nc) != (m, n):
+        raise ValueError("c must be m x n")
+    st = load_library().fp8_scaled_gemm(_ptr(a), FORMATS[a_fmt], lda, _ptr(b), FORMATS[b_fmt], ldb, m, n, k,
+                                        _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(c), ldc, _stream(stream))
+    _check(st, "fp8_scaled_gemm")
+
+
+class DelayedScalingState:
+    """Device buffers of one tensor's recipe state: history[L], scale, scale_inv.
+
+    Cold start: history 0, scale 1, scale_inv 1. ``state_dict``/``load_state_dict``
+    copy the three buffers (the checkpointable FP8 state).
+    """
+
+    def __init__(self, fmt, history_len: int = 1024, margin: int = 0, device="cuda"):
+        import torch
+        self.fmt = FORMATS[fmt]
+        self.margin = int(margin)
+        self.history = torch.zeros(history_len, dtype=torch.float32, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.scale_inv = torch.ones(1, dtype=torch.float32, device=device)
+
+    @property
+    def amax_slot(self):
+        return self.history[0:1]
+
+    def cast(self, x, q=None, q_t=None, record: bool = True, stream=None) -> None:
+        fp8_amax_cast(x, self.fmt, self.scale, q, q_t, self.amax_slot if record else None, stream)
+
+    def update(self, stream=None) -> None:
+        fp8_scale_update(self.history, self.fmt, self.margin, self.scale, self.scale_inv, stream)
+
+    def state_dict(self):
+        return {"amax_history": self.history.clone(), "scale": self.scale.clone(),
+                "scale_inv": self.scale_inv.clone()}
+
+    def load_state_dict(self, sd) -> None:
+        self.history.copy_(sd["amax_history"])
+        self.scale.copy_(sd["scale"])
+        self.scale_inv.copy_(sd["scale_inv"])

@@ -1,0 +1,158 @@
+// C-ABI front end: argument validation, the gfx950 check and dispatch.
+//
+// Validation runs on the host before anything touches the device, so a bad
+// argument returns FP8MP_ERR_INVALID_ARG even on a machine without a GPU.
+// The only device query is the per-device arch check, cached after its first
+// success. [TE] §FP8非対応GPUでのフォールバック実装 checks the device's capability at
+// run time and falls back to 16-bit; here there is no fallback path: a device
+// other than gfx950 gets FP8MP_ERR_WRONG_ARCH.
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unchecked, 1 = gfx950, 2 = another arch. CU count cached alongside.
+std::atomic<int> g_arch_state[kMaxDevices];
+std::atomic<int> g_num_cus[kMaxDevices];
+
+bool valid_format(int f) { return f == FP8MP_E4M3 || f == FP8MP_E5M2; }
+bool valid_dtype(int d) { return d == FP8MP_F32 || d == FP8MP_BF16; }
+
+fp8mp_status query_device(int* dev_out, hipDeviceProp_t* props_out) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return FP8MP_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8MP_ERR_HIP;
+  *dev_out = dev;
+  if (props_out && hipGetDeviceProperties(props_out, dev) != hipSuccess) return FP8MP_ERR_HIP;
+  return FP8MP_OK;
+}
+
+// Ensures the current device is gfx950; returns its CU count through *cus.
+fp8mp_status check_device(int* cus) {
+  int dev = 0;
+  fp8mp_status st = query_device(&dev, nullptr);
+  if (st != FP8MP_OK) return st;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int s = g_arch_state[dev].load(std::memory_order_acquire);
+    if (s == 1) {
+      *cus = g_num_cus[dev].load(std::memory_order_relaxed);
+      return FP8MP_OK;
+    }
+    if (s == 2) return FP8MP_ERR_WRONG_ARCH;
+  }
+  hipDeviceProp_t props;
+  if (hipGetDeviceProperties(&props, dev) != hipSuccess) return FP8MP_ERR_HIP;
+  const bool ok = std::strncmp(props.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    g_num_cus[dev].store(props.multiProcessorCount, std::memory_order_relaxed);
+    g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+  }
+  *cus = props.multiProcessorCount;
+  return ok ? FP8MP_OK : FP8MP_ERR_WRONG_ARCH;
+}
+
+fp8mp_status from_hip(hipError_t e) { return e == hipSuccess ? FP8MP_OK : FP8MP_ERR_HIP; }
+
+bool is_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q, uint8_t* q_t,
+                           int64_t ld_qt, float* amax, hipStream_t stream) {
+  if (!valid_dtype(x_dtype) || !valid_format(fmt)) return FP8MP_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0) return FP8MP_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return FP8MP_OK;
+  if (x == nullptr || ld_x < cols) return FP8MP_ERR_INVALID_ARG;
+  if ((q || q_t) && scale == nullptr) return FP8MP_ERR_INVALID_ARG;
+  if (q && ld_q < cols) return FP8MP_ERR_INVALID_ARG;
+  if (q_t && ld_qt < rows) return FP8MP_ERR_INVALID_ARG;
+  if (!is_aligned(x, x_dtype == FP8MP_BF16 ? 2 : 4)) return FP8MP_ERR_INVALID_ARG;
+  if (amax && !is_aligned(amax, 4)) return FP8MP_ERR_INVALID_ARG;
+  if (scale && !is_aligned(scale, 4)) return FP8MP_ERR_INVALID_ARG;
+  // every row/column index product must stay inside int64
+  if (rows > (INT64_MAX / 8) / ld_x) return FP8MP_ERR_UNSUPPORTED;
+  if (q_t && cols > (INT64_MAX / 8) / ld_qt) return FP8MP_ERR_UNSUPPORTED;
+  if (!q && !q_t && !amax) return FP8MP_OK;
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  return from_hip(fp8mp::launch_amax_cast(x, x_dtype, rows, cols, ld_x, fmt, scale, q, ld_q, q_t, ld_qt,
+                                          amax, cus, stream));
+}
+
+fp8mp_status fp8_scale_update(float* amax_history, int32_t history_len, fp8mp_format fmt, int32_t margin,
+                              float* scale, float* scale_inv, hipStream_t stream) {
+  if (!valid_format(fmt)) return FP8MP_ERR_INVALID_ARG;
+  if (amax_history == nullptr || scale == nullptr || scale_inv == nullptr) return FP8MP_ERR_INVALID_ARG;
+  if (history_len < 1 || margin < 0) return FP8MP_ERR_INVALID_ARG;
+  if (!is_aligned(amax_history, 4) || !is_aligned(scale, 4) || !is_aligned(scale_inv, 4))
+    return FP8MP_ERR_INVALID_ARG;
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  return from_hip(fp8mp::launch_scale_update(amax_history, history_len, fmt, margin, scale, scale_inv,
+                                             stream));
+}
+
+fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
+                             fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                             const float* a_scale_inv, const float* b_scale_inv, uint16_t* c, int64_t ldc,
+                             hipStream_t stream) {
+  if (!valid_format(a_fmt) || !valid_format(b_fmt)) return FP8MP_ERR_INVALID_ARG;
+  if (m < 0 || n < 0 || k < 0) return FP8MP_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return FP8MP_OK;
+  if (c == nullptr || a_scale_inv == nullptr || b_scale_inv == nullptr) return FP8MP_ERR_INVALID_ARG;
+  if (k > 0 && (a == nullptr || b == nullptr)) return FP8MP_ERR_INVALID_ARG;
+  if (lda < k || ldb < k || ldc < n) return FP8MP_ERR_INVALID_ARG;
+  if (!is_aligned(a_scale_inv, 4) || !is_aligned(b_scale_inv, 4)) return FP8MP_ERR_INVALID_ARG;
+  if (k % 16 != 0) return FP8MP_ERR_UNSUPPORTED;
+  if (k > 0 && (lda % 16 != 0 || ldb % 16 != 0 || !is_aligned(a, 16) || !is_aligned(b, 16)))
+    return FP8MP_ERR_UNSUPPORTED;
+  if (!is_aligned(c, 2)) return FP8MP_ERR_INVALID_ARG;
+  if (k > (int64_t)1 << 30) return FP8MP_ERR_UNSUPPORTED;
+  if (m > (INT64_MAX / 8) / lda || n > (INT64_MAX / 8) / ldb || m > (INT64_MAX / 8) / ldc)
+    return FP8MP_ERR_UNSUPPORTED;
+  if (((m + 127) / 128) * ((n + 127) / 128) > 0x7FFFFFFF) return FP8MP_ERR_UNSUPPORTED;
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  return from_hip(fp8mp::launch_scaled_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv,
+                                            c, ldc, cus, stream));
+}
+
+const char* fp8mp_status_string(fp8mp_status status) {
+  switch (status) {
+    case FP8MP_OK: return "ok";
+    case FP8MP_ERR_INVALID_ARG: return "invalid argument";
+    case FP8MP_ERR_UNSUPPORTED: return "unsupported shape, layout or alignment";
+    case FP8MP_ERR_NO_DEVICE: return "no HIP device";
+    case FP8MP_ERR_WRONG_ARCH: return "device is not gfx950";
+    case FP8MP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+fp8mp_status fp8mp_device_info(char* buf, size_t len) {
+  if (buf == nullptr || len == 0) return FP8MP_ERR_INVALID_ARG;
+  buf[0] = '\0';
+  int dev = 0;
+  hipDeviceProp_t props;
+  fp8mp_status st = query_device(&dev, &props);
+  if (st != FP8MP_OK) return st;
+  std::snprintf(buf, len, "arch=%s cus=%d formats=e4m3:448,e5m2:57344", props.gcnArchName,
+                props.multiProcessorCount);
+  return std::strncmp(props.gcnArchName, "gfx950", 6) == 0 ? FP8MP_OK : FP8MP_ERR_WRONG_ARCH;
+}
+
+}  // extern "C"

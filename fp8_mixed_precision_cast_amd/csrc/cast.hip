@@ -1,0 +1,297 @@
+// Fused amax + scaled saturating FP8 cast (+ transposed copy) for gfx950.
+//
+// [TE] §NVIDIA Transformer EngineとFP8混合精度とは: the scaling factor follows each
+// tensor's observed value range. Delayed scaling lets the range (amax) of step
+// t be recorded in the same pass that casts step t with the scale of step t-1,
+// so one read of the source suffices.
+//
+// The work is HBM-bound: per element it reads the source (2 B BF16, 4 B fp32)
+// and writes one code (plus one for the transposed copy). Every kernel streams
+// 16-byte vectors, reduces amax in registers as unsigned bit patterns of |x|,
+// and commits one atomic per workgroup.
+#include "common.h"
+
+namespace fp8mp {
+namespace {
+
+constexpr int kFlatBlock = 256;
+constexpr int kTileBlock = 256;
+constexpr int kTileRows = 256;   // 32 row groups of 8
+constexpr int kTileCols = 64;    // 8 column groups of 8
+
+// ---------------------------------------------------------------------------
+// Contiguous BF16 source, 16 elements (two 16-byte loads) -> one 16-byte store.
+template <int FMT, bool HAS_Q>
+__global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16(const uint4* __restrict__ x,
+                                                             uint4* __restrict__ q, int64_t nchunk,
+                                                             const float* __restrict__ scale,
+                                                             float* __restrict__ amax) {
+  const float s = HAS_Q ? *scale : 1.0f;
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; i < nchunk; i += 2 * stride) {
+    const int64_t j = i + stride;
+    const bool two = j < nchunk;
+    uint4 a0 = x[2 * i], a1 = x[2 * i + 1];
+    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = b0;
+    if (two) { b0 = x[2 * j]; b1 = x[2 * j + 1]; }
+    acc = amax_bf16x2(acc, a0.x); acc = amax_bf16x2(acc, a0.y);
+    acc = amax_bf16x2(acc, a0.z); acc = amax_bf16x2(acc, a0.w);
+    acc = amax_bf16x2(acc, a1.x); acc = amax_bf16x2(acc, a1.y);
+    acc = amax_bf16x2(acc, a1.z); acc = amax_bf16x2(acc, a1.w);
+    acc = amax_bf16x2(acc, b0.x); acc = amax_bf16x2(acc, b0.y);
+    acc = amax_bf16x2(acc, b0.z); acc = amax_bf16x2(acc, b0.w);
+    acc = amax_bf16x2(acc, b1.x); acc = amax_bf16x2(acc, b1.y);
+    acc = amax_bf16x2(acc, b1.z); acc = amax_bf16x2(acc, b1.w);
+    if constexpr (HAS_Q) {
+      uint4 o;
+      o.x = enc4_bf16<FMT>(a0.x, a0.y, s); o.y = enc4_bf16<FMT>(a0.z, a0.w, s);
+      o.z = enc4_bf16<FMT>(a1.x, a1.y, s); o.w = enc4_bf16<FMT>(a1.z, a1.w, s);
+      q[i] = o;
+      if (two) {
+        o.x = enc4_bf16<FMT>(b0.x, b0.y, s); o.y = enc4_bf16<FMT>(b0.z, b0.w, s);
+        o.z = enc4_bf16<FMT>(b1.x, b1.y, s); o.w = enc4_bf16<FMT>(b1.z, b1.w, s);
+        q[j] = o;
+      }
+    }
+  }
+  if (amax) block_amax_commit<kFlatBlock>(bf16x2_acc_to_f32_bits(acc), amax);
+}
+
+// Contiguous fp32 source, 16 elements (four 16-byte loads) -> one 16-byte store.
+template <int FMT, bool HAS_Q>
+__global__ __launch_bounds__(kFlatBlock) void cast_flat_f32(const float4* __restrict__ x,
+                                                            uint4* __restrict__ q, int64_t nchunk,
+                                                            const float* __restrict__ scale,
+                                                            float* __restrict__ amax) {
+  const float s = HAS_Q ? *scale : 1.0f;
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; i < nchunk; i += stride) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = x[4 * i + u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc = amax_f32(acc, v[u].x); acc = amax_f32(acc, v[u].y);
+      acc = amax_f32(acc, v[u].z); acc = amax_f32(acc, v[u].w);
+    }
+    if constexpr (HAS_Q) {
+      uint4 o;
+      o.x = enc4<FMT>(v[0].x, v[0].y, v[0].z, v[0].w, s);
+      o.y = enc4<FMT>(v[1].x, v[1].y, v[1].z, v[1].w, s);
+      o.z = enc4<FMT>(v[2].x, v[2].y, v[2].z, v[2].w, s);
+      o.w = enc4<FMT>(v[3].x, v[3].y, v[3].z, v[3].w, s);
+      q[i] = o;
+    }
+  }
+  if (amax) block_amax_commit<kFlatBlock>(acc, amax);
+}
+
+// ---------------------------------------------------------------------------
+// Any layout, one element per iteration over the row-major index range
+// [start, end). Serves strided views, fp32 with a transposed copy, unaligned
+// pointers and the tails of the flat kernels.
+template <int FMT, int DT>
+__global__ __launch_bounds__(kFlatBlock) void cast_generic(const void* __restrict__ xv, int64_t cols,
+                                                           int64_t ld_x, int64_t start, int64_t end,
+                                                           const float* __restrict__ scale,
+                                                           uint8_t* __restrict__ q, int64_t ld_q,
+                                                           uint8_t* __restrict__ q_t, int64_t ld_qt,
+                                                           float* __restrict__ amax) {
+  const float s = (q || q_t) ? *scale : 1.0f;
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
+  for (int64_t e = start + (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; e < end; e += stride) {
+    const int64_t r = e / cols, c = e - r * cols;
+    float v;
+    if constexpr (DT == FP8MP_BF16) {
+      v = __uint_as_float((uint32_t)static_cast<const uint16_t*>(xv)[r * ld_x + c] << 16);
+    } else {
+      v = static_cast<const float*>(xv)[r * ld_x + c];
+    }
+    acc = amax_f32(acc, v);
+    if (q || q_t) {
+      const uint8_t code = enc1<FMT>(v, s);
+      if (q) q[r * ld_q + c] = code;
+      if (q_t) q_t[c * ld_qt + r] = code;
+    }
+  }
+  if (amax) block_amax_commit<kFlatBlock>(canonical_nan(acc), amax);
+}
+
+// ---------------------------------------------------------------------------
+// BF16 source in 256 x 64 tiles; each thread owns an 8 x 8 block: eight
+// 16-byte row loads, eight 8-byte row stores of q, and after an in-register
+// 8 x 8 byte transpose, eight 8-byte row stores of q_t.
+
+// 4 x 4 byte transpose: input dword i holds row i (byte j = column j); output
+// dword j holds column j (byte i = row i). v_perm_b32 picks any four of the
+// eight bytes {hi:lo}.
+__device__ __forceinline__ void tr4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                    uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3) {
+  const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+  const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+  const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);  // r2.b0 r3.b0 r2.b1 r3.b1
+  const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);  // r2.b2 r3.b2 r2.b3 r3.b3
+  c0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);                  // r0.b0 r1.b0 r2.b0 r3.b0
+  c1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);                  // column 1
+  c2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);                  // column 2
+  c3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);                  // column 3
+}
+
+template <int FMT, bool HAS_Q, bool HAS_QT>
+__global__ __launch_bounds__(kTileBlock) void cast_tile_bf16(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ld_q,
+    uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ amax, int64_t tiles_c,
+    int64_t ntiles, int vec_ok) {
+  const float s = (HAS_Q || HAS_QT) ? *scale : 1.0f;
+  const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  uint32_t acc = 0;        // packed BF16 magnitudes (vector path)
+  uint32_t acc32 = 0;      // fp32 magnitudes (edge path)
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
+    const int64_t r0 = tr * kTileRows + rg * 8, c0 = tc * kTileCols + cg * 8;
+    const bool full = vec_ok && (tr * kTileRows + kTileRows <= rows) && (tc * kTileCols + kTileCols <= cols);
+    if (full) {
+      uint4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + c0);
+      uint32_t lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc = amax_bf16x2(acc, v[i].x); acc = amax_bf16x2(acc, v[i].y);
+        acc = amax_bf16x2(acc, v[i].z); acc = amax_bf16x2(acc, v[i].w);
+        lo[i] = enc4_bf16<FMT>(v[i].x, v[i].y, s);
+        hi[i] = enc4_bf16<FMT>(v[i].z, v[i].w, s);
+      }
+      if constexpr (HAS_Q) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0) = make_uint2(lo[i], hi[i]);
+      }
+      if constexpr (HAS_QT) {
+        uint32_t a[4], b[4], c[4], d[4];
+        tr4(lo[0], lo[1], lo[2], lo[3], a[0], a[1], a[2], a[3]);   // cols 0-3, rows 0-3
+        tr4(lo[4], lo[5], lo[6], lo[7], b[0], b[1], b[2], b[3]);   // cols 0-3, rows 4-7
+        tr4(hi[0], hi[1], hi[2], hi[3], c[0], c[1], c[2], c[3]);   // cols 4-7, rows 0-3
+        tr4(hi[4], hi[5], hi[6], hi[7], d[0], d[1], d[2], d[3]);   // cols 4-7, rows 4-7
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          *reinterpret_cast<uint2*>(q_t + (c0 + j) * ld_qt + r0) = make_uint2(a[j], b[j]);
+          *reinterpret_cast<uint2*>(q_t + (c0 + 4 + j) * ld_qt + r0) = make_uint2(c[j], d[j]);
+        }
+      }
+    } else {
+      for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + i;
+        if (r >= rows) break;
+        for (int j = 0; j < 8; ++j) {
+          const int64_t c = c0 + j;
+          if (c >= cols) break;
+          const float vv = __uint_as_float((uint32_t)x[r * ld_x + c] << 16);
+          acc32 = amax_f32(acc32, vv);
+          if constexpr (HAS_Q || HAS_QT) {
+            const uint8_t code = enc1<FMT>(vv, s);
+            if constexpr (HAS_Q) q[r * ld_q + c] = code;
+            if constexpr (HAS_QT) q_t[c * ld_qt + r] = code;
+          }
+        }
+      }
+    }
+  }
+  if (amax) {
+    uint32_t m = bf16x2_acc_to_f32_bits(acc);
+    m = m > acc32 ? m : acc32;
+    block_amax_commit<kTileBlock>(m, amax);
+  }
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+template <int FMT, int DT>
+hipError_t launch_generic(const void* x, int64_t cols, int64_t ld_x, int64_t start, int64_t end,
+                          const float* scale, uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                          float* amax, int num_cus, hipStream_t stream) {
+  const int64_t n = end - start;
+  if (n <= 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>(cdiv(n, kFlatBlock), (int64_t)num_cus * 8);
+  hipLaunchKernelGGL((cast_generic<FMT, DT>), dim3(grid), dim3(kFlatBlock), 0, stream, x, cols, ld_x,
+                     start, end, scale, q, ld_q, q_t, ld_qt, amax);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
+                      const float* scale, uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                      float* amax, int num_cus, hipStream_t stream) {
+  const int64_t numel = rows * cols;
+  const int esize = dt == FP8MP_BF16 ? 2 : 4;
+  const bool contiguous = ld_x == cols && (q == nullptr || ld_q == cols) && q_t == nullptr;
+
+  if (contiguous && aligned(x, 16) && (q == nullptr || aligned(q, 16))) {
+    const int64_t nchunk = numel / 16;
+    if (nchunk > 0) {
+      const int grid = (int)std::min<int64_t>(cdiv(nchunk, kFlatBlock), (int64_t)num_cus * 8);
+      if (dt == FP8MP_BF16) {
+        if (q) hipLaunchKernelGGL((cast_flat_bf16<FMT, true>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                                  (const uint4*)x, (uint4*)q, nchunk, scale, amax);
+        else hipLaunchKernelGGL((cast_flat_bf16<FMT, false>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                                (const uint4*)x, (uint4*)nullptr, nchunk, scale, amax);
+      } else {
+        if (q) hipLaunchKernelGGL((cast_flat_f32<FMT, true>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                                  (const float4*)x, (uint4*)q, nchunk, scale, amax);
+        else hipLaunchKernelGGL((cast_flat_f32<FMT, false>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                                (const float4*)x, (uint4*)nullptr, nchunk, scale, amax);
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    // the last numel % 16 elements
+    if (dt == FP8MP_BF16)
+      return launch_generic<FMT, FP8MP_BF16>(x, cols, ld_x, nchunk * 16, numel, scale, q, ld_q, q_t,
+                                             ld_qt, amax, num_cus, stream);
+    return launch_generic<FMT, FP8MP_F32>(x, cols, ld_x, nchunk * 16, numel, scale, q, ld_q, q_t, ld_qt,
+                                          amax, num_cus, stream);
+  }
+
+  if (dt == FP8MP_BF16) {
+    const bool vec_ok = aligned(x, 16) && (ld_x * esize) % 16 == 0 &&
+                        (q == nullptr || (aligned(q, 8) && ld_q % 8 == 0)) &&
+                        (q_t == nullptr || (aligned(q_t, 8) && ld_qt % 8 == 0));
+    const int64_t tiles_r = cdiv(rows, kTileRows), tiles_c = cdiv(cols, kTileCols);
+    const int64_t ntiles = tiles_r * tiles_c;
+    const int grid = (int)std::min<int64_t>(ntiles, (int64_t)num_cus * 4);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+#define FP8MP_TILE(HQ, HQT)                                                                       \
+  hipLaunchKernelGGL((cast_tile_bf16<FMT, HQ, HQT>), dim3(grid), dim3(kTileBlock), 0, stream, xb, \
+                     rows, cols, ld_x, scale, q, ld_q, q_t, ld_qt, amax, tiles_c, ntiles, (int)vec_ok)
+    if (q && q_t) FP8MP_TILE(true, true);
+    else if (q) FP8MP_TILE(true, false);
+    else if (q_t) FP8MP_TILE(false, true);
+    else FP8MP_TILE(false, false);
+#undef FP8MP_TILE
+    return hipGetLastError();
+  }
+  return launch_generic<FMT, FP8MP_F32>(x, cols, ld_x, 0, numel, scale, q, ld_q, q_t, ld_qt, amax,
+                                        num_cus, stream);
+}
+
+}  // namespace
+
+hipError_t launch_amax_cast(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
+                            fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q,
+                            uint8_t* q_t, int64_t ld_qt, float* amax, int num_cus,
+                            hipStream_t stream) {
+  if (fmt == FP8MP_E4M3)
+    return launch_fmt<FP8MP_E4M3>(x, dt, rows, cols, ld_x, scale, q, ld_q, q_t, ld_qt, amax, num_cus,
+                                  stream);
+  return launch_fmt<FP8MP_E5M2>(x, dt, rows, cols, ld_x, scale, q, ld_q, q_t, ld_qt, amax, num_cus,
+                                stream);
+}
+
+}  // namespace fp8mp

@@ -1,0 +1,116 @@
+"""One step of a per-tensor-scaled FP8 linear layer, as a sequence of C-ABI calls.
+
+[TE] §基本的なFP8トレーニングコードの構成: the FP8 linear layer replaces nn.Linear and
+runs inside an FP8 recipe context; [TE] §動的スケーリングとFP8レシピの設定: HYBRID uses
+E4M3 in the forward pass and E5M2 in the backward pass. A step is:
+
+  1. for every operand tensor: one fused pass that casts it with the scale of
+     the previous step and records its amax into history[0] (and, when an
+     operand is needed K-contiguous the other way round, writes the transposed
+     codes in the same pass);
+  2. every GEMM, dequantised by the inverse scales those codes were made with;
+  3. the delayed-scaling update of every tensor's scale.
+
+The plan owns its device buffers (allocated once, through torch); a step
+allocates nothing and never synchronises.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import DelayedScalingState, fp8_amax_cast, fp8_scale_update, fp8_scaled_gemm
+
+
+@dataclass(frozen=True)
+class OperandSpec:
+    name: str
+    shape: Tuple[int, int]
+    fmt: str                  # "e4m3" or "e5m2"
+    transposed: bool = False  # also produce the transposed codes
+    plain: bool = True        # produce the row-major codes
+
+
+@dataclass(frozen=True)
+class GemmOp:
+    name: str
+    a: str
+    a_transposed: bool
+    b: str
+    b_transposed: bool
+
+
+class LayerPlan:
+    def __init__(self, operands: Sequence[OperandSpec], gemms: Sequence[GemmOp], history_len: int = 1024,
+                 margin: int = 0, device: str = "cuda"):
+        self.operands = {o.name: o for o in operands}
+        self.gemms = list(gemms)
+        self.state: Dict[str, DelayedScalingState] = {}
+        self.q: Dict[str, Optional[torch.Tensor]] = {}
+        self.qt: Dict[str, Optional[torch.Tensor]] = {}
+        self.out: Dict[str, torch.Tensor] = {}
+        for o in operands:
+            r, c = o.shape
+            self.state[o.name] = DelayedScalingState(o.fmt, history_len, margin, device)
+            self.q[o.name] = torch.empty(r, c, dtype=torch.uint8, device=device) if o.plain else None
+            self.qt[o.name] = torch.empty(c, r, dtype=torch.uint8, device=device) if o.transposed else None
+        self._gemm_args = []
+        for g in self.gemms:
+            a = self.qt[g.a] if g.a_transposed else self.q[g.a]
+            b = self.qt[g.b] if g.b_transposed else self.q[g.b]
+            if a is None or b is None:
+                raise ValueError(f"gemm {g.name}: operand layout not produced")
+            if a.shape[1] != b.shape[1]:
+                raise ValueError(f"gemm {g.name}: K mismatch {tuple(a.shape)} vs {tuple(b.shape)}")
+            c = torch.empty(a.shape[0], b.shape[0], dtype=torch.bfloat16, device=device)
+            self.out[g.name] = c
+            sa, sb = self.state[g.a], self.state[g.b]
+            self._gemm_args.append((a, sa.fmt, b, sb.fmt, sa.scale_inv, sb.scale_inv, c))
+
+    def prime(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
+        """An amax-only pass over every operand, then one update (single-shot workloads)."""
+        for name, st in self.state.items():
+            fp8_amax_cast(inputs[name], st.fmt, None, None, None, st.amax_slot, stream)
+        for st in self.state.values():
+            st.update(stream)
+
+    def cast_all(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
+        for name, st in self.state.items():
+            st.cast(inputs[name], self.q[name], self.qt[name], True, stream)
+
+    def gemm_all(self, stream=None) -> None:
+        for a, af, b, bf, sa, sb, c in self._gemm_args:
+            fp8_scaled_gemm(a, af, b, bf, sa, sb, c, stream)
+
+    def update_all(self, stream=None) -> None:
+        for st in self.state.values():
+            fp8_scale_update(st.history, st.fmt, st.margin, st.scale, st.scale_inv, stream)
+
+    def step(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
+        self.cast_all(inputs, stream)
+        self.gemm_all(stream)
+        self.update_all(stream)
+
+    def gemm_flops(self) -> int:
+        return sum(2 * a.shape[0] * b.shape[0] * a.shape[1] for a, _, b, _, _, _, _ in self._gemm_args)
+
+    def cast_bytes(self, inputs: Dict[str, torch.Tensor]) -> int:
+        """Algorithmic bytes of the casts: source read once, each code layout written once."""
+        total = 0
+        for name, o in self.operands.items():
+            n = o.shape[0] * o.shape[1]
+            total += n * inputs[name].element_size() + n * (int(o.plain) + int(o.transposed))
+        return total
+
+
+def plan_from_workload(w, device: str = "cuda") -> LayerPlan:
+    """A LayerPlan from a workload description with the attributes
+    ``tensors`` (``name``, ``shape``), ``formats``, ``transposed``, ``gemms``
+    (``name``, ``a``, ``a_transposed``, ``b``, ``b_transposed``), ``history_len``
+    and ``margin``."""
+    ops = [OperandSpec(t.name, tuple(t.shape), w.formats[t.name], t.name in w.transposed, True)
+           for t in w.tensors]
+    gemms = [GemmOp(g.name, g.a, g.a_transposed, g.b, g.b_transposed) for g in w.gemms]
+    return LayerPlan(ops, gemms, w.history_len, w.margin, device)

@@ -1,0 +1,153 @@
+/*
+ * fp8mp: the per-tensor-scaled FP8 linear layer of mixed-precision training,
+ * as a C-ABI library for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages):
+ *   [TE]  「AI：NVIDIA Transformer EngineとFP8混合精度の実装ガイド｜環境構築からベンチマークまで」
+ *   [TRT] 「NVIDIA TensorRTによるFP8量子化：高性能推論エンジンの実現」
+ *   [MPT] 「混合精度訓練」 (notes.yuuk.io wiki)
+ *
+ * The layer's hot path: record each tensor's amax while casting it to FP8 with
+ * the scale from the previous step (delayed scaling), update the scale from the
+ * amax history, and multiply the FP8 operands with FP32 accumulation into a
+ * BF16 output dequantised by the inverse scales.
+ *
+ * Conventions for every call:
+ *   - All data pointers are device pointers owned by the caller. The library
+ *     allocates nothing and keeps no state other than a per-device arch check.
+ *   - Work is enqueued on `stream` (NULL = the legacy default stream). No call
+ *     synchronises the stream or copies data to the host; scales and amaxes
+ *     stay on the device.
+ *   - Arguments are validated on the host before anything is launched. A bad
+ *     argument returns FP8MP_ERR_INVALID_ARG and touches nothing.
+ *   - Layouts are row-major with a leading dimension (elements between rows).
+ *   - FP8 codes are bytes: OCP E4M3 (bias 7, largest 448, NaN = S.1111.111,
+ *     no Inf) or OCP E5M2 (bias 15, largest 57344, IEEE Inf/NaN).
+ *   - Calls are thread-safe. Errors of kernels that fault surface at the
+ *     caller's next synchronisation, as usual in HIP.
+ */
+#ifndef FP8MP_H
+#define FP8MP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* FP8 formats. [TE] §NVIDIA Transformer EngineとFP8混合精度とは: E4M3 has 4 exponent
+ * and 3 mantissa bits and suits the forward pass, E5M2 has 5 and 2 and suits
+ * the backward pass. [MPT] §定義 precision table: largest values 448 and 57344. */
+typedef enum { FP8MP_E4M3 = 0, FP8MP_E5M2 = 1 } fp8mp_format;
+
+/* Source element types of the cast: fp32, or BF16 passed as 16-bit patterns. */
+typedef enum { FP8MP_F32 = 0, FP8MP_BF16 = 1 } fp8mp_dtype;
+
+typedef enum {
+  FP8MP_OK = 0,
+  FP8MP_ERR_INVALID_ARG = 1,  /* NULL where required, negative size, ld too small, bad enum */
+  FP8MP_ERR_UNSUPPORTED = 2,  /* a well-formed request the kernels do not handle (e.g. K % 16 != 0) */
+  FP8MP_ERR_NO_DEVICE = 3,    /* no HIP device visible */
+  FP8MP_ERR_WRONG_ARCH = 4,   /* current device is not gfx950 */
+  FP8MP_ERR_HIP = 5           /* a HIP call or kernel launch failed */
+} fp8mp_status;
+
+/*
+ * fp8_amax_cast: amax reduction fused with the scaled saturating cast, and
+ * optionally the transposed copy of the codes, in one pass over x.
+ *
+ * [TE] §NVIDIA Transformer EngineとFP8混合精度とは: each tensor's value range is
+ * watched and its scaling factor adjusted so values fit FP8's narrow range;
+ * [TE] §動的スケーリングとFP8レシピの設定: the recipe keeps an amax history.
+ *
+ *   x       rows x cols source, element stride ld_x (>= cols), type x_dtype.
+ *   scale   one fp32 on the device: the scale in force (the previous step's).
+ *   q       rows x cols codes, ld_q (>= cols): q[r][c] = enc(fp32(x[r][c]) * scale).
+ *   q_t     cols x rows codes, ld_qt (>= rows): q_t[c][r] = q[r][c].
+ *   amax    one fp32 on the device, updated as *amax = max(*amax, max |x|).
+ *
+ * enc rounds to nearest (ties to even), saturates every |v| >= the format's
+ * largest value, +-Inf included, to the largest finite code of that sign, maps
+ * NaN to sign|0x7F, keeps FP8 subnormals and the sign of zero. The product
+ * fp32(x) * scale is one IEEE binary32 multiply (no flushing of subnormals).
+ * amax is exact; any NaN in x makes *amax the canonical NaN 0x7FC00000. *amax
+ * must hold +0..+Inf or that NaN on entry (fp8_scale_update leaves history[0]
+ * at +0).
+ *
+ * q, q_t and amax may each be NULL; scale may be NULL only when q and q_t are
+ * both NULL (an amax-only pass). rows or cols == 0 is a no-op returning OK.
+ * Any alignment is accepted; 16-byte aligned rows take the vector path.
+ */
+fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols,
+                           int64_t ld_x, fp8mp_format fmt, const float* scale,
+                           uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                           float* amax, hipStream_t stream);
+
+/*
+ * fp8_scale_update: the delayed-scaling update of one tensor's recipe state.
+ *
+ * [TE] §動的スケーリングとFP8レシピの設定: DelayedScaling with margin (default 0;
+ * larger means fewer overflows, more underflows) and amax_history_len (default
+ * 1024; the history the scale is computed from). [MPT] §横断的知見 on tensor
+ * scaling: delayed per-tensor scaling uses past amaxes.
+ *
+ *   amax_history  history_len fp32 values; entry 0 holds this step's amax.
+ *   scale, scale_inv  one fp32 each, read and written.
+ *
+ * a = max over all entries (NaN propagates). If a is finite and > 0:
+ *   s' = fp32(fp32(fmax / a) * 2^-margin)   (IEEE division, exact power-of-two step)
+ * and if s' and fp32(1 / s') are finite and > 0 they replace scale and
+ * scale_inv; otherwise both are held. Then the history rolls by one entry
+ * (entry i takes entry i-1, entry 0 becomes +0). history_len >= 1, margin >= 0.
+ * One workgroup; stream-ordered after the casts that wrote entry 0.
+ */
+fp8mp_status fp8_scale_update(float* amax_history, int32_t history_len, fp8mp_format fmt,
+                              int32_t margin, float* scale, float* scale_inv,
+                              hipStream_t stream);
+
+/*
+ * fp8_scaled_gemm: C = (A . B^T) * a_scale_inv * b_scale_inv with FP32
+ * accumulation and a BF16 result (round to nearest even).
+ *
+ * [MPT] §横断的知見 "FP8 への拡張": only the GEMMs run in FP8; §"HPC ソルバーとの目的の分岐":
+ * tensor cores accumulate in FP32. [TE] §NVIDIA Transformer EngineとFP8混合精度とは:
+ * FP8 doubles tensor-core throughput over 16-bit types.
+ *
+ *   a   m x k codes in a_fmt, leading dimension lda (>= k), K contiguous.
+ *   b   n x k codes in b_fmt, leading dimension ldb (>= k), K contiguous.
+ *   a_scale_inv, b_scale_inv  one fp32 each on the device.
+ *   c   m x n BF16 (16-bit patterns), leading dimension ldc (>= n).
+ *
+ * Format pairs: (E4M3, E4M3) for the forward pass; (E5M2, E4M3) for dgrad and
+ * wgrad of the HYBRID recipe ([TE] §動的スケーリングとFP8レシピの設定); (E4M3, E5M2)
+ * and (E5M2, E5M2) are also accepted. k must be a multiple of 16, a and b
+ * 16-byte aligned and lda, ldb multiples of 16 (else FP8MP_ERR_UNSUPPORTED);
+ * c needs only its natural 2-byte alignment and any ldc >= n.
+ * m, n arbitrary; m == 0 or n == 0 is a no-op; k == 0 writes zeros (times the
+ * inverse scales). NaN codes propagate to NaN outputs.
+ */
+fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
+                             const uint8_t* b, fp8mp_format b_fmt, int64_t ldb,
+                             int64_t m, int64_t n, int64_t k,
+                             const float* a_scale_inv, const float* b_scale_inv,
+                             uint16_t* c, int64_t ldc, hipStream_t stream);
+
+/* A static, human-readable name of a status code. Never NULL. */
+const char* fp8mp_status_string(fp8mp_status status);
+
+/*
+ * Writes "arch=<gcnArchName> cus=<n> formats=e4m3:448,e5m2:57344" for the
+ * current device into buf (NUL-terminated, truncated to len). Logs which
+ * precision mode runs, as [TE] §FP8非対応GPUでのフォールバック実装 advises.
+ * Returns FP8MP_ERR_NO_DEVICE without a device, FP8MP_ERR_WRONG_ARCH (with the
+ * text still written) on a device other than gfx950.
+ */
+fp8mp_status fp8mp_device_info(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MP_H */

@@ -1,0 +1,95 @@
+"""The C-ABI library without a GPU: it loads, exports what the header declares, and
+rejects bad arguments on the host before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_mixed_precision_cast_amd as fp8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, NO_DEVICE = 0, 1, 2, 3
+P = ctypes.c_void_p
+A16 = P(4096)   # a fake, 16-byte aligned address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fp8.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = fp8.exported_symbols()
+    assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8mp_status_string",
+                     "fp8mp_device_info"]
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {fp8.lib_path()}").read()
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert fp8.fp8mp_status_string(s)
+    assert fp8.fp8mp_status_string(99) == "unknown status"
+
+
+def test_cast_argument_validation(lib):
+    f = lib.fp8_amax_cast
+    assert f(None, 1, 4, 4, 4, 0, A16, A16, 4, None, 0, None, None) == INVALID   # x NULL
+    assert f(A16, 7, 4, 4, 4, 0, A16, A16, 4, None, 0, None, None) == INVALID    # bad dtype
+    assert f(A16, 1, 4, 4, 4, 9, A16, A16, 4, None, 0, None, None) == INVALID    # bad format
+    assert f(A16, 1, -1, 4, 4, 0, A16, A16, 4, None, 0, None, None) == INVALID   # negative rows
+    assert f(A16, 1, 4, 4, 3, 0, A16, A16, 4, None, 0, None, None) == INVALID    # ld_x < cols
+    assert f(A16, 1, 4, 4, 4, 0, None, A16, 4, None, 0, None, None) == INVALID   # q without scale
+    assert f(A16, 1, 4, 4, 4, 0, A16, A16, 3, None, 0, None, None) == INVALID    # ld_q < cols
+    assert f(A16, 1, 4, 8, 8, 0, A16, None, 0, A16, 3, None, None) == INVALID    # ld_qt < rows
+    assert f(P(4097), 1, 4, 4, 4, 0, A16, A16, 4, None, 0, None, None) == INVALID  # misaligned bf16
+    assert f(A16, 1, 0, 4, 4, 0, None, None, 0, None, 0, None, None) == OK       # empty
+    assert f(A16, 1, 4, 4, 4, 0, None, None, 0, None, 0, None, None) == OK       # nothing requested
+
+
+def test_scale_update_argument_validation(lib):
+    f = lib.fp8_scale_update
+    assert f(None, 4, 0, 0, A16, A16, None) == INVALID
+    assert f(A16, 0, 0, 0, A16, A16, None) == INVALID
+    assert f(A16, 4, 0, -1, A16, A16, None) == INVALID
+    assert f(A16, 4, 5, 0, A16, A16, None) == INVALID
+    assert f(A16, 4, 0, 0, None, A16, None) == INVALID
+
+
+def test_gemm_argument_validation(lib):
+    f = lib.fp8_scaled_gemm
+    args = lambda **kw: [kw.get("a", A16), kw.get("af", 0), kw.get("lda", 32), kw.get("b", A16), kw.get("bf", 0),
+                         kw.get("ldb", 32), kw.get("m", 4), kw.get("n", 8), kw.get("k", 32),
+                         kw.get("sa", A16), kw.get("sb", A16), kw.get("c", A16), kw.get("ldc", 8), None]
+    assert f(*args(af=3)) == INVALID
+    assert f(*args(m=-1)) == INVALID
+    assert f(*args(lda=16)) == INVALID
+    assert f(*args(ldc=4)) == INVALID
+    assert f(*args(c=None)) == INVALID
+    assert f(*args(sa=None)) == INVALID
+    assert f(*args(k=24, lda=32, ldb=32)) == UNSUPPORTED       # k % 16
+    assert f(*args(lda=40)) == UNSUPPORTED                      # lda % 16
+    assert f(*args(a=P(4096 + 8))) == UNSUPPORTED               # a not 16-byte aligned
+    assert f(*args(c=P(4097))) == INVALID                       # c not 2-byte aligned
+    assert f(*args(m=0)) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a device")
+def test_valid_calls_without_device_report_no_device(lib):
+    assert lib.fp8_scale_update(A16, 4, 0, 0, A16, A16, None) == NO_DEVICE
+    assert lib.fp8_amax_cast(A16, 1, 4, 4, 4, 0, A16, A16, 4, None, 0, A16, None) == NO_DEVICE
+    assert lib.fp8_scaled_gemm(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE
+    buf = ctypes.create_string_buffer(64)
+    assert lib.fp8mp_device_info(buf, 64) == NO_DEVICE
+
+
+def test_binding_has_no_cpu_fallback():
+    """The binding's entry points go through the library only."""
+    import inspect
+    src = inspect.getsource(fp8)
+    assert "oracle" not in src and "numpy" not in src

@@ -1,0 +1,112 @@
+"""GPU parity of fp8_scaled_gemm against the oracle's FP64 GEMM, within the stated bound.
+
+|y - y_ref| <= 2**-7 |y_ref| + 1e-6 * sum_k |a_k b_k| elementwise, over shapes
+that span several tiles and ragged edges in M, N and K, every format pair,
+strided operands, NaN propagation and the degenerate sizes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.codec import FMT
+from tests.gpu_util import banner, dev, f32, host, require_gpu
+
+import fp8_mixed_precision_cast_amd as fp8
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")]
+
+
+def _codes(rng, shape, fmt, spread=None):
+    """Finite codes; `spread` limits the exponent range so sums do not cancel to nothing."""
+    top = FMT[fmt].max_code
+    lo = 0 if spread is None else max(0, top - spread)
+    c = rng.integers(lo, top + 1, shape, dtype=np.int64)
+    sign = rng.integers(0, 2, shape, dtype=np.int64) << 7
+    return (c | sign).astype(np.uint8)
+
+
+def _check(a, af, b, bf, sa, sb, y_bits, tag):
+    ref = oracle.gemm_ref(a, af, b, bf, sa, sb)
+    absr = oracle.gemm_abs_ref(a, af, b, bf, sa, sb)
+    ok, worst = oracle.gemm_check(y_bits, ref, absr)
+    assert ok, f"{tag}: worst |err|/bound = {worst}"
+    return worst
+
+
+def _run(a, af, b, bf, sa, sb, ldc_pad=0):
+    m, n = a.shape[0], b.shape[0]
+    c_store = torch.zeros(m, n + ldc_pad, dtype=torch.int16, device="cuda")
+    c = c_store[:, :n]
+    fp8.fp8_scaled_gemm(dev(a), af, dev(b), bf, f32(sa), f32(sb), c)
+    out = host(c_store)
+    if ldc_pad:
+        assert not out[:, n:].any(), "wrote past n"
+    return out[:, :n]
+
+
+SHAPES = [(128, 128, 128), (256, 256, 256), (300, 200, 272), (257, 129, 16), (1, 1, 16), (17, 300, 48),
+          (640, 384, 1024), (129, 257, 4096 + 16)]
+
+
+@pytest.mark.parametrize("af,bf", PAIRS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemm_shapes(af, bf, shape):
+    require_gpu()
+    m, n, k = shape
+    rng = np.random.default_rng(m * 31 + n * 7 + k)
+    a = _codes(rng, (m, k), af, spread=40)
+    b = _codes(rng, (n, k), bf, spread=40)
+    sa, sb = np.float32(1 / 3.0), np.float32(0.0625)
+    banner("gemm", af, bf, shape)
+    y = _run(a, af, b, bf, sa, sb, ldc_pad=8)
+    _check(a, af, b, bf, sa, sb, y, f"{af}x{bf} {shape}")
+
+
+def test_gemm_all_codes_and_strided_operands():
+    require_gpu()
+    rng = np.random.default_rng(5)
+    m, n, k = 192, 160, 512
+    a_full = _codes(rng, (m, k + 64), "e5m2")
+    b_full = _codes(rng, (n, k + 32), "e4m3")
+    ad, bd = dev(a_full)[:, 16:16 + k], dev(b_full)[:, 32:32 + k]
+    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    banner("gemm-strided")
+    fp8.fp8_scaled_gemm(ad, "e5m2", bd, "e4m3", f32(2.0 ** -10), f32(3.0), c)
+    _check(a_full[:, 16:16 + k], "e5m2", b_full[:, 32:32 + k], "e4m3", 2.0 ** -10, 3.0, host(c), "strided")
+
+
+def test_gemm_nan_inputs_and_degenerate_sizes():
+    require_gpu()
+    rng = np.random.default_rng(6)
+    a = _codes(rng, (64, 128), "e4m3", spread=20)
+    b = _codes(rng, (80, 128), "e4m3", spread=20)
+    a[3, 77] = 0x7F
+    b[10, 5] = 0xFF
+    banner("gemm-nan")
+    y = _run(a, "e4m3", b, "e4m3", 1.0, 1.0)
+    _check(a, "e4m3", b, "e4m3", 1.0, 1.0, y, "nan")
+    yf = oracle.gemm.bf16_bits_to_f64(y)
+    assert np.isnan(yf[3]).all() and np.isnan(yf[:, 10]).all()
+    # k == 0: the empty sum, times the inverse scales
+    banner("gemm-k0")
+    c = torch.full((5, 8), 7, dtype=torch.int16, device="cuda")
+    e = torch.zeros(5, 0, dtype=torch.uint8, device="cuda")
+    fp8.fp8_scaled_gemm(e, "e4m3", torch.zeros(8, 0, dtype=torch.uint8, device="cuda"), "e4m3",
+                        f32(1.0), f32(1.0), c)
+    assert not host(c).any()
+    # m == 0 is a no-op
+    fp8.fp8_scaled_gemm(torch.zeros(0, 16, dtype=torch.uint8, device="cuda"), "e4m3",
+                        torch.zeros(8, 16, dtype=torch.uint8, device="cuda"), "e4m3", f32(1.0), f32(1.0),
+                        torch.zeros(0, 8, dtype=torch.int16, device="cuda"))
+
+
+def test_gemm_rejects_unsupported_k():
+    require_gpu()
+    a = torch.zeros(16, 24, dtype=torch.uint8, device="cuda")
+    c = torch.zeros(16, 16, dtype=torch.int16, device="cuda")
+    with pytest.raises(fp8.Fp8mpError) as ei:
+        fp8.fp8_scaled_gemm(a, "e4m3", a, "e4m3", f32(1.0), f32(1.0), c)
+    assert ei.value.status == 2
