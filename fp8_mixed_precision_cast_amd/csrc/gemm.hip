@@ -9,15 +9,25 @@
 //
 //   precise (default): each lane widens its FP8 fragments to BF16 in
 //     registers (v_cvt_scalef32_pk_bf16_{fp8,bf8} with scale 1, exact for
-//     every code) and runs v_mfma_f32_16x16x32_bf16, whose products are exact
+//     every code) and runs v_mfma_f32_32x32x16_bf16, whose products are exact
 //     and whose sums carry about 22 bits relative to sum|a*b| per instruction.
-//     This meets the stated tolerance at every K of the workloads.
+//     (On gfx950 the 16x16x32 BF16 form issues at half the 32x32x16 rate.)
 //   fp8: v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales, twice the
 //     MFMA rate, but gfx950 reduces each 128-product dot with only about 17
 //     bits relative to its largest product (measured: up to 7e-5 of sum|a*b|
 //     per instruction), which exceeds the tolerance on outputs that cancel.
 //
-// The per-tensor scales are applied once in the epilogue.
+// Tiling: 256 x 256 output tiles, K in steps of 128 bytes, 512 threads as 2 x 4
+// waves of 128 x 64 (two waves per SIMD). Tiles of A and B are copied global -> LDS directly
+// (global_load_lds_dwordx4, no VGPR staging) into a double buffer, so the
+// next K step streams in while this one is multiplied. The 16-byte chunk c
+// of tile row r sits in LDS at chunk slot c ^ (r & 7): a wave's copy stays
+// coalesced and the fragment reads of eight consecutive rows hit eight
+// distinct bank groups. Tiles are numbered so that each XCD (workgroups are
+// dealt to the eight XCDs round-robin) owns a contiguous run of tile ids, and
+// runs are walked in groups of kGroupM tile rows so concurrently resident
+// tiles share A and B panels in that XCD's L2. The per-tensor scales are
+// applied once in the epilogue.
 #include "common.h"
 
 namespace fp8mp {
@@ -25,11 +35,20 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kThreads = 256;   // 4 waves, 2 x 2, each 64 x 64 of C
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kThreads = 512;             // 8 waves, two per SIMD
+constexpr int kWavesN = 4;                // waves laid out 2 (M) x 4 (N)
+constexpr int kWM = 128, kWN = 64;        // wave tile
+constexpr int kFM = kWM / 16, kFN = kWN / 16;   // 16 x 16 blocks per wave (FP8 MFMA path)
+constexpr int kPM = kWM / 32, kPN = kWN / 32;   // 32 x 32 blocks per wave (BF16 MFMA path)
+constexpr int kTileBytes = kBM * kBK;     // one operand's K step in LDS: 32 KB
+constexpr int kSlabs = kTileBytes / (kThreads * 16);   // 1 KB LDS slabs each wave fills per operand
+constexpr int kGroupM = 4;
+constexpr int kXcds = 8;
 
 // MFMA operand-format selectors of the f8f6f4 family.
 template <int FMT> struct MfmaFmt;
@@ -60,124 +79,242 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float y) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// LDS tile: 128 rows x 128 bytes; the 16-byte chunk c of row r sits at chunk
-// position c ^ (r & 7), so eight consecutive rows read at one logical chunk
-// hit eight distinct bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+// Byte offset of logical chunk c of tile row r inside one operand's LDS tile.
+// A 16-lane phase of a 16-byte fragment read touches rows r0 .. r0+15 at one
+// logical chunk; with 64 four-byte banks, a 256-byte bank window holds two
+// rows, so the slot of row r is c ^ (r & 7) ^ ((r >> 3) & 1): the sixteen
+// rows then fall into sixteen distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4); }
+
+// Tile id -> (tile row, tile column); a bijection on [0, tm * tn).
+__device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& bm, int& bn) {
+  const int ntiles = tm * tn;
+  const int per = ntiles / kXcds, rem = ntiles % kXcds;
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  const int t = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int group = kGroupM * tn;
+  const int first_m = (t / group) * kGroupM;
+  const int gm = min(tm - first_m, kGroupM);
+  const int in = t % group;
+  bm = first_m + in % gm;
+  bn = in / gm;
+}
+
+// Per-thread part of one operand's copy: this thread fills, in each of its
+// kSlabs 1 KB LDS slabs (slab = kSlabs * wave + j, 64 lanes x 16 B, lane-ordered),
+// chunk slot p = 8 * row + (lane & 7) of tile row row = 8 * slab + lane / 8,
+// i.e. logical chunk c = (lane & 7) ^ (row & 7) ^ (slab & 1) (the inverse of
+// swz). Since 8 * slab is a multiple of 8, row & 7 = (lane >> 3) & 7, and
+// slab & 1 = j & 1 (kSlabs is even): c takes one value on even slabs, c ^ 1
+// on odd ones.
+struct TileCopy {
+  __amdgpu_buffer_rsrc_t rsrc;   // whole operand; loads past its end return 0
+  uint32_t base;                 // byte offset of row 8 * kSlabs * wave + lane / 8 at k = 0
+  uint32_t stride8;              // 8 rows
+  uint32_t kc0, kc1;             // c * 16 on even and odd slabs
+  uint32_t row_ok;               // bit j: slab j's row exists
+};
+static_assert(kSlabs % 2 == 0, "slab parity must equal j parity");
+
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // above any operand (operands are < 2^31 bytes)
+
+__device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int64_t row0, int64_t rows, int64_t K,
+                                              int wave, int lane) {
+  TileCopy t;
+  const uint32_t bytes = (uint32_t)((rows - 1) * ld + K);
+  t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)G, (short)0, (int)bytes, 0x00020000);
+  const int r = wave * 8 * kSlabs + (lane >> 3);
+  const int c = (lane & 7) ^ ((lane >> 3) & 7);
+  t.kc0 = (uint32_t)c * 16u;
+  t.kc1 = (uint32_t)(c ^ 1) * 16u;
+  t.base = (uint32_t)((row0 + r) * ld);
+  t.stride8 = (uint32_t)(8 * ld);
+  t.row_ok = 0;
+#pragma unroll
+  for (int j = 0; j < kSlabs; ++j) t.row_ok |= (row0 + r + 8 * j < rows ? 1u : 0u) << j;
+  return t;
+}
+
+// Copies K step [k0, k0 + 128) of one operand into an LDS tile. Chunks of
+// missing rows or past K are read out of range, which stores zeros.
+__device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32_t K, uint8_t* lds, int wave) {
+  // all-ones where the chunk exists: a branch-free choice between its offset and out of range
+  const uint32_t km0 = 0u - (uint32_t)(k0 + t.kc0 < K), km1 = 0u - (uint32_t)(k0 + t.kc1 < K);
+#pragma unroll
+  for (int j = 0; j < kSlabs; ++j) {
+    const uint32_t m = ((j & 1) ? km1 : km0) & (0u - ((t.row_ok >> j) & 1u));
+    const uint32_t off = ((t.base + j * t.stride8 + ((j & 1) ? t.kc1 : t.kc0) + k0) & m) | (kOutOfRange & ~m);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        t.rsrc, (__attribute__((address_space(3))) void*)(lds + (wave * kSlabs + j) * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+// Accumulators of one wave's 128 x 64 tile: 8 x 4 blocks of 16 x 16 (FP8
+// MFMA) or 4 x 2 blocks of 32 x 32 (BF16 MFMA), 128 floats per lane either way.
+template <bool FP8_MFMA> struct Acc;
+template <> struct Acc<true> { v4f v[kFM][kFN]; };
+template <> struct Acc<false> { v16f v[kPM][kPN]; };
+
+// One K step on the FP8 MFMA: lane group g (lanes 16g .. 16g+15) feeds k bytes
+// 32g .. 32g+31 of the step (chunks 2g, 2g+1) of its row to one K=128 MFMA.
+template <int FA, int FB>
+__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<true>& acc, int wm, int wn,
+                                         int lane) {
+  const int g = lane >> 4;
+  v8i bfr[kFN];
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int r = wn * kWN + j * 16 + (lane & 15);
+    const uint4 lo = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g + 1));
+    bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+#pragma unroll
+  for (int i = 0; i < kFM; ++i) {
+    const int r = wm * kWM + i * 16 + (lane & 15);
+    const uint4 lo = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g + 1));
+    const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          afr, bfr[j], acc.v[i][j], MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 127, 0, 127);
+  }
+}
+
+// One K step on the BF16 MFMA (32 x 32 x 16). Lane group G = lane / 32 owns
+// chunks 4G .. 4G+3 (k bytes 64G .. 64G+63) of its row; sub-step s (0..7)
+// feeds bytes 64G + 8s .. +7, widened to BF16, as the lane's 8 k values.
+// A and B walk k in the same order, so products pair up and the 128-byte step
+// is covered once. Each 16-byte chunk read serves two sub-steps.
+template <int FA, int FB>
+__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<false>& acc, int wm, int wn,
+                                         int lane) {
+  const int G = lane >> 5;
+  const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 bq[kPN], aq[kPM];
+#pragma unroll
+    for (int j = 0; j < kPN; ++j) bq[j] = *reinterpret_cast<const uint4*>(Bs + swz(rb + j * 32, 4 * G + c));
+#pragma unroll
+    for (int i = 0; i < kPM; ++i) aq[i] = *reinterpret_cast<const uint4*>(As + swz(ra + i * 32, 4 * G + c));
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      v8bf bw[kPN];
+#pragma unroll
+      for (int j = 0; j < kPN; ++j) bw[j] = half ? widen8<FB>(bq[j].z, bq[j].w) : widen8<FB>(bq[j].x, bq[j].y);
+#pragma unroll
+      for (int i = 0; i < kPM; ++i) {
+        const v8bf aw = half ? widen8<FA>(aq[i].z, aq[i].w) : widen8<FA>(aq[i].x, aq[i].y);
+#pragma unroll
+        for (int j = 0; j < kPN; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bw[j], acc.v[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Issues the copy of the next K step into `nxt` and multiplies the step in
+// `cur`. The two stages never overlap; saying so (restrict) lets the compiler
+// keep the copy in flight while the fragments of `cur` are read.
+template <int FA, int FB, bool FP8_MFMA>
+__device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bool more,
+                                               const TileCopy& ca, const TileCopy& cb, uint32_t k_next, uint32_t K,
+                                               Acc<FP8_MFMA>& acc, int wm, int wn, int wave, int lane) {
+  if (more) {
+    load_tile(ca, k_next, K, nxt, wave);
+    load_tile(cb, k_next, K, nxt + kTileBytes, wave);
+  }
+  mma_step<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane);
+}
+
+__device__ __forceinline__ void store_bf16(uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t m,
+                                           int64_t n, float v) {
+  if (m < M && n < N) C[m * ldc + n] = f32_to_bf16_rne(v);
+}
 
 template <int FA, int FB, bool FP8_MFMA>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, const float* __restrict__ sb,
-    uint16_t* __restrict__ C, int64_t ldc, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[kBN * kBK];
+    uint16_t* __restrict__ C, int64_t ldc, int tm, int tn) {
+  // Two stages, each an A tile followed by a B tile.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
-  const int64_t m0 = bm * kBM, n0 = bn * kBN;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  int bm, bn;
+  tile_coords(blockIdx.x, tm, tn, bm, bn);
+  const int64_t m0 = (int64_t)bm * kBM, n0 = (int64_t)bn * kBN;
 
-  v4f acc[4][4];
+  Acc<FP8_MFMA> acc;
+  float* accf = reinterpret_cast<float*>(&acc);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < (int)(sizeof(acc) / sizeof(float)); ++e) accf[e] = 0.f;
 
   const int nk = (int)((K + kBK - 1) / kBK);
+  const TileCopy ca = make_copy(A, lda, m0, M, K, wave, lane);
+  const TileCopy cb = make_copy(B, ldb, n0, N, K, wave, lane);
+  const uint32_t Ku = (uint32_t)K;
+  if (nk > 0) {
+    load_tile(ca, 0, Ku, smem, wave);
+    load_tile(cb, 0, Ku, smem + kTileBytes, wave);
+  }
+  // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
+  // step kt + 1. The barrier at the top of a step both publishes the stage to
+  // be read and retires every read of the stage about to be overwritten.
   for (int kt = 0; kt < nk; ++kt) {
-    uint4 va[4], vb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int id = tid + kThreads * j;
-      const int row = id >> 3, ch = id & 7;
-      const int64_t kk = (int64_t)kt * kBK + ch * 16;
-      const int64_t ra = m0 + row < M ? m0 + row : M - 1;   // clamp: rows past M are never stored
-      const int64_t rb = n0 + row < N ? n0 + row : N - 1;
-      if (kk < K) {
-        va[j] = *reinterpret_cast<const uint4*>(A + ra * lda + kk);
-        vb[j] = *reinterpret_cast<const uint4*>(B + rb * ldb + kk);
-      } else {
-        va[j] = make_uint4(0, 0, 0, 0);
-        vb[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    __syncthreads();   // the previous tile's fragments have been read
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int id = tid + kThreads * j;
-      const int row = id >> 3, ch = id & 7;
-      *reinterpret_cast<uint4*>(As + swz(row, ch)) = va[j];
-      *reinterpret_cast<uint4*>(Bs + swz(row, ch)) = vb[j];
-    }
+    uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
+    uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
     __syncthreads();
-
-    const int kc = (lane >> 4) * 2;   // this lane's two 16-byte k chunks
-    v8i af[4], bf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(As + swz(r, kc));
-      const uint4 hi = *reinterpret_cast<const uint4*>(As + swz(r, kc + 1));
-      af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 64 + j * 16 + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + swz(r, kc));
-      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, kc + 1));
-      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    if constexpr (FP8_MFMA) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf[j], acc[i][j], MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 127, 0, 127);
-    } else {
-      // Lane group g holds k = 32g .. 32g+31 of this K tile; sub-step s feeds
-      // bytes 8s .. 8s+7 of it to a K=32 BF16 MFMA. A and B use the same k
-      // order, so together the four sub-steps cover the whole tile once.
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        v8bf aw[4], bw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) aw[i] = widen8<FA>((uint32_t)af[i][2 * st], (uint32_t)af[i][2 * st + 1]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bw[j] = widen8<FB>((uint32_t)bf[j][2 * st], (uint32_t)bf[j][2 * st + 1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[i], bw[j], acc[i][j], 0, 0, 0);
-      }
-    }
+    pipelined_step<FA, FB, FP8_MFMA>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn,
+                                     wave, lane);
   }
 
-  // Epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16 x 16 block.
   const float s = *sa * *sb;
+  if constexpr (FP8_MFMA) {
+    // 16 x 16 blocks: lane holds C[4*(lane/16) + r][lane % 16].
+    const int64_t mb = m0 + wm * kWM + (lane >> 4) * 4, nb = n0 + wn * kWN + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+      for (int j = 0; j < kFN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (m < M && n < N) C[m * ldc + n] = f32_to_bf16_rne(acc[i][j][r] * s);
-      }
-    }
+        for (int r = 0; r < 4; ++r) store_bf16(C, ldc, M, N, mb + i * 16 + r, nb + j * 16, acc.v[i][j][r] * s);
+  } else {
+    // 32 x 32 blocks: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32].
+    const int64_t mb = m0 + wm * kWM + (lane >> 5) * 4, nb = n0 + wn * kWN + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < kPM; ++i)
+#pragma unroll
+      for (int j = 0; j < kPN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          store_bf16(C, ldc, M, N, mb + i * 32 + 8 * (r / 4) + (r % 4), nb + j * 32, acc.v[i][j][r] * s);
+  }
 }
 
-template <int FA, int FB, bool FP8_MFMA = false>
-hipError_t launch_pair(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m,
-                       int64_t n, int64_t k, const float* sa, const float* sb, uint16_t* c, int64_t ldc,
-                       hipStream_t stream) {
-  const int64_t tm = (m + kBM - 1) / kBM, tn = (n + kBN - 1) / kBN;
-  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, FP8_MFMA>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream, a,
-                     lda, b, ldb, m, n, k, sa, sb, c, ldc, (int)tn);
+template <int FA, int FB, bool FP8_MFMA>
+hipError_t launch_pair(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n,
+                       int64_t k, const float* sa, const float* sb, uint16_t* c, int64_t ldc, hipStream_t stream) {
+  const int tm = (int)((m + kBM - 1) / kBM), tn = (int)((n + kBN - 1) / kBN);
+  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, FP8_MFMA>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream,
+                     a, lda, b, ldb, m, n, k, sa, sb, c, ldc, tm, tn);
   return hipGetLastError();
+}
+
+template <bool FP8_MFMA>
+hipError_t dispatch(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b, fp8mp_format b_fmt,
+                    int64_t ldb, int64_t m, int64_t n, int64_t k, const float* sa, const float* sb, uint16_t* c,
+                    int64_t ldc, hipStream_t stream) {
+  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E4M3)
+    return launch_pair<FP8MP_E4M3, FP8MP_E4M3, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
+  if (a_fmt == FP8MP_E5M2 && b_fmt == FP8MP_E4M3)
+    return launch_pair<FP8MP_E5M2, FP8MP_E4M3, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
+  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E5M2)
+    return launch_pair<FP8MP_E4M3, FP8MP_E5M2, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
+  return launch_pair<FP8MP_E5M2, FP8MP_E5M2, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
 }
 
 }  // namespace
@@ -187,17 +324,7 @@ hipError_t launch_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
                               const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
                               int64_t ldc, int num_cus, hipStream_t stream) {
   (void)num_cus;
-  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E4M3)
-    return launch_pair<FP8MP_E4M3, FP8MP_E4M3>(a, lda, b, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc,
-                                               stream);
-  if (a_fmt == FP8MP_E5M2 && b_fmt == FP8MP_E4M3)
-    return launch_pair<FP8MP_E5M2, FP8MP_E4M3>(a, lda, b, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc,
-                                               stream);
-  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E5M2)
-    return launch_pair<FP8MP_E4M3, FP8MP_E5M2>(a, lda, b, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc,
-                                               stream);
-  return launch_pair<FP8MP_E5M2, FP8MP_E5M2>(a, lda, b, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc,
-                                             stream);
+  return dispatch<false>(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, stream);
 }
 
 }  // namespace fp8mp
