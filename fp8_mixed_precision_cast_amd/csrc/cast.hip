@@ -14,13 +14,19 @@
 namespace fp8mp {
 namespace {
 
-constexpr int kFlatBlock = 256;
+constexpr int kFlatBlock = 512;
+constexpr int kFlatUnroll = 4;   // 16-element chunks per thread per iteration
 constexpr int kTileBlock = 256;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // for the non-temporal builtins
 constexpr int kTileRows = 256;   // 32 row groups of 8
 constexpr int kTileCols = 64;    // 8 column groups of 8
 
 // ---------------------------------------------------------------------------
-// Contiguous BF16 source, 16 elements (two 16-byte loads) -> one 16-byte store.
+// Contiguous BF16 source: each thread converts kFlatUnroll chunks of 16
+// elements per iteration (two 16-byte loads -> one 16-byte store per chunk);
+// all loads of an iteration are issued before any conversion. Source and
+// codes are touched once, so both stream past the caches (non-temporal).
 template <int FMT, bool HAS_Q>
 __global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16(const uint4* __restrict__ x,
                                                              uint4* __restrict__ q, int64_t nchunk,
@@ -29,29 +35,35 @@ __global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16(const uint4* __rest
   const float s = HAS_Q ? *scale : 1.0f;
   uint32_t acc = 0;
   const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
-  for (int64_t i = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; i < nchunk; i += 2 * stride) {
-    const int64_t j = i + stride;
-    const bool two = j < nchunk;
-    uint4 a0 = x[2 * i], a1 = x[2 * i + 1];
-    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = b0;
-    if (two) { b0 = x[2 * j]; b1 = x[2 * j + 1]; }
-    acc = amax_bf16x2(acc, a0.x); acc = amax_bf16x2(acc, a0.y);
-    acc = amax_bf16x2(acc, a0.z); acc = amax_bf16x2(acc, a0.w);
-    acc = amax_bf16x2(acc, a1.x); acc = amax_bf16x2(acc, a1.y);
-    acc = amax_bf16x2(acc, a1.z); acc = amax_bf16x2(acc, a1.w);
-    acc = amax_bf16x2(acc, b0.x); acc = amax_bf16x2(acc, b0.y);
-    acc = amax_bf16x2(acc, b0.z); acc = amax_bf16x2(acc, b0.w);
-    acc = amax_bf16x2(acc, b1.x); acc = amax_bf16x2(acc, b1.y);
-    acc = amax_bf16x2(acc, b1.z); acc = amax_bf16x2(acc, b1.w);
-    if constexpr (HAS_Q) {
-      uint4 o;
-      o.x = enc4_bf16<FMT>(a0.x, a0.y, s); o.y = enc4_bf16<FMT>(a0.z, a0.w, s);
-      o.z = enc4_bf16<FMT>(a1.x, a1.y, s); o.w = enc4_bf16<FMT>(a1.z, a1.w, s);
-      q[i] = o;
-      if (two) {
-        o.x = enc4_bf16<FMT>(b0.x, b0.y, s); o.y = enc4_bf16<FMT>(b0.z, b0.w, s);
-        o.z = enc4_bf16<FMT>(b1.x, b1.y, s); o.w = enc4_bf16<FMT>(b1.z, b1.w, s);
-        q[j] = o;
+  for (int64_t base = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; base < nchunk;
+       base += kFlatUnroll * stride) {
+    u32x4 a[kFlatUnroll], b[kFlatUnroll];
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+#pragma unroll
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      const int64_t i = base + u * stride;
+      if (i < nchunk) {
+        a[u] = __builtin_nontemporal_load(xv + 2 * i);
+        b[u] = __builtin_nontemporal_load(xv + 2 * i + 1);
+      } else {
+        a[u] = u32x4{0, 0, 0, 0};
+        b[u] = a[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      acc = amax_bf16x2(acc, a[u].x); acc = amax_bf16x2(acc, a[u].y);
+      acc = amax_bf16x2(acc, a[u].z); acc = amax_bf16x2(acc, a[u].w);
+      acc = amax_bf16x2(acc, b[u].x); acc = amax_bf16x2(acc, b[u].y);
+      acc = amax_bf16x2(acc, b[u].z); acc = amax_bf16x2(acc, b[u].w);
+      if constexpr (HAS_Q) {
+        const int64_t i = base + u * stride;
+        if (i < nchunk) {
+          u32x4 o;
+          o.x = enc4_bf16<FMT>(a[u].x, a[u].y, s); o.y = enc4_bf16<FMT>(a[u].z, a[u].w, s);
+          o.z = enc4_bf16<FMT>(b[u].x, b[u].y, s); o.w = enc4_bf16<FMT>(b[u].z, b[u].w, s);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(q) + i);
+        }
       }
     }
   }
@@ -219,7 +231,7 @@ hipError_t launch_generic(const void* x, int64_t cols, int64_t ld_x, int64_t sta
                           float* amax, int num_cus, hipStream_t stream) {
   const int64_t n = end - start;
   if (n <= 0) return hipSuccess;
-  const int grid = (int)std::min<int64_t>(cdiv(n, kFlatBlock), (int64_t)num_cus * 8);
+  const int grid = (int)std::min<int64_t>(cdiv(n, kFlatBlock), (int64_t)num_cus * 2);
   hipLaunchKernelGGL((cast_generic<FMT, DT>), dim3(grid), dim3(kFlatBlock), 0, stream, x, cols, ld_x,
                      start, end, scale, q, ld_q, q_t, ld_qt, amax);
   return hipGetLastError();
@@ -236,7 +248,8 @@ hipError_t launch_fmt(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols,
   if (contiguous && aligned(x, 16) && (q == nullptr || aligned(q, 16))) {
     const int64_t nchunk = numel / 16;
     if (nchunk > 0) {
-      const int grid = (int)std::min<int64_t>(cdiv(nchunk, kFlatBlock), (int64_t)num_cus * 8);
+      const int per_block = dt == FP8MP_BF16 ? kFlatBlock * kFlatUnroll : kFlatBlock;
+      const int grid = (int)std::min<int64_t>(cdiv(nchunk, per_block), (int64_t)num_cus * 2);
       if (dt == FP8MP_BF16) {
         if (q) hipLaunchKernelGGL((cast_flat_bf16<FMT, true>), dim3(grid), dim3(kFlatBlock), 0, stream,
                                   (const uint4*)x, (uint4*)q, nchunk, scale, amax);
@@ -265,7 +278,7 @@ hipError_t launch_fmt(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols,
                         (q_t == nullptr || (aligned(q_t, 8) && ld_qt % 8 == 0));
     const int64_t tiles_r = cdiv(rows, kTileRows), tiles_c = cdiv(cols, kTileCols);
     const int64_t ntiles = tiles_r * tiles_c;
-    const int grid = (int)std::min<int64_t>(ntiles, (int64_t)num_cus * 4);
+    const int grid = (int)std::min<int64_t>(ntiles, (int64_t)num_cus * 2);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
 #define FP8MP_TILE(HQ, HQT)                                                                       \
   hipLaunchKernelGGL((cast_tile_bf16<FMT, HQ, HQT>), dim3(grid), dim3(kTileBlock), 0, stream, xb, \

@@ -10,49 +10,74 @@ namespace fp8mp {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kLdsEntries = 8192;   // histories up to this long are rolled through LDS in one pass
 
 template <int FMT>
-__global__ __launch_bounds__(kBlock) void scale_update_kernel(float* __restrict__ hist, int32_t len,
-                                                              int32_t margin, float* __restrict__ scale,
-                                                              float* __restrict__ scale_inv) {
-  __shared__ uint32_t red[kBlock / 64];
-  uint32_t* h = reinterpret_cast<uint32_t*>(hist);
-
-  // Max over every entry. History entries are amaxes: non-negative floats or
-  // the canonical NaN, so the unsigned max of the bit patterns is the
-  // NaN-propagating float max.
-  uint32_t m = 0;
-  for (int32_t i = threadIdx.x; i < len; i += kBlock) {
-    const uint32_t v = h[i] & 0x7FFFFFFFu;
-    m = m > v ? m : v;
+__device__ __forceinline__ void update_scale_from(uint32_t a, int32_t margin, float* __restrict__ scale,
+                                                  float* __restrict__ scale_inv) {
+  // finite and positive: 0 < bits < +Inf
+  if (a != 0u && a < 0x7F800000u) {
+    const float ratio = Fp8Traits<FMT>::kMax / __uint_as_float(a);  // IEEE binary32 division
+    const float s = __builtin_ldexpf(ratio, -margin);               // exact 2^-margin, one rounding
+    const float inv = 1.0f / s;
+    const uint32_t sb = __float_as_uint(s), ib = __float_as_uint(inv);
+    if (sb != 0u && sb < 0x7F800000u && ib < 0x7F800000u) {
+      *scale = s;
+      *scale_inv = inv;
+    }
   }
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* red) {
   for (int off = 32; off > 0; off >>= 1) {
     const uint32_t o = __shfl_xor(m, off, 64);
     m = m > o ? m : o;
   }
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-
-  if (threadIdx.x == 0) {
-    uint32_t a = red[0];
+  uint32_t a = red[0];
 #pragma unroll
-    for (int w = 1; w < kBlock / 64; ++w) a = a > red[w] ? a : red[w];
-    // finite and positive: 0 < bits < +Inf
-    if (a != 0u && a < 0x7F800000u) {
-      const float ratio = Fp8Traits<FMT>::kMax / __uint_as_float(a);  // IEEE binary32 division
-      const float s = __builtin_ldexpf(ratio, -margin);               // exact 2^-margin, one rounding
-      const float inv = 1.0f / s;
-      const uint32_t sb = __float_as_uint(s), ib = __float_as_uint(inv);
-      if (sb != 0u && sb < 0x7F800000u && ib < 0x7F800000u) {
-        *scale = s;
-        *scale_inv = inv;
-      }
+  for (int w = 1; w < kBlock / 64; ++w) a = a > red[w] ? a : red[w];
+  return a;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kBlock) void scale_update_kernel(float* __restrict__ hist, int32_t len,
+                                                              int32_t margin, float* __restrict__ scale,
+                                                              float* __restrict__ scale_inv) {
+  __shared__ uint32_t red[kBlock / 64];
+  __shared__ uint32_t stage[kLdsEntries];
+  uint32_t* h = reinterpret_cast<uint32_t*>(hist);
+
+  // Max over every entry. History entries are amaxes: non-negative floats or
+  // the canonical NaN, so the unsigned max of the bit patterns (sign masked)
+  // is the NaN-propagating float max.
+  if (len <= kLdsEntries) {
+    // One pass: every entry is read once into LDS, then written back shifted.
+    uint32_t m = 0;
+    for (int32_t i = threadIdx.x; i < len; i += kBlock) {
+      const uint32_t v = h[i];
+      stage[i] = v;
+      const uint32_t a = v & 0x7FFFFFFFu;
+      m = m > a ? m : a;
     }
+    const uint32_t a = block_max(m, red);   // also orders the LDS writes before the reads below
+    if (threadIdx.x == 0) update_scale_from<FMT>(a, margin, scale, scale_inv);
+    for (int32_t i = threadIdx.x; i < len; i += kBlock) h[i] = i == 0 ? 0u : stage[i - 1];
+    return;
   }
 
-  // Roll by one entry: h[i] = h[i-1], h[0] = 0. Chunks are moved from the top
-  // down, each read fully before any of it is written; a chunk's writes never
-  // reach entries a lower chunk still has to read.
+  uint32_t m = 0;
+  for (int32_t i = threadIdx.x; i < len; i += kBlock) {
+    const uint32_t v = h[i] & 0x7FFFFFFFu;
+    m = m > v ? m : v;
+  }
+  const uint32_t a = block_max(m, red);
+  if (threadIdx.x == 0) update_scale_from<FMT>(a, margin, scale, scale_inv);
+
+  // Long histories roll in place by chunks moved from the top down, each read
+  // fully before any of it is written; a chunk's writes never reach entries a
+  // lower chunk still has to read.
   for (int32_t top = len; top > 0; top -= kBlock) {
     const int32_t i = top - kBlock + (int32_t)threadIdx.x;   // destination index
     __syncthreads();

@@ -30,7 +30,7 @@ def _one(hist, fmt, margin, scale=1.0, scale_inv=1.0):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
-@pytest.mark.parametrize("L", [1, 2, 5, 16, 255, 256, 257, 1024, 1500])
+@pytest.mark.parametrize("L", [1, 2, 5, 16, 255, 256, 257, 1024, 1500, 8192, 8193, 10000])
 def test_random_histories(fmt, L):
     require_gpu()
     rng = np.random.default_rng(L)
