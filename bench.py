@@ -41,7 +41,27 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES three times (calibrates HBM counters)")
     return ap.parse_args()
+
+
+def source_digest() -> str:
+    """Digest of the GEMM kernel source; counter readings are valid only for the source they were taken on."""
+    import hashlib
+    with open(os.path.join(ROOT, "fp8_mixed_precision_cast_amd", "csrc", "gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def copy_reference(nbytes: int) -> None:
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes": nbytes}), flush=True)
 
 
 def cpu_baseline(w, inp, min_seconds: float = 10.0):
@@ -77,6 +97,9 @@ def cpu_baseline(w, inp, min_seconds: float = 10.0):
 
 def main():
     args = parse()
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); every box has one MI355X and this "
               "path does not shard across GPUs.", file=sys.stderr)
@@ -132,8 +155,9 @@ def main():
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
-            t = json.load(f)
-        traffic = t.get(w.name, {}).get("gemm_bytes_per_launch")
+            t = json.load(f).get(w.name, {})
+        if t.get("gemm_source") == source_digest():
+            traffic = t.get("gemm_bytes_per_launch")
 
     g = w.gemms[0]
     out = {
