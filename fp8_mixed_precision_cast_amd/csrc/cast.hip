@@ -19,8 +19,8 @@ constexpr int kFlatUnroll = 4;   // 16-element chunks per thread per iteration
 constexpr int kTileBlock = 256;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // for the non-temporal builtins
-constexpr int kTileRows = 256;   // 32 row groups of 8
-constexpr int kTileCols = 64;    // 8 column groups of 8
+constexpr int kTileRows = 128;   // 32 row groups of 4
+constexpr int kTileCols = 128;   // 8 column groups of 16
 
 // ---------------------------------------------------------------------------
 // Contiguous BF16 source: each thread converts kFlatUnroll chunks of 16
@@ -133,9 +133,18 @@ __global__ __launch_bounds__(kFlatBlock) void cast_generic(const void* __restric
 }
 
 // ---------------------------------------------------------------------------
-// BF16 source in 256 x 64 tiles; each thread owns an 8 x 8 block: eight
-// 16-byte row loads, eight 8-byte row stores of q, and after an in-register
-// 8 x 8 byte transpose, eight 8-byte row stores of q_t.
+// BF16 source in 128 x 128 tiles, 256 threads. Thread (rg, cg) = (t / 8, t % 8)
+// owns rows 4rg .. 4rg+3 and columns 16cg .. 16cg+15 of the tile: two 16-byte
+// loads per row (eight lanes read a 256-byte row), one 16-byte store of q per
+// row. For q_t the thread's 4 x 16 codes are transposed in registers into
+// sixteen dwords (one column, four rows each) and written to an LDS tile held
+// in q_t orientation; after a barrier every thread copies four 16-byte pieces
+// of it to q_t (eight lanes per 128-byte q_t row).
+//
+// LDS tile T: 128 q_t rows (tile columns) x 128 bytes (tile rows). The 16-byte
+// chunk k of T row c sits at chunk slot k ^ ((c >> 4) & 7): the eight column
+// groups of a wave then write eight different chunks (2-way bank sharing at
+// most) and the 16-byte reads are conflict-free.
 
 // 4 x 4 byte transpose: input dword i holds row i (byte j = column j); output
 // dword j holds column j (byte i = row i). v_perm_b32 picks any four of the
@@ -152,56 +161,77 @@ __device__ __forceinline__ void tr4(uint32_t r0, uint32_t r1, uint32_t r2, uint3
   c3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);                  // column 3
 }
 
+__device__ __forceinline__ int tslot(int c, int k) { return c * kTileRows + ((k ^ ((c >> 4) & 7)) << 4); }
+
 template <int FMT, bool HAS_Q, bool HAS_QT>
 __global__ __launch_bounds__(kTileBlock) void cast_tile_bf16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ld_q,
     uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ amax, int64_t tiles_c,
     int64_t ntiles, int vec_ok) {
+  __shared__ __attribute__((aligned(16))) uint8_t T[kTileCols * kTileRows];
   const float s = (HAS_Q || HAS_QT) ? *scale : 1.0f;
-  const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  const int tid = threadIdx.x, cg = tid & 7, rg = tid >> 3;
   uint32_t acc = 0;        // packed BF16 magnitudes (vector path)
   uint32_t acc32 = 0;      // fp32 magnitudes (edge path)
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
-    const int64_t r0 = tr * kTileRows + rg * 8, c0 = tc * kTileCols + cg * 8;
-    const bool full = vec_ok && (tr * kTileRows + kTileRows <= rows) && (tc * kTileCols + kTileCols <= cols);
+    const int64_t R0 = tr * kTileRows, C0 = tc * kTileCols;
+    const bool full = vec_ok && (R0 + kTileRows <= rows) && (C0 + kTileCols <= cols);
     if (full) {
-      uint4 v[8];
+      const int64_t r0 = R0 + rg * 4, c0 = C0 + cg * 16;
+      u32x4 v[4][2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld_x + c0);
-      uint32_t lo[8], hi[8];
+      for (int i = 0; i < 4; ++i) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + (r0 + i) * ld_x + c0);
+        v[i][0] = __builtin_nontemporal_load(src);
+        v[i][1] = __builtin_nontemporal_load(src + 1);
+      }
+      uint32_t code[4][4];   // [row][dword]: dword d holds columns 4d .. 4d+3
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc = amax_bf16x2(acc, v[i].x); acc = amax_bf16x2(acc, v[i].y);
-        acc = amax_bf16x2(acc, v[i].z); acc = amax_bf16x2(acc, v[i].w);
-        lo[i] = enc4_bf16<FMT>(v[i].x, v[i].y, s);
-        hi[i] = enc4_bf16<FMT>(v[i].z, v[i].w, s);
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          acc = amax_bf16x2(acc, v[i][h].x); acc = amax_bf16x2(acc, v[i][h].y);
+          acc = amax_bf16x2(acc, v[i][h].z); acc = amax_bf16x2(acc, v[i][h].w);
+          code[i][2 * h] = enc4_bf16<FMT>(v[i][h].x, v[i][h].y, s);
+          code[i][2 * h + 1] = enc4_bf16<FMT>(v[i][h].z, v[i][h].w, s);
+        }
       }
       if constexpr (HAS_Q) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0) = make_uint2(lo[i], hi[i]);
+        for (int i = 0; i < 4; ++i)
+          __builtin_nontemporal_store(u32x4{code[i][0], code[i][1], code[i][2], code[i][3]},
+                                      reinterpret_cast<u32x4*>(q + (r0 + i) * ld_q + c0));
       }
       if constexpr (HAS_QT) {
-        uint32_t a[4], b[4], c[4], d[4];
-        tr4(lo[0], lo[1], lo[2], lo[3], a[0], a[1], a[2], a[3]);   // cols 0-3, rows 0-3
-        tr4(lo[4], lo[5], lo[6], lo[7], b[0], b[1], b[2], b[3]);   // cols 0-3, rows 4-7
-        tr4(hi[0], hi[1], hi[2], hi[3], c[0], c[1], c[2], c[3]);   // cols 4-7, rows 0-3
-        tr4(hi[4], hi[5], hi[6], hi[7], d[0], d[1], d[2], d[3]);   // cols 4-7, rows 4-7
+        __syncthreads();   // the previous tile's T has been copied out
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *reinterpret_cast<uint2*>(q_t + (c0 + j) * ld_qt + r0) = make_uint2(a[j], b[j]);
-          *reinterpret_cast<uint2*>(q_t + (c0 + 4 + j) * ld_qt + r0) = make_uint2(c[j], d[j]);
+        for (int d = 0; d < 4; ++d) {
+          uint32_t col[4];
+          tr4(code[0][d], code[1][d], code[2][d], code[3][d], col[0], col[1], col[2], col[3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = cg * 16 + d * 4 + e;      // tile column = T row
+            *reinterpret_cast<uint32_t*>(T + tslot(c, rg >> 2) + (rg & 3) * 4) = col[e];
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int idx = it * kTileBlock + tid;
+          const int c = idx >> 3, k = idx & 7;
+          const u32x4 piece = *reinterpret_cast<const u32x4*>(T + tslot(c, k));
+          __builtin_nontemporal_store(piece, reinterpret_cast<u32x4*>(q_t + (C0 + c) * ld_qt + R0 + k * 16));
         }
       }
     } else {
-      for (int i = 0; i < 8; ++i) {
-        const int64_t r = r0 + i;
+      // edge tile: element by element, same thread-to-element map
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = R0 + rg * 4 + i;
         if (r >= rows) break;
-        for (int j = 0; j < 8; ++j) {
-          const int64_t c = c0 + j;
+        for (int j = 0; j < 16; ++j) {
+          const int64_t c = C0 + cg * 16 + j;
           if (c >= cols) break;
           const float vv = __uint_as_float((uint32_t)x[r * ld_x + c] << 16);
           acc32 = amax_f32(acc32, vv);
@@ -274,8 +304,8 @@ hipError_t launch_fmt(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols,
 
   if (dt == FP8MP_BF16) {
     const bool vec_ok = aligned(x, 16) && (ld_x * esize) % 16 == 0 &&
-                        (q == nullptr || (aligned(q, 8) && ld_q % 8 == 0)) &&
-                        (q_t == nullptr || (aligned(q_t, 8) && ld_qt % 8 == 0));
+                        (q == nullptr || (aligned(q, 16) && ld_q % 16 == 0)) &&
+                        (q_t == nullptr || (aligned(q_t, 16) && ld_qt % 16 == 0));
     const int64_t tiles_r = cdiv(rows, kTileRows), tiles_c = cdiv(cols, kTileCols);
     const int64_t ntiles = tiles_r * tiles_c;
     const int grid = (int)std::min<int64_t>(ntiles, (int64_t)num_cus * 2);
