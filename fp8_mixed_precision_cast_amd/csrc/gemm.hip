@@ -187,29 +187,57 @@ __device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, A
 // feeds bytes 64G + 8s .. +7, widened to BF16, as the lane's 8 k values.
 // A and B walk k in the same order, so products pair up and the 128-byte step
 // is covered once. Each 16-byte chunk read serves two sub-steps.
+//
+// Software pipeline: the fragments of chunk c+1 are read from LDS while chunk
+// c is multiplied, and the operands of each sub-step are widened while the
+// MFMAs of the sub-step before it run.
 template <int FA, int FB>
 __device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<false>& acc, int wm, int wn,
                                          int lane) {
   const int G = lane >> 5;
   const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
+  uint4 aq[2][kPM], bq[2][kPN];
+  auto read_chunk = [&](int c, uint4 (&a)[kPM], uint4 (&b)[kPN]) {
+#pragma unroll
+    for (int j = 0; j < kPN; ++j) b[j] = *reinterpret_cast<const uint4*>(Bs + swz(rb + j * 32, 4 * G + c));
+#pragma unroll
+    for (int i = 0; i < kPM; ++i) a[i] = *reinterpret_cast<const uint4*>(As + swz(ra + i * 32, 4 * G + c));
+  };
+  read_chunk(0, aq[0], bq[0]);
+  v8bf aw[kPM], bw[kPN];
+#pragma unroll
+  for (int i = 0; i < kPM; ++i) aw[i] = widen8<FA>(aq[0][i].x, aq[0][i].y);
+#pragma unroll
+  for (int j = 0; j < kPN; ++j) bw[j] = widen8<FB>(bq[0][j].x, bq[0][j].y);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    uint4 bq[kPN], aq[kPM];
-#pragma unroll
-    for (int j = 0; j < kPN; ++j) bq[j] = *reinterpret_cast<const uint4*>(Bs + swz(rb + j * 32, 4 * G + c));
-#pragma unroll
-    for (int i = 0; i < kPM; ++i) aq[i] = *reinterpret_cast<const uint4*>(As + swz(ra + i * 32, 4 * G + c));
+    const int cur = c & 1, nxt = cur ^ 1;
+    if (c + 1 < 4) read_chunk(c + 1, aq[nxt], bq[nxt]);
+    // keep the prefetch at the top of the chunk (the scheduler would otherwise sink it to its use)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      v8bf bw[kPN];
+      const bool last = c == 3 && half == 1;
+      v8bf an[kPM], bn[kPN];
+      if (!last) {
+        const int sc = half == 0 ? cur : nxt;
 #pragma unroll
-      for (int j = 0; j < kPN; ++j) bw[j] = half ? widen8<FB>(bq[j].z, bq[j].w) : widen8<FB>(bq[j].x, bq[j].y);
-#pragma unroll
-      for (int i = 0; i < kPM; ++i) {
-        const v8bf aw = half ? widen8<FA>(aq[i].z, aq[i].w) : widen8<FA>(aq[i].x, aq[i].y);
+        for (int i = 0; i < kPM; ++i)
+          an[i] = half == 0 ? widen8<FA>(aq[sc][i].z, aq[sc][i].w) : widen8<FA>(aq[sc][i].x, aq[sc][i].y);
 #pragma unroll
         for (int j = 0; j < kPN; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bw[j], acc.v[i][j], 0, 0, 0);
+          bn[j] = half == 0 ? widen8<FB>(bq[sc][j].z, bq[sc][j].w) : widen8<FB>(bq[sc][j].x, bq[sc][j].y);
+      }
+#pragma unroll
+      for (int i = 0; i < kPM; ++i)
+#pragma unroll
+        for (int j = 0; j < kPN; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bw[j], acc.v[i][j], 0, 0, 0);
+      if (!last) {
+#pragma unroll
+        for (int i = 0; i < kPM; ++i) aw[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < kPN; ++j) bw[j] = bn[j];
       }
     }
   }
