@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp7b_up_fwd")
+    ap.add_argument("--recipe", default="delayed", choices=["delayed", "current"],
+                    help="delayed scaling (the pages' default recipe) or just-in-time scaling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
@@ -116,7 +118,7 @@ def main():
     info = fp8.fp8mp_device_info()
     inp = wl.load(w.name)
     dinp = {k: torch.from_numpy(v.view("int16")).cuda() for k, v in inp.items()}
-    plan = plan_from_workload(w)
+    plan = plan_from_workload(w, recipe=args.recipe)
     stream = torch.cuda.current_stream()
     plan.prime(dinp)
     for _ in range(args.warmup):
@@ -174,7 +176,7 @@ def main():
         "dtype": "fp8-e4m3 operands; bf16 MFMA (exact on FP8 values), f32 accumulate, bf16 out",
         "data": "synthetic",
         "config": {"workload": w.name, "m": g.m, "n": g.n, "k": g.k, "x": "bf16 N(0,1)+0.1% x20",
-                   "w": "bf16 N(0,0.02)", "history_len": w.history_len, "margin": w.margin,
+                   "w": "bf16 N(0,0.02)", "history_len": w.history_len, "margin": w.margin, "recipe": args.recipe,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_MFMA_TFLOPS, 4),

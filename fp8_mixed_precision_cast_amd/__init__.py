@@ -24,7 +24,7 @@ from typing import Optional
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
     "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8mp_status_string",
-    "fp8mp_device_info", "exported_symbols", "DelayedScalingState",
+    "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
 
 E4M3, E5M2 = 0, 1
@@ -191,3 +191,28 @@ class DelayedScalingState:
         self.history.copy_(sd["amax_history"])
         self.scale.copy_(sd["scale"])
         self.scale_inv.copy_(sd["scale_inv"])
+
+
+class CurrentScalingState:
+    """Just-in-time (current) per-tensor scaling through the same three calls.
+
+    [MPT] §横断的知見 "テンソルスケーリングが FP8 実用化の鍵" names just-in-time per-tensor
+    scaling beside delayed scaling: the scale comes from the tensor's own amax
+    in the same step. Here that is an amax-only pass into a one-entry history,
+    the update (scale = fmax / amax / 2**margin, same hold rules; the entry is
+    reset to 0), then the cast with the fresh scale: two reads of the source
+    instead of one.
+    """
+
+    def __init__(self, fmt, margin: int = 0, device="cuda"):
+        import torch
+        self.fmt = FORMATS[fmt]
+        self.margin = int(margin)
+        self.slot = torch.zeros(1, dtype=torch.float32, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.scale_inv = torch.ones(1, dtype=torch.float32, device=device)
+
+    def cast(self, x, q=None, q_t=None, stream=None) -> None:
+        fp8_amax_cast(x, self.fmt, None, None, None, self.slot, stream)
+        fp8_scale_update(self.slot, self.fmt, self.margin, self.scale, self.scale_inv, stream)
+        fp8_amax_cast(x, self.fmt, self.scale, q, q_t, None, stream)

@@ -21,7 +21,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import DelayedScalingState, fp8_amax_cast, fp8_scale_update, fp8_scaled_gemm
+from . import CurrentScalingState, DelayedScalingState, fp8_amax_cast, fp8_scale_update, fp8_scaled_gemm
 
 
 @dataclass(frozen=True)
@@ -43,8 +43,13 @@ class GemmOp:
 
 
 class LayerPlan:
+    """recipe "delayed" (the default) or "current" (just-in-time scaling: amax pass, update, cast)."""
+
     def __init__(self, operands: Sequence[OperandSpec], gemms: Sequence[GemmOp], history_len: int = 1024,
-                 margin: int = 0, device: str = "cuda"):
+                 margin: int = 0, device: str = "cuda", recipe: str = "delayed"):
+        if recipe not in ("delayed", "current"):
+            raise ValueError(recipe)
+        self.recipe = recipe
         self.operands = {o.name: o for o in operands}
         self.gemms = list(gemms)
         self.state: Dict[str, DelayedScalingState] = {}
@@ -53,7 +58,8 @@ class LayerPlan:
         self.out: Dict[str, torch.Tensor] = {}
         for o in operands:
             r, c = o.shape
-            self.state[o.name] = DelayedScalingState(o.fmt, history_len, margin, device)
+            self.state[o.name] = (DelayedScalingState(o.fmt, history_len, margin, device) if recipe == "delayed"
+                                  else CurrentScalingState(o.fmt, margin, device))
             self.q[o.name] = torch.empty(r, c, dtype=torch.uint8, device=device) if o.plain else None
             self.qt[o.name] = torch.empty(c, r, dtype=torch.uint8, device=device) if o.transposed else None
         self._gemm_args = []
@@ -71,6 +77,8 @@ class LayerPlan:
 
     def prime(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
         """An amax-only pass over every operand, then one update (single-shot workloads)."""
+        if self.recipe == "current":
+            return
         for name, st in self.state.items():
             fp8_amax_cast(inputs[name], st.fmt, None, None, None, st.amax_slot, stream)
         for st in self.state.values():
@@ -78,13 +86,18 @@ class LayerPlan:
 
     def cast_all(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
         for name, st in self.state.items():
-            st.cast(inputs[name], self.q[name], self.qt[name], True, stream)
+            if self.recipe == "delayed":
+                st.cast(inputs[name], self.q[name], self.qt[name], True, stream)
+            else:
+                st.cast(inputs[name], self.q[name], self.qt[name], stream)
 
     def gemm_all(self, stream=None) -> None:
         for a, af, b, bf, sa, sb, c in self._gemm_args:
             fp8_scaled_gemm(a, af, b, bf, sa, sb, c, stream)
 
     def update_all(self, stream=None) -> None:
+        if self.recipe == "current":
+            return
         for st in self.state.values():
             fp8_scale_update(st.history, st.fmt, st.margin, st.scale, st.scale_inv, stream)
 
@@ -97,15 +110,17 @@ class LayerPlan:
         return sum(2 * a.shape[0] * b.shape[0] * a.shape[1] for a, _, b, _, _, _, _ in self._gemm_args)
 
     def cast_bytes(self, inputs: Dict[str, torch.Tensor]) -> int:
-        """Algorithmic bytes of the casts: source read once, each code layout written once."""
+        """Algorithmic bytes of the casts: source read once (twice for just-in-time scaling),
+        each code layout written once."""
+        reads = 1 if self.recipe == "delayed" else 2
         total = 0
         for name, o in self.operands.items():
             n = o.shape[0] * o.shape[1]
-            total += n * inputs[name].element_size() + n * (int(o.plain) + int(o.transposed))
+            total += reads * n * inputs[name].element_size() + n * (int(o.plain) + int(o.transposed))
         return total
 
 
-def plan_from_workload(w, device: str = "cuda") -> LayerPlan:
+def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed") -> LayerPlan:
     """A LayerPlan from a workload description with the attributes
     ``tensors`` (``name``, ``shape``), ``formats``, ``transposed``, ``gemms``
     (``name``, ``a``, ``a_transposed``, ``b``, ``b_transposed``), ``history_len``
@@ -113,4 +128,4 @@ def plan_from_workload(w, device: str = "cuda") -> LayerPlan:
     ops = [OperandSpec(t.name, tuple(t.shape), w.formats[t.name], t.name in w.transposed, True)
            for t in w.tensors]
     gemms = [GemmOp(g.name, g.a, g.a_transposed, g.b, g.b_transposed) for g in w.gemms]
-    return LayerPlan(ops, gemms, w.history_len, w.margin, device)
+    return LayerPlan(ops, gemms, w.history_len, w.margin, device, recipe)
