@@ -5,17 +5,15 @@
 // the matrix units accumulate in FP32.
 //
 // Both operands are K-contiguous (A[m][k], B[n][k]) and stay FP8 in HBM and
-// LDS (one byte per element). Two MFMA paths exist:
-//
-//   precise (default): each lane widens its FP8 fragments to BF16 in
-//     registers (v_cvt_scalef32_pk_bf16_{fp8,bf8} with scale 1, exact for
-//     every code) and runs v_mfma_f32_32x32x16_bf16, whose products are exact
-//     and whose sums carry about 22 bits relative to sum|a*b| per instruction.
-//     (On gfx950 the 16x16x32 BF16 form issues at half the 32x32x16 rate.)
-//   fp8: v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales, twice the
-//     MFMA rate, but gfx950 reduces each 128-product dot with only about 17
-//     bits relative to its largest product (measured: up to 7e-5 of sum|a*b|
-//     per instruction), which exceeds the tolerance on outputs that cancel.
+// LDS (one byte per element). Each lane widens its FP8 fragments to BF16 in
+// registers (v_cvt_scalef32_pk_bf16_{fp8,bf8} with scale 1, exact for every
+// code) and runs v_mfma_f32_32x32x16_bf16, whose products are exact and whose
+// sums carry about 22 bits relative to sum|a*b| per instruction. gfx950's FP8
+// MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4 and the older fp8 forms) run twice
+// as fast but reduce each dot product with only about 17 bits relative to its
+// largest product (measured: up to 7e-5 of sum|a*b| per instruction), which
+// exceeds the tolerance on outputs that cancel; they are not used. (The
+// 16x16x32 BF16 form issues at half the 32x32x16 rate on gfx950.)
 //
 // Tiling: 256 x 256 output tiles, K in steps of 128 bytes, 512 threads as 2 x 4
 // waves of 128 x 64 (two waves per SIMD). Tiles of A and B are copied global -> LDS directly
@@ -26,15 +24,20 @@
 // distinct bank groups. Tiles are numbered so that each XCD (workgroups are
 // dealt to the eight XCDs round-robin) owns a contiguous run of tile ids, and
 // runs are walked in groups of kGroupM tile rows so concurrently resident
-// tiles share A and B panels in that XCD's L2. The per-tensor scales are
-// applied once in the epilogue.
+// tiles share A and B panels in that XCD's L2.
+//
+// The MFMA is fed B as its first operand and A as its second, so it computes
+// the tile transposed and each lane ends up holding four consecutive output
+// columns of one output row. The epilogue scales by sa_inv * sb_inv, rounds to
+// BF16 (v_cvt_pk_bf16_f32, round to nearest even), stages the whole 256 x 256
+// BF16 tile in LDS (128 KB, the two stages' space) and writes it out with
+// 16-byte stores, 512 contiguous bytes per row.
 #include "common.h"
 
 namespace fp8mp {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -43,17 +46,13 @@ constexpr int kBM = 256, kBN = 256, kBK = 128;
 constexpr int kThreads = 512;             // 8 waves, two per SIMD
 constexpr int kWavesN = 4;                // waves laid out 2 (M) x 4 (N)
 constexpr int kWM = 128, kWN = 64;        // wave tile
-constexpr int kFM = kWM / 16, kFN = kWN / 16;   // 16 x 16 blocks per wave (FP8 MFMA path)
-constexpr int kPM = kWM / 32, kPN = kWN / 32;   // 32 x 32 blocks per wave (BF16 MFMA path)
+constexpr int kPM = kWM / 32, kPN = kWN / 32;   // 32 x 32 MFMA blocks per wave
 constexpr int kTileBytes = kBM * kBK;     // one operand's K step in LDS: 32 KB
 constexpr int kSlabs = kTileBytes / (kThreads * 16);   // 1 KB LDS slabs each wave fills per operand
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
-
-// MFMA operand-format selectors of the f8f6f4 family.
-template <int FMT> struct MfmaFmt;
-template <> struct MfmaFmt<FP8MP_E4M3> { static constexpr int v = 0; };   // FP8 E4M3
-template <> struct MfmaFmt<FP8MP_E5M2> { static constexpr int v = 1; };   // BF8 E5M2
+constexpr int kCRow = kBN * 2;            // bytes of one BF16 output row of the tile in LDS
+static_assert(kBM * kCRow <= 4 * kTileBytes, "the BF16 output tile must fit in the two stages");
 
 // Eight FP8 codes (two dwords) -> eight BF16 values, exactly.
 template <int FMT>
@@ -73,10 +72,9 @@ __device__ __forceinline__ v8bf widen8(uint32_t lo, uint32_t hi) {
   return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float y) {
-  const uint32_t u = __float_as_uint(y);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN, sign kept
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// Two floats -> two BF16 (low half = first), round to nearest even, NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{x, y}, v2bf));
 }
 
 // Byte offset of logical chunk c of tile row r inside one operand's LDS tile.
@@ -149,51 +147,24 @@ __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32
   }
 }
 
-// Accumulators of one wave's 128 x 64 tile: 8 x 4 blocks of 16 x 16 (FP8
-// MFMA) or 4 x 2 blocks of 32 x 32 (BF16 MFMA), 128 floats per lane either way.
-template <bool FP8_MFMA> struct Acc;
-template <> struct Acc<true> { v4f v[kFM][kFN]; };
-template <> struct Acc<false> { v16f v[kPM][kPN]; };
+// Accumulators of one wave's 128 x 64 tile: 4 x 2 blocks of 32 x 32, each
+// held transposed (see mma_step), 128 floats per lane.
+struct Acc { v16f v[kPM][kPN]; };
 
-// One K step on the FP8 MFMA: lane group g (lanes 16g .. 16g+15) feeds k bytes
-// 32g .. 32g+31 of the step (chunks 2g, 2g+1) of its row to one K=128 MFMA.
-template <int FA, int FB>
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<true>& acc, int wm, int wn,
-                                         int lane) {
-  const int g = lane >> 4;
-  v8i bfr[kFN];
-#pragma unroll
-  for (int j = 0; j < kFN; ++j) {
-    const int r = wn * kWN + j * 16 + (lane & 15);
-    const uint4 lo = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g));
-    const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g + 1));
-    bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  }
-#pragma unroll
-  for (int i = 0; i < kFM; ++i) {
-    const int r = wm * kWM + i * 16 + (lane & 15);
-    const uint4 lo = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g));
-    const uint4 hi = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g + 1));
-    const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-    for (int j = 0; j < kFN; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          afr, bfr[j], acc.v[i][j], MfmaFmt<FA>::v, MfmaFmt<FB>::v, 0, 127, 0, 127);
-  }
-}
-
-// One K step on the BF16 MFMA (32 x 32 x 16). Lane group G = lane / 32 owns
+// One K step (32 x 32 x 16 BF16 MFMAs). Lane group G = lane / 32 owns
 // chunks 4G .. 4G+3 (k bytes 64G .. 64G+63) of its row; sub-step s (0..7)
 // feeds bytes 64G + 8s .. +7, widened to BF16, as the lane's 8 k values.
 // A and B walk k in the same order, so products pair up and the 128-byte step
 // is covered once. Each 16-byte chunk read serves two sub-steps.
 //
+// Block (i, j) is accumulated as B_j . A_i^T: lane l, register r then holds
+// C[32 i + l % 32][32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of the wave's tile.
+//
 // Software pipeline: the fragments of chunk c+1 are read from LDS while chunk
 // c is multiplied, and the operands of each sub-step are widened while the
 // MFMAs of the sub-step before it run.
 template <int FA, int FB>
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<false>& acc, int wm, int wn,
-                                         int lane) {
+__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc& acc, int wm, int wn, int lane) {
   const int G = lane >> 5;
   const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
   uint4 aq[2][kPM], bq[2][kPN];
@@ -232,7 +203,7 @@ __device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, A
       for (int i = 0; i < kPM; ++i)
 #pragma unroll
         for (int j = 0; j < kPN; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bw[j], acc.v[i][j], 0, 0, 0);
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[j], aw[i], acc.v[i][j], 0, 0, 0);
       if (!last) {
 #pragma unroll
         for (int i = 0; i < kPM; ++i) aw[i] = an[i];
@@ -246,10 +217,10 @@ __device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, A
 // Issues the copy of the next K step into `nxt` and multiplies the step in
 // `cur`. The two stages never overlap; saying so (restrict) lets the compiler
 // keep the copy in flight while the fragments of `cur` are read.
-template <int FA, int FB, bool FP8_MFMA>
+template <int FA, int FB>
 __device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bool more,
                                                const TileCopy& ca, const TileCopy& cb, uint32_t k_next, uint32_t K,
-                                               Acc<FP8_MFMA>& acc, int wm, int wn, int wave, int lane) {
+                                               Acc& acc, int wm, int wn, int wave, int lane) {
   if (more) {
     load_tile(ca, k_next, K, nxt, wave);
     load_tile(cb, k_next, K, nxt + kTileBytes, wave);
@@ -257,12 +228,7 @@ __device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, 
   mma_step<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane);
 }
 
-__device__ __forceinline__ void store_bf16(uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t m,
-                                           int64_t n, float v) {
-  if (m < M && n < N) C[m * ldc + n] = f32_to_bf16_rne(v);
-}
-
-template <int FA, int FB, bool FP8_MFMA>
+template <int FA, int FB>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, const float* __restrict__ sb,
@@ -272,19 +238,22 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int nk = (int)((K + kBK - 1) / kBK);
+  const uint32_t Ku = (uint32_t)K;
+  const float s = *sa * *sb;
+  const bool vec = ((reinterpret_cast<uintptr_t>(C) | (uintptr_t)(ldc * 2)) & 15) == 0;
+
   int bm, bn;
   tile_coords(blockIdx.x, tm, tn, bm, bn);
   const int64_t m0 = (int64_t)bm * kBM, n0 = (int64_t)bn * kBN;
 
-  Acc<FP8_MFMA> acc;
+  Acc acc;
   float* accf = reinterpret_cast<float*>(&acc);
 #pragma unroll
   for (int e = 0; e < (int)(sizeof(acc) / sizeof(float)); ++e) accf[e] = 0.f;
 
-  const int nk = (int)((K + kBK - 1) / kBK);
   const TileCopy ca = make_copy(A, lda, m0, M, K, wave, lane);
   const TileCopy cb = make_copy(B, ldb, n0, N, K, wave, lane);
-  const uint32_t Ku = (uint32_t)K;
   if (nk > 0) {
     load_tile(ca, 0, Ku, smem, wave);
     load_tile(cb, 0, Ku, smem + kTileBytes, wave);
@@ -296,53 +265,78 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
     uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
     __syncthreads();
-    pipelined_step<FA, FB, FP8_MFMA>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn,
-                                     wave, lane);
+    pipelined_step<FA, FB>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn, wave, lane);
   }
 
-  const float s = *sa * *sb;
-  if constexpr (FP8_MFMA) {
-    // 16 x 16 blocks: lane holds C[4*(lane/16) + r][lane % 16].
-    const int64_t mb = m0 + wm * kWM + (lane >> 4) * 4, nb = n0 + wn * kWN + (lane & 15);
+  // Epilogue. Every wave must be done reading the last stage before the
+  // output tile overwrites it.
+  __syncthreads();
+  // BF16 tile in LDS: row r (0..255) at r * 512 bytes, its 16-byte chunk c
+  // (columns 8c .. 8c+7) at slot c ^ (r & 31). A lane's 8-byte piece (four
+  // columns) goes to the half chunk 4 (lane / 32) / 4 = lane / 32.
+  {
+    const int half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < kFM; ++i)
-#pragma unroll
-      for (int j = 0; j < kFN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) store_bf16(C, ldc, M, N, mb + i * 16 + r, nb + j * 16, acc.v[i][j][r] * s);
-  } else {
-    // 32 x 32 blocks: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane % 32].
-    const int64_t mb = m0 + wm * kWM + (lane >> 5) * 4, nb = n0 + wn * kWN + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < kPM; ++i)
+    for (int i = 0; i < kPM; ++i) {
+      const int row = wm * kWM + i * 32 + (lane & 31);
+      uint8_t* rp = smem + row * kCRow + half * 8;
 #pragma unroll
       for (int j = 0; j < kPN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          store_bf16(C, ldc, M, N, mb + i * 32 + 8 * (r / 4) + (r % 4), nb + j * 32, acc.v[i][j][r] * s);
+        for (int q = 0; q < 4; ++q) {
+          const int chunk = (wn * kWN + j * 32 + 8 * q) >> 3;
+          const v16f& a = acc.v[i][j];
+          const uint2 v = {pack_bf16(a[4 * q] * s, a[4 * q + 1] * s),
+                           pack_bf16(a[4 * q + 2] * s, a[4 * q + 3] * s)};
+          *reinterpret_cast<uint2*>(rp + ((chunk ^ (row & 31)) << 4)) = v;
+        }
+    }
+  }
+  __syncthreads();
+  // Write-out: each pass covers 16 rows, 32 threads per row, one 16-byte
+  // chunk each. Chunks wholly inside N go out as one 16-byte store when C
+  // and ldc allow it, the rest element by element.
+  const int c = tid & 31;
+  const int64_t gn = n0 + 8 * c;
+#pragma unroll 4
+  for (int p = 0; p < kBM / 16; ++p) {
+    const int row = p * 16 + (tid >> 5);
+    const int64_t gm = m0 + row;
+    if (gm >= M) break;
+    const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
+    uint16_t* dst = C + gm * ldc + gn;
+    if (vec && gn + 8 <= N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gn + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
   }
 }
 
-template <int FA, int FB, bool FP8_MFMA>
+template <int FA, int FB>
 hipError_t launch_pair(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n,
-                       int64_t k, const float* sa, const float* sb, uint16_t* c, int64_t ldc, hipStream_t stream) {
+                       int64_t k, const float* sa, const float* sb, uint16_t* c, int64_t ldc, int num_cus,
+                       hipStream_t stream) {
   const int tm = (int)((m + kBM - 1) / kBM), tn = (int)((n + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, FP8_MFMA>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream,
+  (void)num_cus;
+  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream,
                      a, lda, b, ldb, m, n, k, sa, sb, c, ldc, tm, tn);
   return hipGetLastError();
 }
 
-template <bool FP8_MFMA>
 hipError_t dispatch(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b, fp8mp_format b_fmt,
                     int64_t ldb, int64_t m, int64_t n, int64_t k, const float* sa, const float* sb, uint16_t* c,
-                    int64_t ldc, hipStream_t stream) {
+                    int64_t ldc, int num_cus, hipStream_t stream) {
   if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E4M3)
-    return launch_pair<FP8MP_E4M3, FP8MP_E4M3, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
+    return launch_pair<FP8MP_E4M3, FP8MP_E4M3>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
   if (a_fmt == FP8MP_E5M2 && b_fmt == FP8MP_E4M3)
-    return launch_pair<FP8MP_E5M2, FP8MP_E4M3, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
+    return launch_pair<FP8MP_E5M2, FP8MP_E4M3>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
   if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E5M2)
-    return launch_pair<FP8MP_E4M3, FP8MP_E5M2, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
-  return launch_pair<FP8MP_E5M2, FP8MP_E5M2, FP8_MFMA>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, stream);
+    return launch_pair<FP8MP_E4M3, FP8MP_E5M2>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
+  return launch_pair<FP8MP_E5M2, FP8MP_E5M2>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
 }
 
 }  // namespace
@@ -351,8 +345,7 @@ hipError_t launch_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
                               fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
                               const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
                               int64_t ldc, int num_cus, hipStream_t stream) {
-  (void)num_cus;
-  return dispatch<false>(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, stream);
+  return dispatch(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, num_cus, stream);
 }
 
 }  // namespace fp8mp
