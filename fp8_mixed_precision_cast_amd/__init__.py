@@ -23,7 +23,7 @@ from typing import Optional
 
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
-    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8mp_status_string",
+    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8mp_status_string",
     "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
 
@@ -63,6 +63,9 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_scaled_gemm.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp,
                                     i64, vp]
     lib.fp8_scaled_gemm.restype = ctypes.c_int
+    lib.fp8_scaled_gemm_amax_cast.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp,
+                                              vp, i64, ctypes.c_int, vp, vp, i64, vp, vp]
+    lib.fp8_scaled_gemm_amax_cast.restype = ctypes.c_int
     lib.fp8mp_status_string.argtypes = [ctypes.c_int]
     lib.fp8mp_status_string.restype = ctypes.c_char_p
     lib.fp8mp_device_info.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -156,6 +159,27 @@ def fp8_scaled_gemm(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None
     st = load_library().fp8_scaled_gemm(_ptr(a), FORMATS[a_fmt], lda, _ptr(b), FORMATS[b_fmt], ldb, m, n, k,
                                         _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(c), ldc, _stream(stream))
     _check(st, "fp8_scaled_gemm")
+
+
+def fp8_scaled_gemm_amax_cast(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt, y_scale=None, y_q=None,
+                              y_amax=None, stream=None) -> None:
+    """fp8_scaled_gemm, and in the same kernel y_amax = max(y_amax, max|c|), y_q = enc(c * y_scale)."""
+    m, k, lda = _rows_ld(a, "a")
+    n, kb, ldb = _rows_ld(b, "b")
+    if kb != k:
+        raise ValueError("a and b must share k")
+    mc, nc, ldc = _rows_ld(c, "c")
+    if (mc, nc) != (m, n):
+        raise ValueError("c must be m x n")
+    ld_yq = 0
+    if y_q is not None:
+        mq, nq, ld_yq = _rows_ld(y_q, "y_q")
+        if (mq, nq) != (m, n):
+            raise ValueError("y_q must be m x n")
+    st = load_library().fp8_scaled_gemm_amax_cast(
+        _ptr(a), FORMATS[a_fmt], lda, _ptr(b), FORMATS[b_fmt], ldb, m, n, k, _ptr(a_scale_inv), _ptr(b_scale_inv),
+        _ptr(c), ldc, FORMATS[y_fmt], _ptr(y_scale), _ptr(y_q), ld_yq, _ptr(y_amax), _stream(stream))
+    _check(st, "fp8_scaled_gemm_amax_cast")
 
 
 class DelayedScalingState:

@@ -130,6 +130,10 @@ __device__ __forceinline__ void block_amax_commit(uint32_t m, float* amax) {
   }
 }
 
+// Largest GEMM leading dimension in bytes: a 256-row tile then spans less
+// than 2^30 bytes, so its copies use 32-bit buffer offsets.
+constexpr int64_t kGemmMaxLd = int64_t(1) << 22;
+
 // Launchers (host side), one translation unit each.
 hipError_t launch_amax_cast(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
                             fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q,
@@ -141,5 +145,10 @@ hipError_t launch_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
                               fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
                               const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
                               int64_t ldc, int num_cus, hipStream_t stream);
+hipError_t launch_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
+                                        fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                                        const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
+                                        int64_t ldc, fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
+                                        int64_t ld_yq, float* y_amax, int num_cus, hipStream_t stream);
 
 }  // namespace fp8mp

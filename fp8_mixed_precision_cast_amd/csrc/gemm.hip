@@ -106,30 +106,38 @@ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& bm, in
 // slab & 1 = j & 1 (kSlabs is even): c takes one value on even slabs, c ^ 1
 // on odd ones.
 struct TileCopy {
-  __amdgpu_buffer_rsrc_t rsrc;   // whole operand; loads past its end return 0
+  __amdgpu_buffer_rsrc_t rsrc;   // this tile's rows of the operand; loads past their end return 0
   uint32_t base;                 // byte offset of row 8 * kSlabs * wave + lane / 8 at k = 0
   uint32_t stride8;              // 8 rows
   uint32_t kc0, kc1;             // c * 16 on even and odd slabs
   uint32_t row_ok;               // bit j: slab j's row exists
 };
 static_assert(kSlabs % 2 == 0, "slab parity must equal j parity");
+static_assert(kBM == kBN, "one copy geometry serves both operands");
 
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // above any operand (operands are < 2^31 bytes)
+// Leading dimensions are at most kGemmMaxLd bytes, so a tile's rows span less
+// than 2^30 bytes: every offset fits the 32-bit buffer offset, and
+// kOutOfRange lies above all of them.
+static_assert(kBM * kGemmMaxLd <= (int64_t(1) << 30), "tile span must fit 32-bit offsets");
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
+// The buffer resource starts at the tile's first row, so operands of any size
+// are addressed with 32-bit offsets.
 __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int64_t row0, int64_t rows, int64_t K,
                                               int wave, int lane) {
   TileCopy t;
-  const uint32_t bytes = (uint32_t)((rows - 1) * ld + K);
-  t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)G, (short)0, (int)bytes, 0x00020000);
+  const int64_t here = rows - row0 < kBM ? rows - row0 : kBM;   // rows of this tile that exist (>= 1)
+  const uint32_t bytes = (uint32_t)((here - 1) * ld + K);
+  t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(G + row0 * ld), (short)0, (int)bytes, 0x00020000);
   const int r = wave * 8 * kSlabs + (lane >> 3);
   const int c = (lane & 7) ^ ((lane >> 3) & 7);
   t.kc0 = (uint32_t)c * 16u;
   t.kc1 = (uint32_t)(c ^ 1) * 16u;
-  t.base = (uint32_t)((row0 + r) * ld);
+  t.base = (uint32_t)(r * ld);
   t.stride8 = (uint32_t)(8 * ld);
   t.row_ok = 0;
 #pragma unroll
-  for (int j = 0; j < kSlabs; ++j) t.row_ok |= (row0 + r + 8 * j < rows ? 1u : 0u) << j;
+  for (int j = 0; j < kSlabs; ++j) t.row_ok |= (r + 8 * j < here ? 1u : 0u) << j;
   return t;
 }
 
@@ -228,11 +236,19 @@ __device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, 
   mma_step<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane);
 }
 
-template <int FA, int FB>
+// No FP8 copy of the output (YF of the plain GEMM).
+constexpr int kNoY = -1;
+
+// YF = kNoY: the plain GEMM. YF = a format: the epilogue also runs the cast
+// of the BF16 output C on the fly, exactly as fp8_amax_cast would on C:
+// *y_amax = max(*y_amax, max|C|) (if y_amax) and y_q = enc_YF(C * *y_scale)
+// (if y_q).
+template <int FA, int FB, int YF>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, const float* __restrict__ sb,
-    uint16_t* __restrict__ C, int64_t ldc, int tm, int tn) {
+    uint16_t* __restrict__ C, int64_t ldc, int tm, int tn, const float* __restrict__ y_scale,
+    uint8_t* __restrict__ y_q, int64_t ld_yq, float* __restrict__ y_amax) {
   // Two stages, each an A tile followed by a B tile.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
 
@@ -295,48 +311,91 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   __syncthreads();
   // Write-out: each pass covers 16 rows, 32 threads per row, one 16-byte
   // chunk each. Chunks wholly inside N go out as one 16-byte store when C
-  // and ldc allow it, the rest element by element.
+  // and ldc allow it, the rest element by element. With a fused cast, the
+  // same eight BF16 values feed the amax and become eight codes of y_q.
   const int c = tid & 31;
   const int64_t gn = n0 + 8 * c;
+  const bool do_q = YF != kNoY && y_q != nullptr, do_amax = YF != kNoY && y_amax != nullptr;
+  const float ys = do_q ? *y_scale : 0.f;
+  const bool vq = ((reinterpret_cast<uintptr_t>(y_q) | (uintptr_t)ld_yq) & 7) == 0;
+  uint32_t am = 0;   // packed BF16 magnitudes of the in-range outputs
 #pragma unroll 4
   for (int p = 0; p < kBM / 16; ++p) {
     const int row = p * 16 + (tid >> 5);
     const int64_t gm = m0 + row;
     if (gm >= M) break;
     const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint16_t* dst = C + gm * ldc + gn;
-    if (vec && gn + 8 <= N) {
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (gn + 8 <= N) {
+      if (vec) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gn + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < 8; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+      if constexpr (YF != kNoY) {
+        if (do_amax) am = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(am, v.x), v.y), v.z), v.w);
+        if (do_q) {
+          const uint32_t q0 = enc4_bf16<YF>(w[0], w[1], ys), q1 = enc4_bf16<YF>(w[2], w[3], ys);
+          uint8_t* qd = y_q + gm * ld_yq + gn;
+          if (vq) {
+            *reinterpret_cast<uint2*>(qd) = uint2{q0, q1};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qd[e] = (uint8_t)((e < 4 ? q0 : q1) >> (8 * (e & 3)));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (gn + e >= N) break;
+        const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        dst[e] = (uint16_t)h;
+        if constexpr (YF != kNoY) {
+          if (do_amax) am = amax_bf16x2(am, h);
+          if (do_q) y_q[gm * ld_yq + gn + e] = enc1<YF>(__uint_as_float(h << 16), ys);
+        }
+      }
     }
+  }
+  if constexpr (YF != kNoY) {
+    if (do_amax) block_amax_commit<kThreads>(bf16x2_acc_to_f32_bits(am), y_amax);
   }
 }
 
-template <int FA, int FB>
-hipError_t launch_pair(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t m, int64_t n,
-                       int64_t k, const float* sa, const float* sb, uint16_t* c, int64_t ldc, int num_cus,
-                       hipStream_t stream) {
-  const int tm = (int)((m + kBM - 1) / kBM), tn = (int)((n + kBN - 1) / kBN);
-  (void)num_cus;
-  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream,
-                     a, lda, b, ldb, m, n, k, sa, sb, c, ldc, tm, tn);
+// Everything a launch needs besides the format templates.
+struct GemmArgs {
+  const uint8_t* a; int64_t lda;
+  const uint8_t* b; int64_t ldb;
+  int64_t m, n, k;
+  const float* sa; const float* sb;
+  uint16_t* c; int64_t ldc;
+  const float* y_scale; uint8_t* y_q; int64_t ld_yq; float* y_amax;
+};
+
+template <int FA, int FB, int YF>
+hipError_t launch_one(const GemmArgs& g, hipStream_t stream) {
+  const int tm = (int)((g.m + kBM - 1) / kBM), tn = (int)((g.n + kBN - 1) / kBN);
+  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, YF>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream, g.a,
+                     g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, tm, tn, g.y_scale, g.y_q, g.ld_yq,
+                     g.y_amax);
   return hipGetLastError();
 }
 
-hipError_t dispatch(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b, fp8mp_format b_fmt,
-                    int64_t ldb, int64_t m, int64_t n, int64_t k, const float* sa, const float* sb, uint16_t* c,
-                    int64_t ldc, int num_cus, hipStream_t stream) {
-  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E4M3)
-    return launch_pair<FP8MP_E4M3, FP8MP_E4M3>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
-  if (a_fmt == FP8MP_E5M2 && b_fmt == FP8MP_E4M3)
-    return launch_pair<FP8MP_E5M2, FP8MP_E4M3>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
-  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E5M2)
-    return launch_pair<FP8MP_E4M3, FP8MP_E5M2>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
-  return launch_pair<FP8MP_E5M2, FP8MP_E5M2>(a, lda, b, ldb, m, n, k, sa, sb, c, ldc, num_cus, stream);
+template <int FA, int FB>
+hipError_t launch_y(const GemmArgs& g, int y_fmt, hipStream_t stream) {
+  if (y_fmt == FP8MP_E4M3) return launch_one<FA, FB, FP8MP_E4M3>(g, stream);
+  if (y_fmt == FP8MP_E5M2) return launch_one<FA, FB, FP8MP_E5M2>(g, stream);
+  return launch_one<FA, FB, kNoY>(g, stream);
+}
+
+hipError_t dispatch(const GemmArgs& g, fp8mp_format a_fmt, fp8mp_format b_fmt, int y_fmt, hipStream_t stream) {
+  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E4M3) return launch_y<FP8MP_E4M3, FP8MP_E4M3>(g, y_fmt, stream);
+  if (a_fmt == FP8MP_E5M2 && b_fmt == FP8MP_E4M3) return launch_y<FP8MP_E5M2, FP8MP_E4M3>(g, y_fmt, stream);
+  if (a_fmt == FP8MP_E4M3 && b_fmt == FP8MP_E5M2) return launch_y<FP8MP_E4M3, FP8MP_E5M2>(g, y_fmt, stream);
+  return launch_y<FP8MP_E5M2, FP8MP_E5M2>(g, y_fmt, stream);
 }
 
 }  // namespace
@@ -345,7 +404,19 @@ hipError_t launch_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
                               fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
                               const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
                               int64_t ldc, int num_cus, hipStream_t stream) {
-  return dispatch(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, num_cus, stream);
+  (void)num_cus;
+  const GemmArgs g{a, lda, b, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, nullptr, nullptr, 0, nullptr};
+  return dispatch(g, a_fmt, b_fmt, kNoY, stream);
+}
+
+hipError_t launch_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
+                                        fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                                        const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
+                                        int64_t ldc, fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
+                                        int64_t ld_yq, float* y_amax, int num_cus, hipStream_t stream) {
+  (void)num_cus;
+  const GemmArgs g{a, lda, b, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, y_scale, y_q, ld_yq, y_amax};
+  return dispatch(g, a_fmt, b_fmt, y_fmt, stream);
 }
 
 }  // namespace fp8mp

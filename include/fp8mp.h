@@ -134,6 +134,37 @@ fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
                              const float* a_scale_inv, const float* b_scale_inv,
                              uint16_t* c, int64_t ldc, hipStream_t stream);
 
+/*
+ * fp8_scaled_gemm_amax_cast: fp8_scaled_gemm, and in the same kernel the cast
+ * of its BF16 output C for the next layer, with exactly the result of
+ * fp8_amax_cast(C, FP8MP_BF16, m, n, ldc, y_fmt, y_scale, y_q, ld_yq, NULL, 0,
+ * y_amax) run afterwards on C:
+ *   *y_amax = max(*y_amax, max |C|)      (if y_amax; NaN -> 0x7FC00000)
+ *   y_q[i][j] = enc_{y_fmt}(C[i][j] * *y_scale)   (if y_q; saturating RNE)
+ *
+ * [TE] §基本的なFP8トレーニングコードの構成: consecutive te.Linear layers feed one
+ * another, so the output of one is the FP8 operand of the next; under the
+ * delayed recipe ([TE] §動的スケーリングとFP8レシピの設定) that operand is cast with
+ * the next layer's current scale and its amax goes into that layer's
+ * history. Fusing the cast saves a read of C.
+ *
+ *   c        required, as for fp8_scaled_gemm (all its rules apply).
+ *   y_fmt    the format of y_q (validated even when y_q is NULL).
+ *   y_scale  one fp32 on the device; required when y_q is given.
+ *   y_q      m x n codes, leading dimension ld_yq (>= n), or NULL.
+ *   y_amax   one fp32 on the device, max-accumulated, or NULL.
+ * With y_q and y_amax both NULL the call equals fp8_scaled_gemm. y_q and
+ * y_amax must not overlap c, a or b.
+ */
+fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
+                                       const uint8_t* b, fp8mp_format b_fmt, int64_t ldb,
+                                       int64_t m, int64_t n, int64_t k,
+                                       const float* a_scale_inv, const float* b_scale_inv,
+                                       uint16_t* c, int64_t ldc,
+                                       fp8mp_format y_fmt, const float* y_scale,
+                                       uint8_t* y_q, int64_t ld_yq, float* y_amax,
+                                       hipStream_t stream);
+
 /* A static, human-readable name of a status code. Never NULL. */
 const char* fp8mp_status_string(fp8mp_status status);
 

@@ -22,8 +22,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = fp8.exported_symbols()
-    assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8mp_status_string",
-                     "fp8mp_device_info"]
+    assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast",
+                     "fp8mp_status_string", "fp8mp_device_info"]
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {fp8.lib_path()}").read()
@@ -77,6 +77,27 @@ def test_gemm_argument_validation(lib):
     assert f(*args(a=P(4096 + 8))) == UNSUPPORTED               # a not 16-byte aligned
     assert f(*args(c=P(4097))) == INVALID                       # c not 2-byte aligned
     assert f(*args(m=0)) == OK
+    assert f(*args(lda=2**22 + 16)) == UNSUPPORTED              # a tile's rows would pass 32-bit offsets
+    assert f(*args(ldb=2**22 + 16)) == UNSUPPORTED
+
+
+def test_fused_gemm_argument_validation(lib):
+    f = lib.fp8_scaled_gemm_amax_cast
+    args = lambda **kw: [kw.get("a", A16), kw.get("af", 0), kw.get("lda", 32), kw.get("b", A16), kw.get("bf", 0),
+                         kw.get("ldb", 32), kw.get("m", 4), kw.get("n", 8), kw.get("k", 32),
+                         kw.get("sa", A16), kw.get("sb", A16), kw.get("c", A16), kw.get("ldc", 8),
+                         kw.get("yf", 0), kw.get("ys", A16), kw.get("yq", A16), kw.get("ldq", 8),
+                         kw.get("ya", A16), None]
+    assert f(*args(af=3)) == INVALID                            # the GEMM's own rules apply
+    assert f(*args(c=None)) == INVALID
+    assert f(*args(lda=40)) == UNSUPPORTED
+    assert f(*args(yf=2)) == INVALID
+    assert f(*args(yf=2, yq=None, ya=None)) == INVALID          # y_fmt checked even without y outputs
+    assert f(*args(ys=None)) == INVALID                         # y_q needs a scale
+    assert f(*args(ldq=7)) == INVALID                           # ld_yq < n
+    assert f(*args(ys=P(4097), yq=None)) == INVALID             # misaligned scale
+    assert f(*args(ya=P(4098))) == INVALID                      # misaligned amax
+    assert f(*args(m=0)) == OK
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a device")
@@ -84,6 +105,10 @@ def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_scale_update(A16, 4, 0, 0, A16, A16, None) == NO_DEVICE
     assert lib.fp8_amax_cast(A16, 1, 4, 4, 4, 0, A16, A16, 4, None, 0, A16, None) == NO_DEVICE
     assert lib.fp8_scaled_gemm(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE
+    assert lib.fp8_scaled_gemm_amax_cast(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, 0, A16, A16, 8, A16,
+                                         None) == NO_DEVICE
+    # k == 0 with zero leading dimensions passes the host checks (no division by a zero ld)
+    assert lib.fp8_scaled_gemm(A16, 0, 0, A16, 0, 0, 4, 8, 0, A16, A16, A16, 8, None) == NO_DEVICE
     buf = ctypes.create_string_buffer(64)
     assert lib.fp8mp_device_info(buf, 64) == NO_DEVICE
 
