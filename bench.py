@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--workload", default="mlp7b_up_fwd")
     ap.add_argument("--recipe", default="delayed", choices=["delayed", "current"],
                     help="delayed scaling (the pages' default recipe) or just-in-time scaling")
+    ap.add_argument("--output-cast", default="none", choices=["none", "fused", "separate"],
+                    help="also cast the GEMM output to E4M3 for a next layer: in the GEMM epilogue or as a second pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
@@ -118,7 +120,8 @@ def main():
     info = fp8.fp8mp_device_info()
     inp = wl.load(w.name)
     dinp = {k: torch.from_numpy(v.view("int16")).cuda() for k, v in inp.items()}
-    plan = plan_from_workload(w, recipe=args.recipe)
+    plan = plan_from_workload(w, recipe=args.recipe,
+                              output_cast=None if args.output_cast == "none" else args.output_cast)
     stream = torch.cuda.current_stream()
     plan.prime(dinp)
     for _ in range(args.warmup):
@@ -126,7 +129,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
@@ -136,15 +139,18 @@ def main():
         e[1].record(stream)
         plan.gemm_all()
         e[2].record(stream)
-        plan.update_all()
+        plan.output_cast_all()
         e[3].record(stream)
+        plan.update_all()
+        e[4].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     step_s = (t1 - t0) / K
     cast_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    upd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    ocast_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    upd_ms = sum(e[3].elapsed_time(e[4]) for e in ev) / K
 
     flops = plan.gemm_flops()
     n_gemm = len(plan.gemms)
@@ -177,7 +183,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "m": g.m, "n": g.n, "k": g.k, "x": "bf16 N(0,1)+0.1% x20",
                    "w": "bf16 N(0,0.02)", "history_len": w.history_len, "margin": w.margin, "recipe": args.recipe,
-                   "parallelism": "single GPU"},
+                   "output_cast": args.output_cast, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_MFMA_TFLOPS, 4),
                      "traffic": traffic, "kernel": "gemm_fp8_kernel (bf16 MFMA on widened FP8)",
@@ -190,6 +196,10 @@ def main():
         },
         "device": info,
     }
+    if args.output_cast != "none":
+        out["components"]["output_cast"] = args.output_cast
+        out["components"]["output_cast_bytes"] = plan.output_cast_bytes()
+        out["components"]["separate_output_cast_ms"] = round(ocast_ms, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)

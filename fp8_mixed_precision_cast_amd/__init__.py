@@ -163,14 +163,17 @@ def fp8_scaled_gemm(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None
 
 def fp8_scaled_gemm_amax_cast(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt, y_scale=None, y_q=None,
                               y_amax=None, stream=None) -> None:
-    """fp8_scaled_gemm, and in the same kernel y_amax = max(y_amax, max|c|), y_q = enc(c * y_scale)."""
+    """fp8_scaled_gemm, and in the same kernel y_amax = max(y_amax, max|c|), y_q = enc(c * y_scale);
+    c may be None when y_q or y_amax is given (the BF16 output is then not stored)."""
     m, k, lda = _rows_ld(a, "a")
     n, kb, ldb = _rows_ld(b, "b")
     if kb != k:
         raise ValueError("a and b must share k")
-    mc, nc, ldc = _rows_ld(c, "c")
-    if (mc, nc) != (m, n):
-        raise ValueError("c must be m x n")
+    ldc = 0
+    if c is not None:
+        mc, nc, ldc = _rows_ld(c, "c")
+        if (mc, nc) != (m, n):
+            raise ValueError("c must be m x n")
     ld_yq = 0
     if y_q is not None:
         mq, nq, ld_yq = _rows_ld(y_q, "y_q")

@@ -66,13 +66,13 @@ bool is_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 // Host-side checks shared by the GEMM entry points (no device access).
 fp8mp_status check_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b, fp8mp_format b_fmt,
                         int64_t ldb, int64_t m, int64_t n, int64_t k, const float* a_scale_inv,
-                        const float* b_scale_inv, const uint16_t* c, int64_t ldc) {
+                        const float* b_scale_inv, const uint16_t* c, int64_t ldc, bool c_optional = false) {
   if (!valid_format(a_fmt) || !valid_format(b_fmt)) return FP8MP_ERR_INVALID_ARG;
   if (m < 0 || n < 0 || k < 0) return FP8MP_ERR_INVALID_ARG;
   if (m == 0 || n == 0) return FP8MP_OK;
-  if (c == nullptr || a_scale_inv == nullptr || b_scale_inv == nullptr) return FP8MP_ERR_INVALID_ARG;
+  if ((c == nullptr && !c_optional) || a_scale_inv == nullptr || b_scale_inv == nullptr) return FP8MP_ERR_INVALID_ARG;
   if (k > 0 && (a == nullptr || b == nullptr)) return FP8MP_ERR_INVALID_ARG;
-  if (lda < k || ldb < k || ldc < n) return FP8MP_ERR_INVALID_ARG;
+  if (lda < k || ldb < k || (c != nullptr && ldc < n)) return FP8MP_ERR_INVALID_ARG;
   if (!is_aligned(a_scale_inv, 4) || !is_aligned(b_scale_inv, 4)) return FP8MP_ERR_INVALID_ARG;
   if (k % 16 != 0) return FP8MP_ERR_UNSUPPORTED;
   if (k > 0 && (lda % 16 != 0 || ldb % 16 != 0 || !is_aligned(a, 16) || !is_aligned(b, 16)))
@@ -81,7 +81,8 @@ fp8mp_status check_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const
   // tile copies address at most 256 rows with 32-bit offsets
   if (k > 0 && (lda > fp8mp::kGemmMaxLd || ldb > fp8mp::kGemmMaxLd)) return FP8MP_ERR_UNSUPPORTED;
   // every row index product must stay inside int64 (lda, ldb may be 0 when k == 0)
-  if ((lda > 0 && m > (INT64_MAX / 8) / lda) || (ldb > 0 && n > (INT64_MAX / 8) / ldb) || m > (INT64_MAX / 8) / ldc)
+  if ((lda > 0 && m > (INT64_MAX / 8) / lda) || (ldb > 0 && n > (INT64_MAX / 8) / ldb) ||
+      (c != nullptr && m > (INT64_MAX / 8) / ldc))
     return FP8MP_ERR_UNSUPPORTED;
   if (((m + 127) / 128) * ((n + 127) / 128) > 0x7FFFFFFF) return FP8MP_ERR_UNSUPPORTED;
   return FP8MP_OK;
@@ -147,7 +148,8 @@ fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int
                                        const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
                                        int64_t ldc, fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
                                        int64_t ld_yq, float* y_amax, hipStream_t stream) {
-  fp8mp_status st = check_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc);
+  fp8mp_status st = check_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc,
+                               /*c_optional=*/y_q != nullptr || y_amax != nullptr);
   if (st != FP8MP_OK) return st;
   if (!valid_format(y_fmt)) return FP8MP_ERR_INVALID_ARG;
   if (y_q && (y_scale == nullptr || ld_yq < n)) return FP8MP_ERR_INVALID_ARG;

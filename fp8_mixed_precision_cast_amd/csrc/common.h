@@ -69,6 +69,19 @@ __device__ __forceinline__ uint32_t enc4(float x0, float x1, float x2, float x3,
   return r;
 }
 
+// enc4 without the side path: NaN bytes are patched with selects, so the
+// code is straight-line (for epilogues that convert many groups in a row).
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4_sel(float x0, float x1, float x2, float x3, float s) {
+  const float p0 = x0 * s, p1 = x1 * s, p2 = x2 * s, p3 = x3 * s;
+  uint32_t r = cvt4<FMT>(sat_clamp<FMT>(p0), sat_clamp<FMT>(p1), sat_clamp<FMT>(p2), sat_clamp<FMT>(p3));
+  r = p0 != p0 ? (r & 0xFFFFFF00u) | nan_code(x0, s) : r;
+  r = p1 != p1 ? (r & 0xFFFF00FFu) | (nan_code(x1, s) << 8) : r;
+  r = p2 != p2 ? (r & 0xFF00FFFFu) | (nan_code(x2, s) << 16) : r;
+  r = p3 != p3 ? (r & 0x00FFFFFFu) | (nan_code(x3, s) << 24) : r;
+  return r;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -76,6 +89,19 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 template <int FMT>
 __device__ __forceinline__ uint32_t enc4_bf16(uint32_t w0, uint32_t w1, float s) {
   return enc4<FMT>(bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1), s);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4_bf16_sel(uint32_t w0, uint32_t w1, float s) {
+  return enc4_sel<FMT>(bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1), s);
+}
+
+// Four BF16 values -> four codes when no product can be NaN (no NaN source,
+// and s finite and nonzero, so neither 0 * Inf nor Inf * 0 occurs).
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4_bf16_nonan(uint32_t w0, uint32_t w1, float s) {
+  return cvt4<FMT>(sat_clamp<FMT>(bf16_lo(w0) * s), sat_clamp<FMT>(bf16_hi(w0) * s), sat_clamp<FMT>(bf16_lo(w1) * s),
+                   sat_clamp<FMT>(bf16_hi(w1) * s));
 }
 
 // One source value -> one code (edge paths).

@@ -258,6 +258,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   const uint32_t Ku = (uint32_t)K;
   const float s = *sa * *sb;
   const bool vec = ((reinterpret_cast<uintptr_t>(C) | (uintptr_t)(ldc * 2)) & 15) == 0;
+  const bool do_c = YF == kNoY || C != nullptr;   // the fused call may skip the BF16 output
 
   int bm, bn;
   tile_coords(blockIdx.x, tm, tn, bm, bn);
@@ -310,52 +311,96 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   }
   __syncthreads();
   // Write-out: each pass covers 16 rows, 32 threads per row, one 16-byte
-  // chunk each. Chunks wholly inside N go out as one 16-byte store when C
-  // and ldc allow it, the rest element by element. With a fused cast, the
-  // same eight BF16 values feed the amax and become eight codes of y_q.
+  // chunk each. With a fused cast, the same eight BF16 values feed the amax
+  // and become eight codes of y_q.
   const int c = tid & 31;
   const int64_t gn = n0 + 8 * c;
   const bool do_q = YF != kNoY && y_q != nullptr, do_amax = YF != kNoY && y_amax != nullptr;
   const float ys = do_q ? *y_scale : 0.f;
   const bool vq = ((reinterpret_cast<uintptr_t>(y_q) | (uintptr_t)ld_yq) & 7) == 0;
   uint32_t am = 0;   // packed BF16 magnitudes of the in-range outputs
-#pragma unroll 4
-  for (int p = 0; p < kBM / 16; ++p) {
-    const int row = p * 16 + (tid >> 5);
-    const int64_t gm = m0 + row;
-    if (gm >= M) break;
-    const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint16_t* dst = C + gm * ldc + gn;
-    if (gn + 8 <= N) {
-      if (vec) {
-        *reinterpret_cast<uint4*>(dst) = v;
-      } else {
+  const bool full = m0 + kBM <= M && n0 + kBN <= N && vec && (!do_q || vq);
+  if (full) {
+    // Interior tile: all sixteen chunks are read first (the accumulators are
+    // dead, so the registers are free), then stored with 16-byte stores and
+    // converted without branches.
+    uint4 v[kBM / 16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-      }
-      if constexpr (YF != kNoY) {
-        if (do_amax) am = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(am, v.x), v.y), v.z), v.w);
-        if (do_q) {
-          const uint32_t q0 = enc4_bf16<YF>(w[0], w[1], ys), q1 = enc4_bf16<YF>(w[2], w[3], ys);
-          uint8_t* qd = y_q + gm * ld_yq + gn;
-          if (vq) {
-            *reinterpret_cast<uint2*>(qd) = uint2{q0, q1};
-          } else {
+    for (int p = 0; p < kBM / 16; ++p) {
+      const int row = p * 16 + (tid >> 5);
+      v[p] = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
+    }
+    if (do_c) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qd[e] = (uint8_t)((e < 4 ? q0 : q1) >> (8 * (e & 3)));
+      for (int p = 0; p < kBM / 16; ++p)
+        *reinterpret_cast<uint4*>(C + (m0 + p * 16 + (tid >> 5)) * ldc + gn) = v[p];
+    }
+    if constexpr (YF != kNoY) {
+      // Magnitude max of this thread's 128 values: the amax contribution,
+      // and the test for NaN sources.
+      uint32_t mx = 0;
+#pragma unroll
+      for (int p = 0; p < kBM / 16; ++p)
+        mx = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(mx, v[p].x), v[p].y), v[p].z), v[p].w);
+      if (do_amax) am = mx;
+      if (do_q) {
+        const uint32_t sb = __float_as_uint(ys) & 0x7FFFFFFFu;
+        const bool no_nan = (mx & 0xFFFFu) <= 0x7F80u && (mx >> 16) <= 0x7F80u && sb != 0u && sb < 0x7F800000u;
+        if (no_nan) {
+#pragma unroll
+          for (int p = 0; p < kBM / 16; ++p) {
+            const uint2 qq = {enc4_bf16_nonan<YF>(v[p].x, v[p].y, ys), enc4_bf16_nonan<YF>(v[p].z, v[p].w, ys)};
+            *reinterpret_cast<uint2*>(y_q + (m0 + p * 16 + (tid >> 5)) * ld_yq + gn) = qq;
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < kBM / 16; ++p) {
+            const uint2 qq = {enc4_bf16_sel<YF>(v[p].x, v[p].y, ys), enc4_bf16_sel<YF>(v[p].z, v[p].w, ys)};
+            *reinterpret_cast<uint2*>(y_q + (m0 + p * 16 + (tid >> 5)) * ld_yq + gn) = qq;
           }
         }
       }
-    } else {
+    }
+  } else {
+    // Edge tiles and unaligned outputs: row and column checks, element stores
+    // where a chunk straddles N or the layout forbids wide stores.
+    for (int p = 0; p < kBM / 16; ++p) {
+      const int row = p * 16 + (tid >> 5);
+      const int64_t gm = m0 + row;
+      if (gm >= M) break;
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint16_t* dst = C + gm * ldc + gn;
+      if (gn + 8 <= N) {
+        if (!do_c) {
+        } else if (vec) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (gn + e >= N) break;
-        const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        dst[e] = (uint16_t)h;
+          for (int e = 0; e < 8; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
         if constexpr (YF != kNoY) {
-          if (do_amax) am = amax_bf16x2(am, h);
-          if (do_q) y_q[gm * ld_yq + gn + e] = enc1<YF>(__uint_as_float(h << 16), ys);
+          if (do_amax) am = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(am, w[0]), w[1]), w[2]), w[3]);
+          if (do_q) {
+            const uint32_t q0 = enc4_bf16_sel<YF>(w[0], w[1], ys), q1 = enc4_bf16_sel<YF>(w[2], w[3], ys);
+            uint8_t* qd = y_q + gm * ld_yq + gn;
+            if (vq) {
+              *reinterpret_cast<uint2*>(qd) = uint2{q0, q1};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) qd[e] = (uint8_t)((e < 4 ? q0 : q1) >> (8 * (e & 3)));
+            }
+          }
+        }
+      } else {
+        for (int e = 0; e < 8; ++e) {
+          if (gn + e >= N) break;
+          const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          if (do_c) dst[e] = (uint16_t)h;
+          if constexpr (YF != kNoY) {
+            if (do_amax) am = amax_bf16x2(am, h);
+            if (do_q) y_q[gm * ld_yq + gn + e] = enc1<YF>(__uint_as_float(h << 16), ys);
+          }
         }
       }
     }

@@ -11,6 +11,12 @@ E4M3 in the forward pass and E5M2 in the backward pass. A step is:
   2. every GEMM, dequantised by the inverse scales those codes were made with;
   3. the delayed-scaling update of every tensor's scale.
 
+With ``output_cast`` the GEMM outputs are also cast to E4M3 for a following
+layer ([TE] §基本的なFP8トレーニングコードの構成 chains te.Linear layers), under the
+same delayed recipe with a state of their own: "fused" does it in the GEMM's
+epilogue (fp8_scaled_gemm_amax_cast), "separate" with a second pass over the
+BF16 output (fp8_amax_cast), the unfused reference.
+
 The plan owns its device buffers (allocated once, through torch); a step
 allocates nothing and never synchronises.
 """
@@ -21,7 +27,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import CurrentScalingState, DelayedScalingState, fp8_amax_cast, fp8_scale_update, fp8_scaled_gemm
+from . import (CurrentScalingState, DelayedScalingState, fp8_amax_cast, fp8_scale_update, fp8_scaled_gemm,
+               fp8_scaled_gemm_amax_cast)
 
 
 @dataclass(frozen=True)
@@ -43,13 +50,21 @@ class GemmOp:
 
 
 class LayerPlan:
-    """recipe "delayed" (the default) or "current" (just-in-time scaling: amax pass, update, cast)."""
+    """recipe "delayed" (the default) or "current" (just-in-time scaling: amax pass, update, cast);
+    output_cast None, "fused" or "separate" (delayed recipe only)."""
 
     def __init__(self, operands: Sequence[OperandSpec], gemms: Sequence[GemmOp], history_len: int = 1024,
-                 margin: int = 0, device: str = "cuda", recipe: str = "delayed"):
+                 margin: int = 0, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None):
         if recipe not in ("delayed", "current"):
             raise ValueError(recipe)
+        if output_cast not in (None, "fused", "separate"):
+            raise ValueError(output_cast)
+        if output_cast and recipe != "delayed":
+            raise ValueError("the output cast follows the delayed recipe (its amax is taken while casting)")
         self.recipe = recipe
+        self.output_cast = output_cast
+        self.ystate: Dict[str, DelayedScalingState] = {}
+        self.yq: Dict[str, torch.Tensor] = {}
         self.operands = {o.name: o for o in operands}
         self.gemms = list(gemms)
         self.state: Dict[str, DelayedScalingState] = {}
@@ -72,6 +87,9 @@ class LayerPlan:
                 raise ValueError(f"gemm {g.name}: K mismatch {tuple(a.shape)} vs {tuple(b.shape)}")
             c = torch.empty(a.shape[0], b.shape[0], dtype=torch.bfloat16, device=device)
             self.out[g.name] = c
+            if output_cast:
+                self.ystate[g.name] = DelayedScalingState("e4m3", history_len, margin, device)
+                self.yq[g.name] = torch.empty(a.shape[0], b.shape[0], dtype=torch.uint8, device=device)
             sa, sb = self.state[g.a], self.state[g.b]
             self._gemm_args.append((a, sa.fmt, b, sb.fmt, sa.scale_inv, sb.scale_inv, c))
 
@@ -83,6 +101,15 @@ class LayerPlan:
             fp8_amax_cast(inputs[name], st.fmt, None, None, None, st.amax_slot, stream)
         for st in self.state.values():
             st.update(stream)
+        if self.output_cast:
+            # the outputs' scales need the outputs: cast (without recording), multiply, record their amax
+            for name, st in self.state.items():
+                st.cast(inputs[name], self.q[name], self.qt[name], False, stream)
+            for g, (a, af, b, bf, sa, sb, c) in zip(self.gemms, self._gemm_args):
+                ys = self.ystate[g.name]
+                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c, ys.fmt, None, None, ys.amax_slot, stream)
+            for ys in self.ystate.values():
+                ys.update(stream)
 
     def cast_all(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
         for name, st in self.state.items():
@@ -92,18 +119,32 @@ class LayerPlan:
                 st.cast(inputs[name], self.q[name], self.qt[name], stream)
 
     def gemm_all(self, stream=None) -> None:
-        for a, af, b, bf, sa, sb, c in self._gemm_args:
-            fp8_scaled_gemm(a, af, b, bf, sa, sb, c, stream)
+        for g, (a, af, b, bf, sa, sb, c) in zip(self.gemms, self._gemm_args):
+            if self.output_cast == "fused":
+                ys = self.ystate[g.name]
+                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c, ys.fmt, ys.scale, self.yq[g.name], ys.amax_slot,
+                                          stream)
+            else:
+                fp8_scaled_gemm(a, af, b, bf, sa, sb, c, stream)
+
+    def output_cast_all(self, stream=None) -> None:
+        """The unfused output cast (a no-op unless output_cast == "separate")."""
+        if self.output_cast != "separate":
+            return
+        for g in self.gemms:
+            ys = self.ystate[g.name]
+            ys.cast(self.out[g.name], self.yq[g.name], None, True, stream)
 
     def update_all(self, stream=None) -> None:
         if self.recipe == "current":
             return
-        for st in self.state.values():
+        for st in list(self.state.values()) + list(self.ystate.values()):
             fp8_scale_update(st.history, st.fmt, st.margin, st.scale, st.scale_inv, stream)
 
     def step(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
         self.cast_all(inputs, stream)
         self.gemm_all(stream)
+        self.output_cast_all(stream)
         self.update_all(stream)
 
     def gemm_flops(self) -> int:
@@ -119,8 +160,16 @@ class LayerPlan:
             total += reads * n * inputs[name].element_size() + n * (int(o.plain) + int(o.transposed))
         return total
 
+    def output_cast_bytes(self) -> int:
+        """Algorithmic bytes of the output casts beyond the BF16 outputs themselves: the codes
+        written, plus (separate only) a second read of each output."""
+        total = 0
+        for c in self.out.values() if self.output_cast else ():
+            total += c.numel() * (1 + (2 if self.output_cast == "separate" else 0))
+        return total
 
-def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed") -> LayerPlan:
+
+def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None) -> LayerPlan:
     """A LayerPlan from a workload description with the attributes
     ``tensors`` (``name``, ``shape``), ``formats``, ``transposed``, ``gemms``
     (``name``, ``a``, ``a_transposed``, ``b``, ``b_transposed``), ``history_len``
@@ -128,4 +177,4 @@ def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed") -> Laye
     ops = [OperandSpec(t.name, tuple(t.shape), w.formats[t.name], t.name in w.transposed, True)
            for t in w.tensors]
     gemms = [GemmOp(g.name, g.a, g.a_transposed, g.b, g.b_transposed) for g in w.gemms]
-    return LayerPlan(ops, gemms, w.history_len, w.margin, device, recipe)
+    return LayerPlan(ops, gemms, w.history_len, w.margin, device, recipe, output_cast)

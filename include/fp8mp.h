@@ -148,7 +148,8 @@ fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
  * the next layer's current scale and its amax goes into that layer's
  * history. Fusing the cast saves a read of C.
  *
- *   c        required, as for fp8_scaled_gemm (all its rules apply).
+ *   c        as for fp8_scaled_gemm (all its rules apply), or NULL when y_q or
+ *            y_amax is given: the BF16 output is then computed but not stored.
  *   y_fmt    the format of y_q (validated even when y_q is NULL).
  *   y_scale  one fp32 on the device; required when y_q is given.
  *   y_q      m x n codes, leading dimension ld_yq (>= n), or NULL.

@@ -89,7 +89,7 @@ def test_fused_gemm_argument_validation(lib):
                          kw.get("yf", 0), kw.get("ys", A16), kw.get("yq", A16), kw.get("ldq", 8),
                          kw.get("ya", A16), None]
     assert f(*args(af=3)) == INVALID                            # the GEMM's own rules apply
-    assert f(*args(c=None)) == INVALID
+    assert f(*args(c=None, yq=None, ya=None)) == INVALID         # c may be NULL only with another output
     assert f(*args(lda=40)) == UNSUPPORTED
     assert f(*args(yf=2)) == INVALID
     assert f(*args(yf=2, yq=None, ya=None)) == INVALID          # y_fmt checked even without y outputs

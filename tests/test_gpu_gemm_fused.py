@@ -91,13 +91,15 @@ def test_fused_outputs_one_at_a_time_and_amax_accumulates():
 
 
 def test_fused_nan_outputs():
-    """A NaN code in A makes its output row NaN: the amax is the canonical NaN, the codes follow the sign rule."""
+    """A NaN code in A makes its output row NaN: the amax is the canonical NaN, the codes follow the sign rule;
+    zero and infinite output scales make NaN products out of infinite and zero outputs."""
     require_gpu()
     rng = np.random.default_rng(11)
     a, b = _codes(rng, (64, 128), "e4m3"), _codes(rng, (96, 128), "e4m3")
     a[5, 17] = 0x7F
     a[40, 3] = 0xFF
-    for ys in (1.0, -1.0):
+    a[7, :] = 0                       # a zero output row: 0 * Inf is NaN under an infinite scale
+    for ys in (1.0, -1.0, 0.0, float("inf"), float("-inf")):
         banner("fused-nan", ys)
         c = _fused(a, "e4m3", b, "e4m3", 1.0, 1.0, "e4m3", ys)
         assert np.isnan(oracle.gemm.bf16_bits_to_f64(c[5])).all()
@@ -128,3 +130,52 @@ def test_fused_full_size_mlp_shape():
     absr = oracle.gemm_abs_ref(a[rows], "e4m3", b[cols], "e4m3", sa, sb)
     ok, worst = oracle.gemm_check(cb[rows][:, cols], ref, absr)
     assert ok, worst
+
+
+def test_layer_plan_output_cast_fused_equals_separate():
+    """A chained layer step: the fused output cast and the separate second pass give the same codes,
+    histories and scales, and the codes are the oracle's cast of the BF16 output with the delayed scale."""
+    require_gpu()
+    from fp8_mixed_precision_cast_amd.linear import GemmOp, LayerPlan, OperandSpec
+    import workloads as wl
+    x = wl.small_normal(3, (300, 256), std=1.0, outlier_factor=20.0)
+    w = wl.small_normal(4, (520, 256), std=0.02)
+    inp = {"X": dev(x), "W": dev(w)}
+    ops = [OperandSpec("X", (300, 256), "e4m3"), OperandSpec("W", (520, 256), "e4m3")]
+    gem = [GemmOp("fwd", "X", False, "W", False)]
+    plans = {mode: LayerPlan(ops, gem, history_len=8, output_cast=mode) for mode in ("fused", "separate")}
+    for mode, plan in plans.items():
+        banner("plan-output-cast", mode)
+        plan.prime(inp)
+    for step in range(3):
+        for mode, plan in plans.items():
+            ys = plan.ystate["fwd"]
+            s_before = host(ys.scale)[0]
+            banner("plan-output-cast", mode, step)
+            plan.step(inp)
+            cb = host(plan.out["fwd"].view(torch.int16))
+            want = oracle.cast(cb, s_before, "e4m3", "bf16")
+            got = host(plan.yq["fwd"])
+            assert np.array_equal(got, want), (mode, step, first_diff(got, want))
+        f, s = plans["fused"], plans["separate"]
+        assert np.array_equal(host(f.yq["fwd"]), host(s.yq["fwd"]))
+        for attr in ("history", "scale", "scale_inv"):
+            a = host(getattr(f.ystate["fwd"], attr)).view(np.uint32)
+            b = host(getattr(s.ystate["fwd"], attr)).view(np.uint32)
+            assert np.array_equal(a, b), attr
+
+
+def test_fused_without_bf16_output():
+    """c = NULL: the codes and the amax are still those of the (unstored) BF16 output."""
+    require_gpu()
+    rng = np.random.default_rng(21)
+    for m, n, k in ((512, 768, 256), (300, 200, 64)):
+        a, b = _codes(rng, (m, k), "e4m3"), _codes(rng, (n, k), "e5m2")
+        banner("fused-no-c", m, n, k)
+        cb = _fused(a, "e4m3", b, "e5m2", 0.5, 2.0, "e4m3", 3.0)      # reference run with c
+        q = torch.empty(m, n, dtype=torch.uint8, device="cuda")
+        am = f32(0.0)
+        fp8.fp8_scaled_gemm_amax_cast(dev(a), "e4m3", dev(b), "e5m2", f32(0.5), f32(2.0), None, "e4m3", f32(3.0), q, am)
+        want = oracle.cast(cb, np.float32(3.0), "e4m3", "bf16")
+        assert np.array_equal(host(q), want), first_diff(host(q), want)
+        assert _bits(host(am)[0]) == _bits(oracle.amax(cb, "bf16"))
