@@ -23,7 +23,8 @@ from typing import Optional
 
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
-    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8mp_status_string",
+    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast",
+    "fp8mp_status_string",
     "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
 
@@ -66,6 +67,9 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_scaled_gemm_amax_cast.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp,
                                               vp, i64, ctypes.c_int, vp, vp, i64, vp, vp]
     lib.fp8_scaled_gemm_amax_cast.restype = ctypes.c_int
+    lib.fp8_layernorm_amax_cast.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, ctypes.c_float, vp, i64,
+                                            ctypes.c_int, vp, vp, i64, vp, vp, vp, vp]
+    lib.fp8_layernorm_amax_cast.restype = ctypes.c_int
     lib.fp8mp_status_string.argtypes = [ctypes.c_int]
     lib.fp8mp_status_string.restype = ctypes.c_char_p
     lib.fp8mp_device_info.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -183,6 +187,25 @@ def fp8_scaled_gemm_amax_cast(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y
         _ptr(a), FORMATS[a_fmt], lda, _ptr(b), FORMATS[b_fmt], ldb, m, n, k, _ptr(a_scale_inv), _ptr(b_scale_inv),
         _ptr(c), ldc, FORMATS[y_fmt], _ptr(y_scale), _ptr(y_q), ld_yq, _ptr(y_amax), _stream(stream))
     _check(st, "fp8_scaled_gemm_amax_cast")
+
+
+def fp8_layernorm_amax_cast(x, gamma, beta, eps, fmt, y=None, scale=None, q=None, amax=None, mean=None, rstd=None,
+                            stream=None) -> None:
+    """y = LayerNorm(x) * gamma + beta in BF16; in the same pass amax = max(amax, max|y|), q = enc(y * scale)."""
+    rows, cols, ld_x = _rows_ld(x, "x")
+    ld_y = ld_q = 0
+    if y is not None:
+        ry, cy, ld_y = _rows_ld(y, "y")
+        if (ry, cy) != (rows, cols):
+            raise ValueError("y must be rows x cols")
+    if q is not None:
+        rq, cq, ld_q = _rows_ld(q, "q")
+        if (rq, cq) != (rows, cols):
+            raise ValueError("q must be rows x cols")
+    st = load_library().fp8_layernorm_amax_cast(
+        _ptr(x), _src_dtype(x), rows, cols, ld_x, _ptr(gamma), _ptr(beta), float(eps), _ptr(y), ld_y, FORMATS[fmt],
+        _ptr(scale), _ptr(q), ld_q, _ptr(amax), _ptr(mean), _ptr(rstd), _stream(stream))
+    _check(st, "fp8_layernorm_amax_cast")
 
 
 class DelayedScalingState:

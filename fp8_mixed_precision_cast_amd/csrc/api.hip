@@ -10,6 +10,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <cmath>
+
 #include "common.h"
 
 namespace {
@@ -163,6 +165,32 @@ fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int
   return from_hip(fp8mp::launch_scaled_gemm_amax_cast(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv,
                                                       b_scale_inv, c, ldc, y_fmt, y_scale, y_q, ld_yq, y_amax,
                                                       cus, stream));
+}
+
+fp8mp_status fp8_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                     const float* gamma, const float* beta, float eps, uint16_t* y, int64_t ld_y,
+                                     fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax,
+                                     float* mean, float* rstd, hipStream_t stream) {
+  if (!valid_dtype(x_dtype) || !valid_format(fmt)) return FP8MP_ERR_INVALID_ARG;
+  if (rows < 0 || cols <= 0 || cols > INT32_MAX) return FP8MP_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps == INFINITY) return FP8MP_ERR_INVALID_ARG;   // also rejects NaN
+  if (rows == 0) return FP8MP_OK;
+  if (x == nullptr || gamma == nullptr || ld_x < cols) return FP8MP_ERR_INVALID_ARG;
+  if (y && ld_y < cols) return FP8MP_ERR_INVALID_ARG;
+  if (q && (scale == nullptr || ld_q < cols)) return FP8MP_ERR_INVALID_ARG;
+  if (!is_aligned(x, x_dtype == FP8MP_BF16 ? 2 : 4) || !is_aligned(gamma, 4) || (beta && !is_aligned(beta, 4)))
+    return FP8MP_ERR_INVALID_ARG;
+  if ((y && !is_aligned(y, 2)) || (scale && !is_aligned(scale, 4)) || (amax && !is_aligned(amax, 4)) ||
+      (mean && !is_aligned(mean, 4)) || (rstd && !is_aligned(rstd, 4)))
+    return FP8MP_ERR_INVALID_ARG;
+  if (rows > (INT64_MAX / 8) / ld_x || (y && rows > (INT64_MAX / 8) / ld_y) || (q && rows > (INT64_MAX / 8) / ld_q))
+    return FP8MP_ERR_UNSUPPORTED;
+  if (!y && !q && !amax && !mean && !rstd) return FP8MP_OK;
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  return from_hip(fp8mp::launch_layernorm_amax_cast(x, x_dtype, rows, cols, ld_x, gamma, beta, eps, y, ld_y, fmt,
+                                                    scale, q, ld_q, amax, mean, rstd, cus, stream));
 }
 
 const char* fp8mp_status_string(fp8mp_status status) {

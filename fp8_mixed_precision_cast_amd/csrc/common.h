@@ -136,7 +136,7 @@ __device__ __forceinline__ uint32_t canonical_nan(uint32_t m) {
   return m > 0x7F800000u ? 0x7FC00000u : m;
 }
 
-// Block-wide unsigned max, then one atomic per block into *amax.
+// Block-wide unsigned max, then at most one atomic per block into *amax.
 template <int BLOCK>
 __device__ __forceinline__ void block_amax_commit(uint32_t m, float* amax) {
   __shared__ uint32_t red[BLOCK / 64];
@@ -152,7 +152,12 @@ __device__ __forceinline__ void block_amax_commit(uint32_t m, float* amax) {
 #pragma unroll
     for (int w = 1; w < BLOCK / 64; ++w) r = r > red[w] ? r : red[w];
     r = canonical_nan(r);
-    if (r != 0u) atomicMax(reinterpret_cast<unsigned int*>(amax), r);
+    // amax only grows, so a block whose max does not exceed the value already
+    // there has nothing to add: the atomic is skipped. Same-address atomics
+    // serialize in L2, and most blocks end up skipping once a large value
+    // has landed.
+    unsigned int* a = reinterpret_cast<unsigned int*>(amax);
+    if (r != 0u && r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
   }
 }
 
@@ -176,5 +181,9 @@ hipError_t launch_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, in
                                         const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
                                         int64_t ldc, fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
                                         int64_t ld_yq, float* y_amax, int num_cus, hipStream_t stream);
+hipError_t launch_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                      const float* gamma, const float* beta, float eps, uint16_t* y, int64_t ld_y,
+                                      fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax,
+                                      float* mean, float* rstd, int num_cus, hipStream_t stream);
 
 }  // namespace fp8mp

@@ -166,6 +166,39 @@ fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int
                                        uint8_t* y_q, int64_t ld_yq, float* y_amax,
                                        hipStream_t stream);
 
+/*
+ * fp8_layernorm_amax_cast: LayerNorm over each row of x, its BF16 output, and
+ * in the same pass the cast of that output for the following FP8 linear layer.
+ *
+ * [TE] §基本的なFP8トレーニングコードの構成: nn.LayerNorm is swapped for the FP8-aware
+ * LayerNorm together with nn.Linear. The pages give no formula; the textbook
+ * form over the contiguous dimension is computed in FP32:
+ *   mu_i = mean_j x_ij, var_i = mean_j (x_ij - mu_i)^2 (divides by cols),
+ *   rstd_i = 1 / sqrt(var_i + eps),
+ *   y_ij = bf16_rne(((x_ij - mu_i) * rstd_i) * gamma_j + beta_j).
+ * The cast is exactly fp8_amax_cast(y, FP8MP_BF16, rows, cols, .., fmt, scale,
+ * q, ld_q, NULL, 0, amax) applied to that y:
+ *   *amax = max(*amax, max |y|)  (NaN -> 0x7FC00000), q = enc_fmt(y * *scale).
+ *
+ *   x      rows x cols source (x_dtype), leading dimension ld_x (>= cols).
+ *   gamma  cols fp32 (required); beta cols fp32 or NULL (zero).
+ *   eps    finite, >= 0.
+ *   y      rows x cols BF16, leading dimension ld_y (>= cols), or NULL.
+ *   q      rows x cols codes, leading dimension ld_q (>= cols), or NULL;
+ *          scale (one fp32 on the device) is required with q.
+ *   amax   one fp32 on the device, max-accumulated, or NULL.
+ *   mean, rstd  rows fp32 each (the row statistics, for a backward pass), or NULL.
+ * rows == 0 or no output is a no-op; cols must be >= 1. Any layout is
+ * accepted; BF16 rows with 16-byte alignment, cols a multiple of 8 (<= 16384),
+ * ld_x and ld_y multiples of 8, q 8-byte aligned with ld_q a multiple of 8 and
+ * gamma/beta 16-byte aligned take the single-read register path.
+ */
+fp8mp_status fp8_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols,
+                                     int64_t ld_x, const float* gamma, const float* beta, float eps,
+                                     uint16_t* y, int64_t ld_y, fp8mp_format fmt, const float* scale,
+                                     uint8_t* q, int64_t ld_q, float* amax, float* mean, float* rstd,
+                                     hipStream_t stream);
+
 /* A static, human-readable name of a status code. Never NULL. */
 const char* fp8mp_status_string(fp8mp_status status);
 

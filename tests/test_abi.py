@@ -23,7 +23,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = fp8.exported_symbols()
     assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast",
-                     "fp8mp_status_string", "fp8mp_device_info"]
+                     "fp8_layernorm_amax_cast", "fp8mp_status_string", "fp8mp_device_info"]
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {fp8.lib_path()}").read()
@@ -100,6 +100,32 @@ def test_fused_gemm_argument_validation(lib):
     assert f(*args(m=0)) == OK
 
 
+def test_layernorm_argument_validation(lib):
+    f = lib.fp8_layernorm_amax_cast
+    args = lambda **kw: [kw.get("x", A16), kw.get("dt", 1), kw.get("rows", 4), kw.get("cols", 8), kw.get("ldx", 8),
+                         kw.get("g", A16), kw.get("b", A16), kw.get("eps", 1e-5), kw.get("y", A16), kw.get("ldy", 8),
+                         kw.get("fmt", 0), kw.get("s", A16), kw.get("q", A16), kw.get("ldq", 8), kw.get("am", A16),
+                         kw.get("mu", None), kw.get("rs", None), None]
+    assert f(*args(dt=5)) == INVALID
+    assert f(*args(fmt=7)) == INVALID
+    assert f(*args(cols=0)) == INVALID
+    assert f(*args(rows=-1)) == INVALID
+    assert f(*args(eps=-1.0)) == INVALID
+    assert f(*args(eps=float("nan"))) == INVALID
+    assert f(*args(eps=float("inf"))) == INVALID
+    assert f(*args(x=None)) == INVALID
+    assert f(*args(g=None)) == INVALID                           # gamma required
+    assert f(*args(ldx=7)) == INVALID
+    assert f(*args(ldy=7)) == INVALID
+    assert f(*args(s=None)) == INVALID                           # q needs a scale
+    assert f(*args(ldq=7)) == INVALID
+    assert f(*args(x=P(4097))) == INVALID                        # misaligned bf16
+    assert f(*args(dt=0, x=P(4098))) == INVALID                  # misaligned f32
+    assert f(*args(g=P(4098))) == INVALID
+    assert f(*args(rows=0)) == OK
+    assert f(*args(y=None, q=None, am=None)) == OK               # nothing to write
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a device")
 def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_scale_update(A16, 4, 0, 0, A16, A16, None) == NO_DEVICE
@@ -107,6 +133,8 @@ def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_scaled_gemm(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE
     assert lib.fp8_scaled_gemm_amax_cast(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, 0, A16, A16, 8, A16,
                                          None) == NO_DEVICE
+    assert lib.fp8_layernorm_amax_cast(A16, 1, 4, 8, 8, A16, None, 1e-5, A16, 8, 0, A16, A16, 8, A16, None, None,
+                                       None) == NO_DEVICE
     # k == 0 with zero leading dimensions passes the host checks (no division by a zero ld)
     assert lib.fp8_scaled_gemm(A16, 0, 0, A16, 0, 0, 4, 8, 0, A16, A16, A16, 8, None) == NO_DEVICE
     buf = ctypes.create_string_buffer(64)
