@@ -42,6 +42,8 @@ def parse():
                     help="delayed scaling (the pages' default recipe) or just-in-time scaling")
     ap.add_argument("--output-cast", default="none", choices=["none", "fused", "separate"],
                     help="also cast the GEMM output to E4M3 for a next layer: in the GEMM epilogue or as a second pass")
+    ap.add_argument("--layernorm", action="store_true",
+                    help="X is LayerNorm(X) (gamma ~ N(1, 0.2), beta ~ N(0, 0.2), eps 1e-5), normalised and cast in one pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
@@ -120,8 +122,16 @@ def main():
     info = fp8.fp8mp_device_info()
     inp = wl.load(w.name)
     dinp = {k: torch.from_numpy(v.view("int16")).cuda() for k, v in inp.items()}
+    ln_params = None
+    if args.layernorm:
+        import numpy as np
+        rng = np.random.default_rng(20261202)
+        cols = inp["X"].shape[1]
+        ln_params = {"X": (torch.from_numpy(rng.normal(1.0, 0.2, cols).astype(np.float32)).cuda(),
+                           torch.from_numpy(rng.normal(0.0, 0.2, cols).astype(np.float32)).cuda(), 1e-5)}
     plan = plan_from_workload(w, recipe=args.recipe,
-                              output_cast=None if args.output_cast == "none" else args.output_cast)
+                              output_cast=None if args.output_cast == "none" else args.output_cast,
+                              layernorm=("X",) if args.layernorm else (), ln_params=ln_params)
     stream = torch.cuda.current_stream()
     plan.prime(dinp)
     for _ in range(args.warmup):
@@ -183,7 +193,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "m": g.m, "n": g.n, "k": g.k, "x": "bf16 N(0,1)+0.1% x20",
                    "w": "bf16 N(0,0.02)", "history_len": w.history_len, "margin": w.margin, "recipe": args.recipe,
-                   "output_cast": args.output_cast, "parallelism": "single GPU"},
+                   "output_cast": args.output_cast, "layernorm_x": bool(args.layernorm),
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_MFMA_TFLOPS, 4),
                      "traffic": traffic, "kernel": "gemm_fp8_kernel (bf16 MFMA on widened FP8)",

@@ -11,6 +11,11 @@ E4M3 in the forward pass and E5M2 in the backward pass. A step is:
   2. every GEMM, dequantised by the inverse scales those codes were made with;
   3. the delayed-scaling update of every tensor's scale.
 
+An operand marked ``layernorm`` is the LayerNorm of its source, normalised and
+cast in one pass (fp8_layernorm_amax_cast; [TE] §基本的なFP8トレーニングコードの構成
+swaps nn.LayerNorm along with nn.Linear); ``ln_params`` supplies its gamma,
+beta (device fp32) and eps.
+
 With ``output_cast`` the GEMM outputs are also cast to E4M3 for a following
 layer ([TE] §基本的なFP8トレーニングコードの構成 chains te.Linear layers), under the
 same delayed recipe with a state of their own: "fused" does it in the GEMM's
@@ -27,8 +32,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (CurrentScalingState, DelayedScalingState, fp8_amax_cast, fp8_scale_update, fp8_scaled_gemm,
-               fp8_scaled_gemm_amax_cast)
+from . import (CurrentScalingState, DelayedScalingState, fp8_amax_cast, fp8_layernorm_amax_cast,
+               fp8_scale_update, fp8_scaled_gemm, fp8_scaled_gemm_amax_cast)
 
 
 @dataclass(frozen=True)
@@ -38,6 +43,7 @@ class OperandSpec:
     fmt: str                  # "e4m3" or "e5m2"
     transposed: bool = False  # also produce the transposed codes
     plain: bool = True        # produce the row-major codes
+    layernorm: bool = False   # the operand is LayerNorm(source) (row-major codes only)
 
 
 @dataclass(frozen=True)
@@ -54,7 +60,8 @@ class LayerPlan:
     output_cast None, "fused" or "separate" (delayed recipe only)."""
 
     def __init__(self, operands: Sequence[OperandSpec], gemms: Sequence[GemmOp], history_len: int = 1024,
-                 margin: int = 0, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None):
+                 margin: int = 0, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None,
+                 ln_params: Optional[Dict[str, tuple]] = None):
         if recipe not in ("delayed", "current"):
             raise ValueError(recipe)
         if output_cast not in (None, "fused", "separate"):
@@ -63,6 +70,16 @@ class LayerPlan:
             raise ValueError("the output cast follows the delayed recipe (its amax is taken while casting)")
         self.recipe = recipe
         self.output_cast = output_cast
+        self.ln = {}
+        for o in operands:
+            if o.layernorm:
+                if o.transposed or not o.plain:
+                    raise ValueError(f"{o.name}: the LayerNorm path writes row-major codes only")
+                if recipe != "delayed":
+                    raise ValueError("the LayerNorm path follows the delayed recipe")
+                if not ln_params or o.name not in ln_params:
+                    raise ValueError(f"{o.name}: gamma, beta, eps missing")
+                self.ln[o.name] = ln_params[o.name]
         self.ystate: Dict[str, DelayedScalingState] = {}
         self.yq: Dict[str, torch.Tensor] = {}
         self.operands = {o.name: o for o in operands}
@@ -98,13 +115,23 @@ class LayerPlan:
         if self.recipe == "current":
             return
         for name, st in self.state.items():
-            fp8_amax_cast(inputs[name], st.fmt, None, None, None, st.amax_slot, stream)
+            if name in self.ln:
+                g, b, eps = self.ln[name]
+                fp8_layernorm_amax_cast(inputs[name], g, b, eps, st.fmt, None, None, None, st.amax_slot,
+                                        stream=stream)
+            else:
+                fp8_amax_cast(inputs[name], st.fmt, None, None, None, st.amax_slot, stream)
         for st in self.state.values():
             st.update(stream)
         if self.output_cast:
             # the outputs' scales need the outputs: cast (without recording), multiply, record their amax
             for name, st in self.state.items():
-                st.cast(inputs[name], self.q[name], self.qt[name], False, stream)
+                if name in self.ln:
+                    g, b, eps = self.ln[name]
+                    fp8_layernorm_amax_cast(inputs[name], g, b, eps, st.fmt, None, st.scale, self.q[name], None,
+                                            stream=stream)
+                else:
+                    st.cast(inputs[name], self.q[name], self.qt[name], False, stream)
             for g, (a, af, b, bf, sa, sb, c) in zip(self.gemms, self._gemm_args):
                 ys = self.ystate[g.name]
                 fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c, ys.fmt, None, None, ys.amax_slot, stream)
@@ -113,7 +140,11 @@ class LayerPlan:
 
     def cast_all(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
         for name, st in self.state.items():
-            if self.recipe == "delayed":
+            if name in self.ln:
+                g, b, eps = self.ln[name]
+                fp8_layernorm_amax_cast(inputs[name], g, b, eps, st.fmt, None, st.scale, self.q[name], st.amax_slot,
+                                        stream=stream)
+            elif self.recipe == "delayed":
                 st.cast(inputs[name], self.q[name], self.qt[name], True, stream)
             else:
                 st.cast(inputs[name], self.q[name], self.qt[name], stream)
@@ -169,12 +200,13 @@ class LayerPlan:
         return total
 
 
-def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None) -> LayerPlan:
+def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None,
+                       layernorm: Sequence[str] = (), ln_params: Optional[Dict[str, tuple]] = None) -> LayerPlan:
     """A LayerPlan from a workload description with the attributes
     ``tensors`` (``name``, ``shape``), ``formats``, ``transposed``, ``gemms``
     (``name``, ``a``, ``a_transposed``, ``b``, ``b_transposed``), ``history_len``
     and ``margin``."""
-    ops = [OperandSpec(t.name, tuple(t.shape), w.formats[t.name], t.name in w.transposed, True)
+    ops = [OperandSpec(t.name, tuple(t.shape), w.formats[t.name], t.name in w.transposed, True, t.name in layernorm)
            for t in w.tensors]
     gemms = [GemmOp(g.name, g.a, g.a_transposed, g.b, g.b_transposed) for g in w.gemms]
-    return LayerPlan(ops, gemms, w.history_len, w.margin, device, recipe, output_cast)
+    return LayerPlan(ops, gemms, w.history_len, w.margin, device, recipe, output_cast, ln_params)

@@ -150,3 +150,33 @@ def test_layernorm_full_size_activation():
     qh = host(q[torch.from_numpy(sel).cuda()])
     want = oracle.cast(yh[sel], np.float32(3.0), "e4m3", "bf16")
     assert np.array_equal(qh, want), first_diff(qh, want)
+
+
+def test_layer_plan_with_layernorm_operand():
+    """A layer step whose X operand is LayerNorm(X): its codes and recorded amax are those of the LayerNorm
+    output (taken from a separate call that also writes y), under the delayed scale; W takes the plain cast."""
+    require_gpu()
+    from fp8_mixed_precision_cast_amd.linear import GemmOp, LayerPlan, OperandSpec
+    x, g, b = _inputs(31, 256, 512)
+    w = wl.small_normal(32, (384, 512), std=0.02)
+    inp = {"X": dev(x), "W": dev(w)}
+    dg, db = dev(g), dev(b)
+    plan = LayerPlan([OperandSpec("X", (256, 512), "e4m3", layernorm=True), OperandSpec("W", (384, 512), "e4m3")],
+                     [GemmOp("fwd", "X", False, "W", False)], history_len=4, ln_params={"X": (dg, db, 1e-5)})
+    banner("plan-layernorm", "prime")
+    plan.prime(inp)
+    y = torch.empty(256, 512, dtype=torch.int16, device="cuda")
+    fp8.fp8_layernorm_amax_cast(inp["X"], dg, db, 1e-5, "e4m3", y)
+    yh = host(y)
+    for step in range(2):
+        st = plan.state["X"]
+        s_before = host(st.scale)[0]
+        banner("plan-layernorm", step)
+        plan.cast_all(inp)
+        want = oracle.cast(yh, s_before, "e4m3", "bf16")
+        got = host(plan.q["X"])
+        assert np.array_equal(got, want), first_diff(got, want)
+        assert _bits(host(st.history)[0]) == _bits(oracle.amax(yh, "bf16"))
+        plan.gemm_all()
+        plan.update_all()
+    assert _bits(host(plan.state["X"].scale)[0]) == _bits(np.float32(448.0) / oracle.amax(yh, "bf16"))
