@@ -48,10 +48,12 @@ from .codec import (FMT, FP8Format, decode, decode_table, encode, encode_scalar,
 from .recipe import (amax, cast, DelayedScaling, max_nan, primed_scale, update_scale)
 from .gemm import gemm_ref, gemm_abs_ref, gemm_bound, gemm_check, gemm_entry
 from .layernorm import layer_norm_bound, layer_norm_check, layer_norm_ref
+from .allreduce import reduce_bound, reduce_check, reduce_ref, shared_scale
 
 __all__ = [
     "FMT", "FP8Format", "decode", "decode_table", "encode", "encode_scalar", "bf16_to_f32",
     "amax", "cast", "DelayedScaling", "max_nan", "primed_scale", "update_scale",
     "gemm_ref", "gemm_abs_ref", "gemm_bound", "gemm_check", "gemm_entry",
     "layer_norm_ref", "layer_norm_bound", "layer_norm_check",
+    "shared_scale", "reduce_ref", "reduce_bound", "reduce_check",
 ]
