@@ -23,7 +23,7 @@ from typing import Optional
 
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
-    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast",
+    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale",
     "fp8mp_status_string",
     "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
@@ -70,6 +70,8 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_layernorm_amax_cast.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, ctypes.c_float, vp, i64,
                                             ctypes.c_int, vp, vp, i64, vp, vp, vp, vp]
     lib.fp8_layernorm_amax_cast.restype = ctypes.c_int
+    lib.fp8_reduce_shared_scale.argtypes = [vp, ctypes.c_int, i32, i64, i64, vp, vp, ctypes.c_int, vp]
+    lib.fp8_reduce_shared_scale.restype = ctypes.c_int
     lib.fp8mp_status_string.argtypes = [ctypes.c_int]
     lib.fp8mp_status_string.restype = ctypes.c_char_p
     lib.fp8mp_device_info.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -206,6 +208,20 @@ def fp8_layernorm_amax_cast(x, gamma, beta, eps, fmt, y=None, scale=None, q=None
         _ptr(x), _src_dtype(x), rows, cols, ld_x, _ptr(gamma), _ptr(beta), float(eps), _ptr(y), ld_y, FORMATS[fmt],
         _ptr(scale), _ptr(q), ld_q, _ptr(amax), _ptr(mean), _ptr(rstd), _stream(stream))
     _check(st, "fp8_layernorm_amax_cast")
+
+
+def fp8_reduce_shared_scale(q, fmt, scale_inv, out, stream=None) -> None:
+    """out = (sum over the leading dimension of dec(q)) * scale_inv; q is [ranks, numel] uint8 (row stride
+    is the rank stride), out a contiguous float32 or bfloat16 tensor of numel elements."""
+    if q.dim() != 2 or (q.shape[1] > 1 and q.stride(1) != 1):
+        raise ValueError("q must be [ranks, numel] with unit element stride")
+    n_ranks, numel = q.shape
+    if out.numel() != numel or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of numel elements")
+    st = load_library().fp8_reduce_shared_scale(_ptr(q), FORMATS[fmt], int(n_ranks), int(numel),
+                                                int(max(q.stride(0), numel)), _ptr(scale_inv), _ptr(out),
+                                                _src_dtype(out), _stream(stream))
+    _check(st, "fp8_reduce_shared_scale")
 
 
 class DelayedScalingState:

@@ -193,6 +193,22 @@ fp8mp_status fp8_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t
                                                     scale, q, ld_q, amax, mean, rstd, cus, stream));
 }
 
+fp8mp_status fp8_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t n_ranks, int64_t numel,
+                                     int64_t rank_stride, const float* scale_inv, void* out, fp8mp_dtype out_dtype,
+                                     hipStream_t stream) {
+  if (!valid_format(fmt) || !valid_dtype(out_dtype)) return FP8MP_ERR_INVALID_ARG;
+  if (n_ranks < 1 || numel < 0 || rank_stride < numel) return FP8MP_ERR_INVALID_ARG;
+  if (numel == 0) return FP8MP_OK;
+  if (q == nullptr || scale_inv == nullptr || out == nullptr) return FP8MP_ERR_INVALID_ARG;
+  if (!is_aligned(scale_inv, 4) || !is_aligned(out, out_dtype == FP8MP_BF16 ? 2 : 4)) return FP8MP_ERR_INVALID_ARG;
+  if (n_ranks > 1 && rank_stride > (INT64_MAX / 2) / (n_ranks - 1)) return FP8MP_ERR_UNSUPPORTED;
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  return from_hip(fp8mp::launch_reduce_shared_scale(q, fmt, n_ranks, numel, rank_stride, scale_inv, out, out_dtype,
+                                                    cus, stream));
+}
+
 const char* fp8mp_status_string(fp8mp_status status) {
   switch (status) {
     case FP8MP_OK: return "ok";

@@ -185,5 +185,8 @@ hipError_t launch_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_
                                       const float* gamma, const float* beta, float eps, uint16_t* y, int64_t ld_y,
                                       fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax,
                                       float* mean, float* rstd, int num_cus, hipStream_t stream);
+hipError_t launch_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t n_ranks, int64_t numel,
+                                      int64_t rank_stride, const float* scale_inv, void* out,
+                                      fp8mp_dtype out_dtype, int num_cus, hipStream_t stream);
 
 }  // namespace fp8mp

@@ -199,6 +199,33 @@ fp8mp_status fp8_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t
                                      uint8_t* q, int64_t ld_q, float* amax, float* mean, float* rstd,
                                      hipStream_t stream);
 
+/*
+ * fp8_reduce_shared_scale: the receive-side arithmetic of an FP8 gradient
+ * all-reduce whose ranks share one scale:
+ *   out[i] = round_out( (sum_{r=0}^{n_ranks-1} dec(q_r[i])) * (*scale_inv) ),
+ * the sum in FP32 in rank order starting from rank 0's value (so a lone -0
+ * stays -0), one multiply, then round to nearest even into out_dtype
+ * (FP8MP_BF16 or FP8MP_F32).
+ *
+ * [MPT] §横断的知見 "テンソルスケーリングが FP8 実用化の鍵": FP8-LM shares one scalar
+ * over all GPUs for its FP8 all-reduce, s'_g = min(s'_1, ..., s'_N). Since a
+ * rank's delayed-scaling scale does not increase with its amax, s'_g is the
+ * ordinary update (fp8_scale_update) of the largest amax over the ranks: one
+ * MAX all-reduce of the amax slots before the update gives every rank s'_g.
+ * Each rank then casts its gradient with s'_g (fp8_amax_cast) and the
+ * collective delivers the shards this call sums.
+ *
+ *   q            n_ranks blocks of numel codes in fmt; block r at q + r * rank_stride
+ *                (rank_stride >= numel).
+ *   scale_inv    one fp32 on the device: 1 / s'_g.
+ *   out          numel values of out_dtype.
+ * numel == 0 is a no-op. NaN codes give NaN; E5M2 infinities give infinities.
+ * 16-byte aligned q, out and rank_stride take 16-byte loads.
+ */
+fp8mp_status fp8_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t n_ranks, int64_t numel,
+                                     int64_t rank_stride, const float* scale_inv, void* out,
+                                     fp8mp_dtype out_dtype, hipStream_t stream);
+
 /* A static, human-readable name of a status code. Never NULL. */
 const char* fp8mp_status_string(fp8mp_status status);
 

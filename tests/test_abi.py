@@ -23,7 +23,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = fp8.exported_symbols()
     assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast",
-                     "fp8_layernorm_amax_cast", "fp8mp_status_string", "fp8mp_device_info"]
+                     "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8mp_status_string",
+                     "fp8mp_device_info"]
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {fp8.lib_path()}").read()
@@ -126,6 +127,23 @@ def test_layernorm_argument_validation(lib):
     assert f(*args(y=None, q=None, am=None)) == OK               # nothing to write
 
 
+def test_reduce_argument_validation(lib):
+    f = lib.fp8_reduce_shared_scale
+    args = lambda **kw: [kw.get("q", A16), kw.get("fmt", 1), kw.get("n", 4), kw.get("numel", 64),
+                         kw.get("stride", 64), kw.get("si", A16), kw.get("out", A16), kw.get("dt", 1), None]
+    assert f(*args(fmt=3)) == INVALID
+    assert f(*args(dt=9)) == INVALID
+    assert f(*args(n=0)) == INVALID
+    assert f(*args(numel=-1)) == INVALID
+    assert f(*args(stride=63)) == INVALID                     # ranks would overlap
+    assert f(*args(q=None)) == INVALID
+    assert f(*args(si=None)) == INVALID
+    assert f(*args(out=None)) == INVALID
+    assert f(*args(out=P(4097))) == INVALID                   # misaligned BF16 output
+    assert f(*args(dt=0, out=P(4098))) == INVALID             # misaligned FP32 output
+    assert f(*args(numel=0, stride=0)) == OK
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a device")
 def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_scale_update(A16, 4, 0, 0, A16, A16, None) == NO_DEVICE
@@ -135,6 +153,7 @@ def test_valid_calls_without_device_report_no_device(lib):
                                          None) == NO_DEVICE
     assert lib.fp8_layernorm_amax_cast(A16, 1, 4, 8, 8, A16, None, 1e-5, A16, 8, 0, A16, A16, 8, A16, None, None,
                                        None) == NO_DEVICE
+    assert lib.fp8_reduce_shared_scale(A16, 1, 4, 64, 64, A16, A16, 1, None) == NO_DEVICE
     # k == 0 with zero leading dimensions passes the host checks (no division by a zero ld)
     assert lib.fp8_scaled_gemm(A16, 0, 0, A16, 0, 0, 4, 8, 0, A16, A16, A16, 8, None) == NO_DEVICE
     buf = ctypes.create_string_buffer(64)
