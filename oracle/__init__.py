@@ -45,15 +45,17 @@ test under tests/):
 """
 from .codec import (FMT, FP8Format, decode, decode_table, encode, encode_scalar,
                     bf16_to_f32)
-from .recipe import (amax, cast, DelayedScaling, max_nan, primed_scale, update_scale)
+from .recipe import (amax, cast, DelayedScaling, max_nan, primed_scale, update_scale, update_scale_fmax)
 from .gemm import gemm_ref, gemm_abs_ref, gemm_bound, gemm_check, gemm_entry
 from .layernorm import layer_norm_bound, layer_norm_check, layer_norm_ref
 from .allreduce import reduce_bound, reduce_check, reduce_ref, shared_scale
+from .adam import adam_step_f64, adam_step_ref, f16_decode, f16_encode, update_fp16_scale
 
 __all__ = [
     "FMT", "FP8Format", "decode", "decode_table", "encode", "encode_scalar", "bf16_to_f32",
-    "amax", "cast", "DelayedScaling", "max_nan", "primed_scale", "update_scale",
+    "amax", "cast", "DelayedScaling", "max_nan", "primed_scale", "update_scale", "update_scale_fmax",
     "gemm_ref", "gemm_abs_ref", "gemm_bound", "gemm_check", "gemm_entry",
     "layer_norm_ref", "layer_norm_bound", "layer_norm_check",
     "shared_scale", "reduce_ref", "reduce_bound", "reduce_check",
+    "adam_step_ref", "adam_step_f64", "f16_encode", "f16_decode", "update_fp16_scale",
 ]

@@ -69,7 +69,14 @@ def cast(x, scale, fmt, dtype: str = "f32") -> np.ndarray:
 
 def update_scale(history: np.ndarray, scale: np.float32, scale_inv: np.float32,
                  fmt, margin: int):
-    """One delayed-scaling update. Returns (scale, scale_inv, rolled history).
+    """One delayed-scaling update for an FP8 format (see update_scale_fmax)."""
+    return update_scale_fmax(history, scale, scale_inv, _fmt(fmt).max, margin)
+
+
+def update_scale_fmax(history: np.ndarray, scale: np.float32, scale_inv: np.float32,
+                      fmax: float, margin: int):
+    """One delayed-scaling update towards a format whose largest value is fmax.
+    Returns (scale, scale_inv, rolled history).
 
     a_max = max over every history entry (NaN propagates). If a_max is finite
     and positive, s' = fp32(fp32(fmax / a_max) * 2**-margin), and if s' and
@@ -78,13 +85,12 @@ def update_scale(history: np.ndarray, scale: np.float32, scale_inv: np.float32,
     history rolls by one: entry i takes entry i-1's value and entry 0 becomes 0,
     ready to receive the next step's amax.
     """
-    f = _fmt(fmt)
     h = np.asarray(history, dtype=np.float32).copy()
     a_max = max_nan(h)
     new_scale, new_inv = np.float32(scale), np.float32(scale_inv)
     if math.isfinite(float(a_max)) and a_max > 0:
         with np.errstate(over="ignore"):
-            ratio = np.float32(f.max) / a_max                  # binary32 division, correctly rounded
+            ratio = np.float32(fmax) / a_max                   # binary32 division, correctly rounded
             s = np.float32(math.ldexp(float(ratio), -int(margin)))  # exact power-of-two step, one rounding
             inv = np.float32(1.0) / s if s > 0 else np.float32(np.inf)
         # a scale is usable only if it and its inverse are finite and positive
