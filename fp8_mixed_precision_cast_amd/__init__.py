@@ -23,14 +23,14 @@ from typing import Optional
 
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
-    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale",
+    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step", "AdamFP8State",
     "fp8mp_status_string",
     "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
 
-E4M3, E5M2 = 0, 1
+E4M3, E5M2, FP16 = 0, 1, 2
 F32, BF16 = 0, 1
-FORMATS = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+FORMATS = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2, "fp16": FP16, FP16: FP16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
@@ -72,6 +72,10 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_layernorm_amax_cast.restype = ctypes.c_int
     lib.fp8_reduce_shared_scale.argtypes = [vp, ctypes.c_int, i32, i64, i64, vp, vp, ctypes.c_int, vp]
     lib.fp8_reduce_shared_scale.restype = ctypes.c_int
+    fl = ctypes.c_float
+    lib.fp8_adam_step.argtypes = [i64, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  fl, fl, fl, fl, fl, fl, fl, vp]
+    lib.fp8_adam_step.restype = ctypes.c_int
     lib.fp8mp_status_string.argtypes = [ctypes.c_int]
     lib.fp8mp_status_string.restype = ctypes.c_char_p
     lib.fp8mp_device_info.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -222,6 +226,66 @@ def fp8_reduce_shared_scale(q, fmt, scale_inv, out, stream=None) -> None:
                                                 int(max(q.stride(0), numel)), _ptr(scale_inv), _ptr(out),
                                                 _src_dtype(out), _stream(stream))
     _check(st, "fp8_reduce_shared_scale")
+
+
+def fp8_adam_step(grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w, w_dq_in, w_dq_out, w_scale,
+                  w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2, stream=None) -> None:
+    """One Adam step over FP8 m (codes), FP16 v and tensor-scaled FP16 w (all updated in place)."""
+    n = grad.numel()
+    for t, name in ((m_q, "m_q"), (v, "v"), (w, "w")):
+        if t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with as many elements as grad")
+    if not grad.is_contiguous():
+        raise ValueError("grad must be contiguous")
+    st = load_library().fp8_adam_step(
+        n, _ptr(grad), _src_dtype(grad), _ptr(m_q), _ptr(m_dq_in), _ptr(m_dq_out), _ptr(m_scale), _ptr(m_scale_inv),
+        _ptr(m_amax), _ptr(v), _ptr(w), _ptr(w_dq_in), _ptr(w_dq_out), _ptr(w_scale), _ptr(w_scale_inv),
+        _ptr(w_amax), float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(bias_c1),
+        float(bias_c2), _stream(stream))
+    _check(st, "fp8_adam_step")
+
+
+class AdamFP8State:
+    """Adam state with decoupled precisions: m as E4M3 codes, v as FP16, master w as tensor-scaled FP16.
+
+    Both scales follow the delayed recipe (histories of history_len, margin).
+    The dequantisation factors of the stored m and w alternate between two
+    device floats (the step reads one and writes the other). Cold start: m = 0,
+    v = 0, scales 1, w stored with scale 1.
+    """
+
+    def __init__(self, w0, history_len: int = 16, margin: int = 0, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                 weight_decay=0.0):
+        import torch
+        dev = w0.device
+        self.n = w0.numel()
+        self.hp = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
+        self.t = 0
+        self.m_q = torch.zeros(self.n, dtype=torch.uint8, device=dev)
+        self.v = torch.zeros(self.n, dtype=torch.float16, device=dev)
+        self.w = w0.detach().reshape(-1).to(torch.float16).clone()
+        self.m_state = DelayedScalingState("e4m3", history_len, margin, dev)
+        self.w_state = DelayedScalingState("fp16", history_len, margin, dev)
+        self.m_dq = torch.ones(2, dtype=torch.float32, device=dev)
+        self.w_dq = torch.ones(2, dtype=torch.float32, device=dev)
+        self.cur = 0
+
+    def step(self, grad, stream=None) -> None:
+        self.t += 1
+        b1, b2 = self.hp["beta1"], self.hp["beta2"]
+        c1, c2 = 1.0 / (1.0 - b1 ** self.t), 1.0 / (1.0 - b2 ** self.t)
+        i, o = self.cur, 1 - self.cur
+        ms, ws = self.m_state, self.w_state
+        fp8_adam_step(grad.reshape(-1), self.m_q, self.m_dq[i:i + 1], self.m_dq[o:o + 1], ms.scale, ms.scale_inv,
+                      ms.amax_slot, self.v, self.w, self.w_dq[i:i + 1], self.w_dq[o:o + 1], ws.scale, ws.scale_inv,
+                      ws.amax_slot, self.hp["lr"], b1, b2, self.hp["eps"], self.hp["weight_decay"], c1, c2, stream)
+        ms.update(stream)
+        ws.update(stream)
+        self.cur = o
+
+    def master_weights(self):
+        """The master weights as float32 (decoded FP16 times the current dequantisation factor)."""
+        return self.w.float() * self.w_dq[self.cur]
 
 
 class DelayedScalingState:

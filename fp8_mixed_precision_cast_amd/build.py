@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8mp.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "cast.hip", "scale_update.hip", "gemm.hip", "layernorm.hip", "reduce.hip"]
+SOURCES = ["api.hip", "cast.hip", "scale_update.hip", "gemm.hip", "layernorm.hip", "reduce.hip", "adam.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

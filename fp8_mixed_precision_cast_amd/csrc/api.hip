@@ -120,7 +120,7 @@ fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int
 
 fp8mp_status fp8_scale_update(float* amax_history, int32_t history_len, fp8mp_format fmt, int32_t margin,
                               float* scale, float* scale_inv, hipStream_t stream) {
-  if (!valid_format(fmt)) return FP8MP_ERR_INVALID_ARG;
+  if (!valid_format(fmt) && fmt != FP8MP_FP16) return FP8MP_ERR_INVALID_ARG;
   if (amax_history == nullptr || scale == nullptr || scale_inv == nullptr) return FP8MP_ERR_INVALID_ARG;
   if (history_len < 1 || margin < 0) return FP8MP_ERR_INVALID_ARG;
   if (!is_aligned(amax_history, 4) || !is_aligned(scale, 4) || !is_aligned(scale_inv, 4))
@@ -207,6 +207,35 @@ fp8mp_status fp8_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t
   if (st != FP8MP_OK) return st;
   return from_hip(fp8mp::launch_reduce_shared_scale(q, fmt, n_ranks, numel, rank_stride, scale_inv, out, out_dtype,
                                                     cus, stream));
+}
+
+fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uint8_t* m_q, const float* m_dq_in,
+                           float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax,
+                           uint16_t* v, uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
+                           const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
+                           float weight_decay, float bias_c1, float bias_c2, hipStream_t stream) {
+  if (!valid_dtype(grad_dtype) || n < 0) return FP8MP_ERR_INVALID_ARG;
+  if (n == 0) return FP8MP_OK;
+  const void* required[] = {grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, v, w, w_dq_in, w_dq_out,
+                            w_scale, w_scale_inv};
+  for (const void* p : required)
+    if (p == nullptr) return FP8MP_ERR_INVALID_ARG;
+  if (m_dq_out == m_dq_in || w_dq_out == w_dq_in || m_dq_out == w_dq_out) return FP8MP_ERR_INVALID_ARG;
+  const float* scalars[] = {m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, w_dq_in, w_dq_out, w_scale, w_scale_inv,
+                            w_amax};
+  for (const float* p : scalars)
+    if (p != nullptr && !is_aligned(p, 4)) return FP8MP_ERR_INVALID_ARG;
+  if (!is_aligned(grad, grad_dtype == FP8MP_BF16 ? 2 : 4) || !is_aligned(v, 2) || !is_aligned(w, 2))
+    return FP8MP_ERR_INVALID_ARG;
+  const float hp[] = {lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2};
+  for (float x : hp)
+    if (!std::isfinite(x)) return FP8MP_ERR_INVALID_ARG;
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  return from_hip(fp8mp::launch_adam_step(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax,
+                                          v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2,
+                                          eps, weight_decay, bias_c1, bias_c2, cus, stream));
 }
 
 const char* fp8mp_status_string(fp8mp_status status) {

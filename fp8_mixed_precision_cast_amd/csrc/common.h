@@ -20,6 +20,11 @@ template <> struct Fp8Traits<FP8MP_E5M2> {
   static constexpr float kMax = 57344.0f;
   static constexpr uint32_t kMaxBits = 0x47600000u;   // 57344.0f
 };
+// Tensor-scaled FP16 storage (scale updates only): [MPT] §定義 table, 65504.
+template <> struct Fp8Traits<FP8MP_FP16> {
+  static constexpr float kMax = 65504.0f;
+  static constexpr uint32_t kMaxBits = 0x477FE000u;   // 65504.0f
+};
 
 // Clamp to [-fmax, fmax] so the hardware conversion never overflows (it is
 // not saturating: 512 would become the E4M3 NaN code). Infinities clamp to
@@ -185,6 +190,11 @@ hipError_t launch_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_
                                       const float* gamma, const float* beta, float eps, uint16_t* y, int64_t ld_y,
                                       fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax,
                                       float* mean, float* rstd, int num_cus, hipStream_t stream);
+hipError_t launch_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uint8_t* m_q, const float* m_dq_in,
+                            float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax,
+                            uint16_t* v, uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
+                            const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, float bias_c1, float bias_c2, int num_cus, hipStream_t stream);
 hipError_t launch_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t n_ranks, int64_t numel,
                                       int64_t rank_stride, const float* scale_inv, void* out,
                                       fp8mp_dtype out_dtype, int num_cus, hipStream_t stream);

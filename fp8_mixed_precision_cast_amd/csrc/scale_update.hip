@@ -96,6 +96,9 @@ hipError_t launch_scale_update(float* history, int32_t len, fp8mp_format fmt, in
   if (fmt == FP8MP_E4M3)
     hipLaunchKernelGGL((scale_update_kernel<FP8MP_E4M3>), dim3(1), dim3(kBlock), 0, stream, history, len,
                        margin, scale, scale_inv);
+  else if (fmt == FP8MP_FP16)
+    hipLaunchKernelGGL((scale_update_kernel<FP8MP_FP16>), dim3(1), dim3(kBlock), 0, stream, history, len,
+                       margin, scale, scale_inv);
   else
     hipLaunchKernelGGL((scale_update_kernel<FP8MP_E5M2>), dim3(1), dim3(kBlock), 0, stream, history, len,
                        margin, scale, scale_inv);

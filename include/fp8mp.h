@@ -39,8 +39,11 @@ extern "C" {
 
 /* FP8 formats. [TE] §NVIDIA Transformer EngineとFP8混合精度とは: E4M3 has 4 exponent
  * and 3 mantissa bits and suits the forward pass, E5M2 has 5 and 2 and suits
- * the backward pass. [MPT] §定義 precision table: largest values 448 and 57344. */
-typedef enum { FP8MP_E4M3 = 0, FP8MP_E5M2 = 1 } fp8mp_format;
+ * the backward pass. [MPT] §定義 precision table: largest values 448 and 57344.
+ * FP8MP_FP16 (largest value 65504, same table) names tensor-scaled FP16
+ * storage; only fp8_scale_update accepts it (the FP16 master weights of
+ * fp8_adam_step), every other entry point rejects it. */
+typedef enum { FP8MP_E4M3 = 0, FP8MP_E5M2 = 1, FP8MP_FP16 = 2 } fp8mp_format;
 
 /* Source element types of the cast: fp32, or BF16 passed as 16-bit patterns. */
 typedef enum { FP8MP_F32 = 0, FP8MP_BF16 = 1 } fp8mp_dtype;
@@ -98,6 +101,7 @@ fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int
  *
  * a = max over all entries (NaN propagates). If a is finite and > 0:
  *   s' = fp32(fp32(fmax / a) * 2^-margin)   (IEEE division, exact power-of-two step)
+ * with fmax = 448 (E4M3), 57344 (E5M2) or 65504 (FP8MP_FP16 storage)
  * and if s' and fp32(1 / s') are finite and > 0 they replace scale and
  * scale_inv; otherwise both are held. Then the history rolls by one entry
  * (entry i takes entry i-1, entry 0 becomes +0). history_len >= 1, margin >= 0.
@@ -225,6 +229,46 @@ fp8mp_status fp8_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t
 fp8mp_status fp8_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t n_ranks, int64_t numel,
                                      int64_t rank_stride, const float* scale_inv, void* out,
                                      fp8mp_dtype out_dtype, hipStream_t stream);
+
+/*
+ * fp8_adam_step: one Adam step over decoupled-precision optimizer state.
+ *
+ * [MPT] §定義 (precision sensitivity of training variables) and §横断的知見
+ * "精度分離 (Precision Decoupling)": the first moment tolerates FP8; the second
+ * moment and the master weights need more. FP8-LM keeps m in FP8, v in FP16
+ * and the master weights in FP16 with tensor scaling (6 bytes per parameter
+ * instead of 16). Per parameter, in binary32 in this order (no contraction):
+ *   g = grad; m = dec_e4m3(m_q) * m_dq_in; v = fp16 v; w = fp16 w * w_dq_in
+ *   m = beta1 * m + (1 - beta1) * g
+ *   v = beta2 * v + (1 - beta2) * (g * g)
+ *   u = (m * bias_c1) / (sqrt(v * bias_c2) + eps)
+ *   w = w - lr * (u + weight_decay * w)
+ *   m_q = enc_e4m3(m * m_scale); v = fp16(v); w = fp16(w * w_scale)
+ * (FP16 stores: round to nearest even, saturating at +-65504; the FP8 store is
+ * the saturating cast of fp8_amax_cast.) *m_amax = max(*m_amax, max |m|) and
+ * *w_amax = max(*w_amax, max |w|) feed the delayed updates of m_scale (E4M3)
+ * and w_scale (FP8MP_FP16) by fp8_scale_update. *m_dq_out = *m_scale_inv and
+ * *w_dq_out = *w_scale_inv: the dequantisation factors of what this step
+ * wrote, to be passed as m_dq_in / w_dq_in next step (the out pointers must
+ * differ from the in pointers; a caller alternates two of each).
+ *
+ *   n                 parameters (0: no-op).
+ *   grad              n values, FP8MP_BF16 or FP8MP_F32.
+ *   m_q, v, w         n bytes / n FP16 / n FP16, read and written in place.
+ *   m_dq_in, w_dq_in, m_scale, m_scale_inv, w_scale, w_scale_inv
+ *                     one fp32 each on the device (read).
+ *   m_dq_out, w_dq_out  one fp32 each (written).
+ *   m_amax, w_amax    one fp32 each (max-accumulated) or NULL.
+ *   bias_c1, bias_c2  1 / (1 - beta1^t) and 1 / (1 - beta2^t) for step t.
+ */
+fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype,
+                           uint8_t* m_q, const float* m_dq_in, float* m_dq_out,
+                           const float* m_scale, const float* m_scale_inv, float* m_amax,
+                           uint16_t* v,
+                           uint16_t* w, const float* w_dq_in, float* w_dq_out,
+                           const float* w_scale, const float* w_scale_inv, float* w_amax,
+                           float lr, float beta1, float beta2, float eps, float weight_decay,
+                           float bias_c1, float bias_c2, hipStream_t stream);
 
 /* A static, human-readable name of a status code. Never NULL. */
 const char* fp8mp_status_string(fp8mp_status status);

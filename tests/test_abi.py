@@ -23,8 +23,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = fp8.exported_symbols()
     assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast",
-                     "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8mp_status_string",
-                     "fp8mp_device_info"]
+                     "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step",
+                     "fp8mp_status_string", "fp8mp_device_info"]
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {fp8.lib_path()}").read()
@@ -144,6 +144,28 @@ def test_reduce_argument_validation(lib):
     assert f(*args(numel=0, stride=0)) == OK
 
 
+def test_adam_argument_validation(lib):
+    f = lib.fp8_adam_step
+    B = [P(4096 + 16 * i) for i in range(12)]     # distinct fake aligned addresses
+    def args(**kw):
+        a = dict(n=64, g=B[0], gd=1, mq=B[1], mdi=B[2], mdo=B[3], ms=B[4], msi=B[5], ma=None, v=B[6], w=B[7],
+                 wdi=B[8], wdo=B[9], ws=B[10], wsi=B[11], wa=None, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0,
+                 c1=10.0, c2=1000.0)
+        a.update(kw)
+        return [a[k] for k in ("n", "g", "gd", "mq", "mdi", "mdo", "ms", "msi", "ma", "v", "w", "wdi", "wdo", "ws",
+                               "wsi", "wa", "lr", "b1", "b2", "eps", "wd", "c1", "c2")] + [None]
+    assert f(*args(gd=4)) == INVALID
+    assert f(*args(n=-1)) == INVALID
+    assert f(*args(g=None)) == INVALID
+    assert f(*args(mdo=B[2])) == INVALID                      # dequantisation factor read and written in place
+    assert f(*args(wdo=B[8])) == INVALID
+    assert f(*args(lr=float("nan"))) == INVALID
+    assert f(*args(c2=float("inf"))) == INVALID
+    assert f(*args(v=P(4097))) == INVALID
+    assert f(*args(n=0)) == OK
+    assert lib.fp8_amax_cast(A16, 1, 4, 4, 4, 2, A16, A16, 4, None, 0, None, None) == INVALID   # not for casts
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a device")
 def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_scale_update(A16, 4, 0, 0, A16, A16, None) == NO_DEVICE
@@ -154,6 +176,7 @@ def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_layernorm_amax_cast(A16, 1, 4, 8, 8, A16, None, 1e-5, A16, 8, 0, A16, A16, 8, A16, None, None,
                                        None) == NO_DEVICE
     assert lib.fp8_reduce_shared_scale(A16, 1, 4, 64, 64, A16, A16, 1, None) == NO_DEVICE
+    assert lib.fp8_scale_update(A16, 4, 2, 0, A16, A16, None) == NO_DEVICE          # FP16 storage accepted
     # k == 0 with zero leading dimensions passes the host checks (no division by a zero ld)
     assert lib.fp8_scaled_gemm(A16, 0, 0, A16, 0, 0, 4, 8, 0, A16, A16, A16, 8, None) == NO_DEVICE
     buf = ctypes.create_string_buffer(64)
