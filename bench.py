@@ -101,6 +101,27 @@ def cpu_baseline(w, inp, min_seconds: float = 10.0):
                       f"update) in {total:.1f} s; elementwise stages single-threaded, BLAS on {threads} threads"}
 
 
+def cold_cast_gbps(plan, dinp, reps: int = 5):
+    """The casts timed after the 256 MB MALL has been flushed by writing a 1 GiB buffer, so the sources
+    and codes come from HBM (GB/s of algorithmic bytes, median over reps)."""
+    import torch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plan.cast_all(dinp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del flush
+    times.sort()
+    ms = times[len(times) // 2]
+    return plan.cast_bytes(dinp) / (ms * 1e-3) / 1e9, ms
+
+
 def main():
     args = parse()
     if args.copy_reference:
@@ -170,6 +191,8 @@ def main():
     cast_bytes = plan.cast_bytes(dinp)
     cast_gbps = cast_bytes / (cast_ms * 1e-3) / 1e9
 
+    cold_gbps, cold_ms = cold_cast_gbps(plan, dinp)
+
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
@@ -204,6 +227,7 @@ def main():
             "cast_ms": round(cast_ms, 4), "cast_bytes": cast_bytes, "cast_gbps": round(cast_gbps, 1),
             "cast_frac_of_hbm": round(cast_gbps / PEAK_HBM_GBPS, 4),
             "scale_update_ms": round(upd_ms, 4),
+            "cast_cold_ms": round(cold_ms, 4), "cast_cold_gbps": round(cold_gbps, 1),
         },
         "device": info,
     }

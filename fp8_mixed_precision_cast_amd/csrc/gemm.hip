@@ -49,6 +49,7 @@ constexpr int kWM = 128, kWN = 64;        // wave tile
 constexpr int kPM = kWM / 32, kPN = kWN / 32;   // 32 x 32 MFMA blocks per wave
 constexpr int kTileBytes = kBM * kBK;     // one operand's K step in LDS: 32 KB
 constexpr int kSlabs = kTileBytes / (kThreads * 16);   // 1 KB LDS slabs each wave fills per operand
+constexpr int kRowsPerPass = kThreads / 32;            // epilogue write-out: 32 threads per 512-byte row
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
 constexpr int kCRow = kBN * 2;            // bytes of one BF16 output row of the tile in LDS
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     }
   }
   __syncthreads();
-  // Write-out: each pass covers 16 rows, 32 threads per row, one 16-byte
+  // Write-out: each pass covers kRowsPerPass rows, 32 threads per row, one 16-byte
   // chunk each. With a fused cast, the same eight BF16 values feed the amax
   // and become eight codes of y_q.
   const int c = tid & 31;
@@ -324,23 +325,23 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     // Interior tile: all sixteen chunks are read first (the accumulators are
     // dead, so the registers are free), then stored with 16-byte stores and
     // converted without branches.
-    uint4 v[kBM / 16];
+    uint4 v[kBM / kRowsPerPass];
 #pragma unroll
-    for (int p = 0; p < kBM / 16; ++p) {
-      const int row = p * 16 + (tid >> 5);
+    for (int p = 0; p < kBM / kRowsPerPass; ++p) {
+      const int row = p * kRowsPerPass + (tid >> 5);
       v[p] = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
     }
     if (do_c) {
 #pragma unroll
-      for (int p = 0; p < kBM / 16; ++p)
-        *reinterpret_cast<uint4*>(C + (m0 + p * 16 + (tid >> 5)) * ldc + gn) = v[p];
+      for (int p = 0; p < kBM / kRowsPerPass; ++p)
+        *reinterpret_cast<uint4*>(C + (m0 + p * kRowsPerPass + (tid >> 5)) * ldc + gn) = v[p];
     }
     if constexpr (YF != kNoY) {
       // Magnitude max of this thread's 128 values: the amax contribution,
       // and the test for NaN sources.
       uint32_t mx = 0;
 #pragma unroll
-      for (int p = 0; p < kBM / 16; ++p)
+      for (int p = 0; p < kBM / kRowsPerPass; ++p)
         mx = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(mx, v[p].x), v[p].y), v[p].z), v[p].w);
       if (do_amax) am = mx;
       if (do_q) {
@@ -348,15 +349,15 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
         const bool no_nan = (mx & 0xFFFFu) <= 0x7F80u && (mx >> 16) <= 0x7F80u && sb != 0u && sb < 0x7F800000u;
         if (no_nan) {
 #pragma unroll
-          for (int p = 0; p < kBM / 16; ++p) {
+          for (int p = 0; p < kBM / kRowsPerPass; ++p) {
             const uint2 qq = {enc4_bf16_nonan<YF>(v[p].x, v[p].y, ys), enc4_bf16_nonan<YF>(v[p].z, v[p].w, ys)};
-            *reinterpret_cast<uint2*>(y_q + (m0 + p * 16 + (tid >> 5)) * ld_yq + gn) = qq;
+            *reinterpret_cast<uint2*>(y_q + (m0 + p * kRowsPerPass + (tid >> 5)) * ld_yq + gn) = qq;
           }
         } else {
 #pragma unroll
-          for (int p = 0; p < kBM / 16; ++p) {
+          for (int p = 0; p < kBM / kRowsPerPass; ++p) {
             const uint2 qq = {enc4_bf16_sel<YF>(v[p].x, v[p].y, ys), enc4_bf16_sel<YF>(v[p].z, v[p].w, ys)};
-            *reinterpret_cast<uint2*>(y_q + (m0 + p * 16 + (tid >> 5)) * ld_yq + gn) = qq;
+            *reinterpret_cast<uint2*>(y_q + (m0 + p * kRowsPerPass + (tid >> 5)) * ld_yq + gn) = qq;
           }
         }
       }
@@ -364,8 +365,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   } else {
     // Edge tiles and unaligned outputs: row and column checks, element stores
     // where a chunk straddles N or the layout forbids wide stores.
-    for (int p = 0; p < kBM / 16; ++p) {
-      const int row = p * 16 + (tid >> 5);
+    for (int p = 0; p < kBM / kRowsPerPass; ++p) {
+      const int row = p * kRowsPerPass + (tid >> 5);
       const int64_t gm = m0 + row;
       if (gm >= M) break;
       const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
