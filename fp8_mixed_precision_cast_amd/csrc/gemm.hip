@@ -171,9 +171,13 @@ struct Acc { v16f v[kPM][kPN]; };
 //
 // Software pipeline: the fragments of chunk c+1 are read from LDS while chunk
 // c is multiplied, and the operands of each sub-step are widened while the
-// MFMAs of the sub-step before it run.
-template <int FA, int FB>
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc& acc, int wm, int wn, int lane) {
+// MFMAs of the sub-step before it run. The copies of the next K step are
+// issued after the first two sub-steps' MFMAs (`issue_copies`): their LDS
+// writes then no longer compete with the first fragment reads of the step
+// (measured 2-5% faster than issuing them at the top).
+template <int FA, int FB, typename Issue>
+__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc& acc, int wm, int wn, int lane,
+                                         Issue&& issue_copies) {
   const int G = lane >> 5;
   const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
   uint4 aq[2][kPM], bq[2][kPN];
@@ -213,6 +217,7 @@ __device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, A
 #pragma unroll
         for (int j = 0; j < kPN; ++j)
           acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[j], aw[i], acc.v[i][j], 0, 0, 0);
+      if (c == 0 && half == 1) issue_copies();
       if (!last) {
 #pragma unroll
         for (int i = 0; i < kPM; ++i) aw[i] = an[i];
@@ -223,18 +228,20 @@ __device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, A
   }
 }
 
-// Issues the copy of the next K step into `nxt` and multiplies the step in
-// `cur`. The two stages never overlap; saying so (restrict) lets the compiler
-// keep the copy in flight while the fragments of `cur` are read.
+// Multiplies the step in `cur` and, from inside it, issues the copy of the
+// next K step into `nxt`. The two stages never overlap; saying so (restrict)
+// lets the compiler keep the copy in flight while the fragments of `cur` are
+// read.
 template <int FA, int FB>
 __device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bool more,
                                                const TileCopy& ca, const TileCopy& cb, uint32_t k_next, uint32_t K,
                                                Acc& acc, int wm, int wn, int wave, int lane) {
-  if (more) {
-    load_tile(ca, k_next, K, nxt, wave);
-    load_tile(cb, k_next, K, nxt + kTileBytes, wave);
-  }
-  mma_step<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane);
+  mma_step<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, [&]() {
+    if (more) {
+      load_tile(ca, k_next, K, nxt, wave);
+      load_tile(cb, k_next, K, nxt + kTileBytes, wave);
+    }
+  });
 }
 
 // No FP8 copy of the output (YF of the plain GEMM).
