@@ -23,7 +23,7 @@ from typing import Optional
 
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
-    "fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step", "AdamFP8State",
+    "fp8_amax_cast", "fp8_scale_update", "fp8_scale_update_batched", "ScaleUpdateBatch", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step", "AdamFP8State",
     "fp8mp_status_string",
     "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
@@ -61,6 +61,8 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_amax_cast.restype = ctypes.c_int
     lib.fp8_scale_update.argtypes = [vp, i32, ctypes.c_int, i32, vp, vp, vp]
     lib.fp8_scale_update.restype = ctypes.c_int
+    lib.fp8_scale_update_batched.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.fp8_scale_update_batched.restype = ctypes.c_int
     lib.fp8_scaled_gemm.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp,
                                     i64, vp]
     lib.fp8_scaled_gemm.restype = ctypes.c_int
@@ -155,6 +157,31 @@ def fp8_scale_update(history, fmt, margin, scale, scale_inv, stream=None) -> Non
     st = load_library().fp8_scale_update(_ptr(history), int(history.numel()), FORMATS[fmt], int(margin),
                                          _ptr(scale), _ptr(scale_inv), _stream(stream))
     _check(st, "fp8_scale_update")
+
+
+class ScaleUpdateBatch:
+    """The host-side argument arrays of fp8_scale_update_batched for a fixed list of recipe states
+    (objects with history, fmt, margin, scale, scale_inv), built once."""
+
+    def __init__(self, states):
+        n = len(states)
+        self.n = n
+        self._keep = list(states)
+        self.hist = (ctypes.c_void_p * n)(*[st.history.data_ptr() for st in states])
+        self.lens = (ctypes.c_int32 * n)(*[int(st.history.numel()) for st in states])
+        self.fmts = (ctypes.c_int * n)(*[int(st.fmt) for st in states])
+        self.margins = (ctypes.c_int32 * n)(*[int(st.margin) for st in states])
+        self.scales = (ctypes.c_void_p * n)(*[st.scale.data_ptr() for st in states])
+        self.scale_invs = (ctypes.c_void_p * n)(*[st.scale_inv.data_ptr() for st in states])
+
+
+def fp8_scale_update_batched(batch, stream=None) -> None:
+    """fp8_scale_update for every state of a ScaleUpdateBatch (or a list of states), in one launch per 16."""
+    if not isinstance(batch, ScaleUpdateBatch):
+        batch = ScaleUpdateBatch(batch)
+    st = load_library().fp8_scale_update_batched(batch.n, batch.hist, batch.lens, batch.fmts, batch.margins,
+                                                 batch.scales, batch.scale_invs, _stream(stream))
+    _check(st, "fp8_scale_update_batched")
 
 
 def fp8_scaled_gemm(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None) -> None:

@@ -132,6 +132,39 @@ fp8mp_status fp8_scale_update(float* amax_history, int32_t history_len, fp8mp_fo
                                              stream));
 }
 
+fp8mp_status fp8_scale_update_batched(int32_t n_tensors, float* const* amax_histories, const int32_t* history_lens,
+                                      const fp8mp_format* fmts, const int32_t* margins, float* const* scales,
+                                      float* const* scale_invs, hipStream_t stream) {
+  if (n_tensors < 0) return FP8MP_ERR_INVALID_ARG;
+  if (n_tensors == 0) return FP8MP_OK;
+  if (!amax_histories || !history_lens || !fmts || !margins || !scales || !scale_invs) return FP8MP_ERR_INVALID_ARG;
+  for (int32_t t = 0; t < n_tensors; ++t) {
+    if (!valid_format(fmts[t]) && fmts[t] != FP8MP_FP16) return FP8MP_ERR_INVALID_ARG;
+    if (!amax_histories[t] || !scales[t] || !scale_invs[t]) return FP8MP_ERR_INVALID_ARG;
+    if (history_lens[t] < 1 || margins[t] < 0) return FP8MP_ERR_INVALID_ARG;
+    if (!is_aligned(amax_histories[t], 4) || !is_aligned(scales[t], 4) || !is_aligned(scale_invs[t], 4))
+      return FP8MP_ERR_INVALID_ARG;
+  }
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  for (int32_t t0 = 0; t0 < n_tensors; t0 += fp8mp::kMaxBatch) {
+    const int n = n_tensors - t0 < fp8mp::kMaxBatch ? n_tensors - t0 : fp8mp::kMaxBatch;
+    fp8mp::ScaleUpdateBatch b{};
+    for (int i = 0; i < n; ++i) {
+      b.history[i] = amax_histories[t0 + i];
+      b.scale[i] = scales[t0 + i];
+      b.scale_inv[i] = scale_invs[t0 + i];
+      b.len[i] = history_lens[t0 + i];
+      b.margin[i] = margins[t0 + i];
+      b.fmt[i] = fmts[t0 + i];
+    }
+    st = from_hip(fp8mp::launch_scale_update_batched(b, n, stream));
+    if (st != FP8MP_OK) return st;
+  }
+  return FP8MP_OK;
+}
+
 fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
                              fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
                              const float* a_scale_inv, const float* b_scale_inv, uint16_t* c, int64_t ldc,

@@ -177,6 +177,17 @@ hipError_t launch_amax_cast(const void* x, fp8mp_dtype dt, int64_t rows, int64_t
                             hipStream_t stream);
 hipError_t launch_scale_update(float* history, int32_t len, fp8mp_format fmt, int32_t margin,
                                float* scale, float* scale_inv, hipStream_t stream);
+// Up to kMaxBatch tensors' recipe state, passed by value to one launch.
+constexpr int kMaxBatch = 16;
+struct ScaleUpdateBatch {
+  float* history[kMaxBatch];
+  float* scale[kMaxBatch];
+  float* scale_inv[kMaxBatch];
+  int32_t len[kMaxBatch];
+  int32_t margin[kMaxBatch];
+  int32_t fmt[kMaxBatch];
+};
+hipError_t launch_scale_update_batched(const ScaleUpdateBatch& batch, int n, hipStream_t stream);
 hipError_t launch_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
                               fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
                               const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,

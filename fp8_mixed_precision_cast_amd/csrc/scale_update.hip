@@ -41,12 +41,12 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* red) {
   return a;
 }
 
+// One tensor's update, run by one whole workgroup (`stage` and `red` are its
+// LDS).
 template <int FMT>
-__global__ __launch_bounds__(kBlock) void scale_update_kernel(float* __restrict__ hist, int32_t len,
-                                                              int32_t margin, float* __restrict__ scale,
-                                                              float* __restrict__ scale_inv) {
-  __shared__ uint32_t red[kBlock / 64];
-  __shared__ uint32_t stage[kLdsEntries];
+__device__ __forceinline__ void update_one(float* __restrict__ hist, int32_t len, int32_t margin,
+                                           float* __restrict__ scale, float* __restrict__ scale_inv,
+                                           uint32_t* stage, uint32_t* red) {
   uint32_t* h = reinterpret_cast<uint32_t*>(hist);
 
   // Max over every entry. History entries are amaxes: non-negative floats or
@@ -89,7 +89,34 @@ __global__ __launch_bounds__(kBlock) void scale_update_kernel(float* __restrict_
   }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(kBlock) void scale_update_kernel(float* __restrict__ hist, int32_t len,
+                                                              int32_t margin, float* __restrict__ scale,
+                                                              float* __restrict__ scale_inv) {
+  __shared__ uint32_t red[kBlock / 64];
+  __shared__ uint32_t stage[kLdsEntries];
+  update_one<FMT>(hist, len, margin, scale, scale_inv, stage, red);
+}
+
+// Several tensors in one launch: workgroup b updates tensor b.
+__global__ __launch_bounds__(kBlock) void scale_update_batched_kernel(ScaleUpdateBatch batch) {
+  __shared__ uint32_t red[kBlock / 64];
+  __shared__ uint32_t stage[kLdsEntries];
+  const int t = blockIdx.x;
+  float* h = batch.history[t];
+  const int32_t len = batch.len[t], margin = batch.margin[t];
+  float *s = batch.scale[t], *si = batch.scale_inv[t];
+  if (batch.fmt[t] == FP8MP_E4M3) update_one<FP8MP_E4M3>(h, len, margin, s, si, stage, red);
+  else if (batch.fmt[t] == FP8MP_E5M2) update_one<FP8MP_E5M2>(h, len, margin, s, si, stage, red);
+  else update_one<FP8MP_FP16>(h, len, margin, s, si, stage, red);
+}
+
 }  // namespace
+
+hipError_t launch_scale_update_batched(const ScaleUpdateBatch& batch, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(scale_update_batched_kernel, dim3(n), dim3(kBlock), 0, stream, batch);
+  return hipGetLastError();
+}
 
 hipError_t launch_scale_update(float* history, int32_t len, fp8mp_format fmt, int32_t margin,
                                float* scale, float* scale_inv, hipStream_t stream) {

@@ -32,8 +32,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (CurrentScalingState, DelayedScalingState, fp8_amax_cast, fp8_layernorm_amax_cast,
-               fp8_scale_update, fp8_scaled_gemm, fp8_scaled_gemm_amax_cast)
+from . import (CurrentScalingState, DelayedScalingState, ScaleUpdateBatch, fp8_amax_cast, fp8_layernorm_amax_cast,
+               fp8_scale_update_batched, fp8_scaled_gemm, fp8_scaled_gemm_amax_cast)
 
 
 @dataclass(frozen=True)
@@ -94,6 +94,7 @@ class LayerPlan:
                                   else CurrentScalingState(o.fmt, margin, device))
             self.q[o.name] = torch.empty(r, c, dtype=torch.uint8, device=device) if o.plain else None
             self.qt[o.name] = torch.empty(c, r, dtype=torch.uint8, device=device) if o.transposed else None
+        self._batch = None
         self._gemm_args = []
         for g in self.gemms:
             a = self.qt[g.a] if g.a_transposed else self.q[g.a]
@@ -167,10 +168,12 @@ class LayerPlan:
             ys.cast(self.out[g.name], self.yq[g.name], None, True, stream)
 
     def update_all(self, stream=None) -> None:
+        """Every tensor's delayed-scaling update, in one launch."""
         if self.recipe == "current":
             return
-        for st in list(self.state.values()) + list(self.ystate.values()):
-            fp8_scale_update(st.history, st.fmt, st.margin, st.scale, st.scale_inv, stream)
+        if self._batch is None:
+            self._batch = ScaleUpdateBatch(list(self.state.values()) + list(self.ystate.values()))
+        fp8_scale_update_batched(self._batch, stream)
 
     def step(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
         self.cast_all(inputs, stream)

@@ -112,6 +112,23 @@ fp8mp_status fp8_scale_update(float* amax_history, int32_t history_len, fp8mp_fo
                               hipStream_t stream);
 
 /*
+ * fp8_scale_update_batched: fp8_scale_update for n_tensors tensors in one
+ * launch per 16 tensors (one workgroup per tensor), with the same result as
+ * n_tensors separate calls. A layer updates all of its tensors' recipe state
+ * after its GEMMs ([TE] §動的スケーリングとFP8レシピの設定); batching saves the
+ * launches.
+ *
+ *   amax_histories, scales, scale_invs   host arrays of n_tensors device pointers.
+ *   history_lens, fmts, margins          host arrays of n_tensors values, each
+ *                                        checked as fp8_scale_update checks it.
+ * The tensors' buffers must not overlap. n_tensors == 0 is a no-op.
+ */
+fp8mp_status fp8_scale_update_batched(int32_t n_tensors, float* const* amax_histories,
+                                      const int32_t* history_lens, const fp8mp_format* fmts,
+                                      const int32_t* margins, float* const* scales,
+                                      float* const* scale_invs, hipStream_t stream);
+
+/*
  * fp8_scaled_gemm: C = (A . B^T) * a_scale_inv * b_scale_inv with FP32
  * accumulation and a BF16 result (round to nearest even).
  *

@@ -22,7 +22,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = fp8.exported_symbols()
-    assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast",
+    assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scale_update_batched", "fp8_scaled_gemm",
+                     "fp8_scaled_gemm_amax_cast",
                      "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step",
                      "fp8mp_status_string", "fp8mp_device_info"]
     for n in names:
@@ -60,6 +61,25 @@ def test_scale_update_argument_validation(lib):
     assert f(A16, 4, 0, -1, A16, A16, None) == INVALID
     assert f(A16, 4, 5, 0, A16, A16, None) == INVALID
     assert f(A16, 4, 0, 0, None, A16, None) == INVALID
+
+
+def test_batched_scale_update_validation(lib):
+    f = lib.fp8_scale_update_batched
+    n = 2
+    ptrs = lambda *v: (ctypes.c_void_p * n)(*v)
+    ints = lambda *v: (ctypes.c_int32 * n)(*v)
+    fmts = lambda *v: (ctypes.c_int * n)(*v)
+    good = dict(h=ptrs(4096, 8192), l=ints(4, 4), f=fmts(0, 1), m=ints(0, 0), s=ptrs(12288, 12292),
+                si=ptrs(12296, 12300))
+    call = lambda **kw: f(n, *[kw.get(k, good[k]) for k in ("h", "l", "f", "m", "s", "si")], None)
+    assert f(-1, None, None, None, None, None, None, None) == INVALID
+    assert f(0, None, None, None, None, None, None, None) == OK
+    assert call(h=None) == INVALID
+    assert call(f=fmts(0, 7)) == INVALID
+    assert call(l=ints(4, 0)) == INVALID
+    assert call(m=ints(-1, 0)) == INVALID
+    assert call(h=ptrs(4096, 0)) == INVALID
+    assert call(s=ptrs(12289, 12292)) == INVALID
 
 
 def test_gemm_argument_validation(lib):
@@ -177,6 +197,9 @@ def test_valid_calls_without_device_report_no_device(lib):
                                        None) == NO_DEVICE
     assert lib.fp8_reduce_shared_scale(A16, 1, 4, 64, 64, A16, A16, 1, None) == NO_DEVICE
     assert lib.fp8_scale_update(A16, 4, 2, 0, A16, A16, None) == NO_DEVICE          # FP16 storage accepted
+    one_p, one_i, one_f = (ctypes.c_void_p * 1)(4096), (ctypes.c_int32 * 1)(4), (ctypes.c_int * 1)(2)
+    assert lib.fp8_scale_update_batched(1, one_p, one_i, one_f, (ctypes.c_int32 * 1)(0), one_p, one_p,
+                                        None) == NO_DEVICE
     # k == 0 with zero leading dimensions passes the host checks (no division by a zero ld)
     assert lib.fp8_scaled_gemm(A16, 0, 0, A16, 0, 0, 4, 8, 0, A16, A16, A16, 8, None) == NO_DEVICE
     buf = ctypes.create_string_buffer(64)

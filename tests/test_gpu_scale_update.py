@@ -92,3 +92,41 @@ def test_sixteen_step_recipe_and_resume():
         ref.update()
         assert np.array_equal(_bits(host(st.history)), _bits(ref.history))
         assert f32_bits(st.scale)[0] == _bits(ref.scale) and f32_bits(st.scale_inv)[0] == _bits(ref.scale_inv)
+
+
+def test_batched_update_equals_oracle_per_tensor():
+    """20 tensors (two launches of up to 16) with mixed formats, lengths, margins and hold cases."""
+    require_gpu()
+    from oracle.adam import update_fp16_scale
+    rng = np.random.default_rng(123)
+    fmts = ["e4m3", "e5m2", "fp16"]
+    cases = []
+    for t in range(20):
+        L = int(rng.choice([1, 3, 256, 1024, 8192, 8193, 10000]))
+        fmt = fmts[t % 3]
+        margin = int(rng.integers(0, 4))
+        hist = np.exp2(rng.uniform(-30, 30, L)).astype(F32)
+        if t == 5:
+            hist[:] = 0                       # held
+        if t == 7:
+            hist[L // 2] = CANONICAL_NAN      # held while the NaN is in the window
+        cases.append((fmt, margin, hist, F32(rng.uniform(0.5, 4)), None))
+
+    class St:
+        pass
+    states = []
+    for fmt, margin, hist, s0, _ in cases:
+        st = St()
+        st.history, st.fmt, st.margin = dev(hist), fp8.FORMATS[fmt], margin
+        st.scale, st.scale_inv = f32(s0), f32(F32(1) / s0)
+        states.append(st)
+    banner("batched-update", len(states))
+    fp8.fp8_scale_update_batched(states)
+    for (fmt, margin, hist, s0, _), st in zip(cases, states):
+        si0 = F32(1) / s0
+        if fmt == "fp16":
+            ws, wsi, wh = update_fp16_scale(hist, s0, si0, margin)
+        else:
+            ws, wsi, wh = update_scale(hist, s0, si0, fmt, margin)
+        assert f32_bits(st.scale)[0] == _bits(ws) and f32_bits(st.scale_inv)[0] == _bits(wsi), (fmt, margin, hist.size)
+        assert np.array_equal(_bits(host(st.history)), _bits(wh))
