@@ -23,7 +23,7 @@ from typing import Optional
 
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
-    "fp8_amax_cast", "fp8_scale_update", "fp8_scale_update_batched", "ScaleUpdateBatch", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step", "AdamFP8State",
+    "fp8_amax_cast", "fp8_amax_cast_batched", "CastBatch", "fp8_scale_update", "fp8_scale_update_batched", "ScaleUpdateBatch", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step", "AdamFP8State",
     "fp8mp_status_string",
     "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     lib.fp8_amax_cast.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, i64, vp, i64, vp, vp]
     lib.fp8_amax_cast.restype = ctypes.c_int
+    lib.fp8_amax_cast_batched.argtypes = [i32, vp, vp]
+    lib.fp8_amax_cast_batched.restype = ctypes.c_int
     lib.fp8_scale_update.argtypes = [vp, i32, ctypes.c_int, i32, vp, vp, vp]
     lib.fp8_scale_update.restype = ctypes.c_int
     lib.fp8_scale_update_batched.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp]
@@ -150,6 +152,36 @@ def fp8_amax_cast(x, fmt, scale=None, q=None, q_t=None, amax=None, stream=None) 
     st = load_library().fp8_amax_cast(_ptr(x), _src_dtype(x), rows, cols, ld_x, FORMATS[fmt], _ptr(scale),
                                       _ptr(q), ld_q, _ptr(q_t), ld_qt, _ptr(amax), _stream(stream))
     _check(st, "fp8_amax_cast")
+
+
+class _CastItem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int), ("numel", ctypes.c_int64), ("fmt", ctypes.c_int),
+                ("scale", ctypes.c_void_p), ("q", ctypes.c_void_p), ("amax", ctypes.c_void_p)]
+
+
+class CastBatch:
+    """The host-side item array of fp8_amax_cast_batched for fixed tensors, built once.
+
+    items: (x, fmt, scale, q, amax) with x contiguous float32/bfloat16, q a contiguous uint8 tensor of
+    x's size or None, amax a float32 tensor or None."""
+
+    def __init__(self, items):
+        self._keep = list(items)
+        arr = (_CastItem * len(items))()
+        for k, (x, fmt, scale, q, amax) in enumerate(items):
+            if not x.is_contiguous() or (q is not None and (not q.is_contiguous() or q.numel() != x.numel())):
+                raise ValueError("batched casts take contiguous tensors of equal size")
+            arr[k] = _CastItem(x.data_ptr(), _src_dtype(x), x.numel(), FORMATS[fmt], _ptr(scale), _ptr(q), _ptr(amax))
+        self.n = len(items)
+        self.items = arr
+
+
+def fp8_amax_cast_batched(batch, stream=None) -> None:
+    """fp8_amax_cast of every item of a CastBatch (or a list of items), one launch per 8 BF16 tensors."""
+    if not isinstance(batch, CastBatch):
+        batch = CastBatch(batch)
+    st = load_library().fp8_amax_cast_batched(batch.n, ctypes.cast(batch.items, ctypes.c_void_p), _stream(stream))
+    _check(st, "fp8_amax_cast_batched")
 
 
 def fp8_scale_update(history, fmt, margin, scale, scale_inv, stream=None) -> None:

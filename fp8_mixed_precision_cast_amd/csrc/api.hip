@@ -118,6 +118,49 @@ fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int
                                           amax, cus, stream));
 }
 
+fp8mp_status fp8_amax_cast_batched(int32_t n_items, const fp8mp_cast_item* items, hipStream_t stream) {
+  if (n_items < 0) return FP8MP_ERR_INVALID_ARG;
+  if (n_items == 0) return FP8MP_OK;
+  if (items == nullptr) return FP8MP_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n_items; ++i) {
+    const fp8mp_cast_item& it = items[i];
+    if (!valid_dtype(it.x_dtype) || !valid_format(it.fmt) || it.numel < 0) return FP8MP_ERR_INVALID_ARG;
+    if (it.numel == 0) continue;
+    if (it.x == nullptr || (it.q && it.scale == nullptr)) return FP8MP_ERR_INVALID_ARG;
+    if (!is_aligned(it.x, it.x_dtype == FP8MP_BF16 ? 2 : 4)) return FP8MP_ERR_INVALID_ARG;
+    if ((it.amax && !is_aligned(it.amax, 4)) || (it.scale && !is_aligned(it.scale, 4))) return FP8MP_ERR_INVALID_ARG;
+  }
+  int cus = 0;
+  fp8mp_status st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  fp8mp::CastBatch b{};
+  auto flush = [&]() -> fp8mp_status {
+    if (b.n == 0) return FP8MP_OK;
+    fp8mp_status r = from_hip(fp8mp::launch_amax_cast_batched(b, cus, stream));
+    b = fp8mp::CastBatch{};
+    return r;
+  };
+  for (int32_t i = 0; i < n_items; ++i) {
+    const fp8mp_cast_item& it = items[i];
+    if (it.numel == 0 || (!it.q && !it.amax)) continue;
+    const bool batchable = it.x_dtype == FP8MP_BF16 && is_aligned(it.x, 16) && (!it.q || is_aligned(it.q, 16));
+    if (!batchable) {
+      st = from_hip(fp8mp::launch_amax_cast(it.x, it.x_dtype, 1, it.numel, it.numel, it.fmt, it.scale, it.q,
+                                            it.numel, nullptr, 0, it.amax, cus, stream));
+      if (st != FP8MP_OK) return st;
+      continue;
+    }
+    b.x[b.n] = it.x;
+    b.q[b.n] = it.q;
+    b.scale[b.n] = it.scale;
+    b.amax[b.n] = it.amax;
+    b.numel[b.n] = it.numel;
+    b.fmt[b.n] = it.fmt;
+    if (++b.n == fp8mp::kMaxCastBatch && (st = flush()) != FP8MP_OK) return st;
+  }
+  return flush();
+}
+
 fp8mp_status fp8_scale_update(float* amax_history, int32_t history_len, fp8mp_format fmt, int32_t margin,
                               float* scale, float* scale_inv, hipStream_t stream) {
   if (!valid_format(fmt) && fmt != FP8MP_FP16) return FP8MP_ERR_INVALID_ARG;

@@ -28,15 +28,11 @@ constexpr int kTileCols = 128;   // 8 column groups of 16
 // all loads of an iteration are issued before any conversion. Source and
 // codes are touched once, so both stream past the caches (non-temporal).
 template <int FMT, bool HAS_Q>
-__global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16(const uint4* __restrict__ x,
-                                                             uint4* __restrict__ q, int64_t nchunk,
-                                                             const float* __restrict__ scale,
-                                                             float* __restrict__ amax) {
-  const float s = HAS_Q ? *scale : 1.0f;
+__device__ __forceinline__ uint32_t flat_bf16_body(const uint4* __restrict__ x, uint4* __restrict__ q,
+                                                   int64_t nchunk, float s, int64_t block, int64_t nblocks) {
   uint32_t acc = 0;
-  const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
-  for (int64_t base = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; base < nchunk;
-       base += kFlatUnroll * stride) {
+  const int64_t stride = nblocks * kFlatBlock;
+  for (int64_t base = block * kFlatBlock + threadIdx.x; base < nchunk; base += kFlatUnroll * stride) {
     u32x4 a[kFlatUnroll], b[kFlatUnroll];
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
 #pragma unroll
@@ -67,7 +63,52 @@ __global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16(const uint4* __rest
       }
     }
   }
-  if (amax) block_amax_commit<kFlatBlock>(bf16x2_acc_to_f32_bits(acc), amax);
+  return bf16x2_acc_to_f32_bits(acc);
+}
+
+template <int FMT, bool HAS_Q>
+__global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16(const uint4* __restrict__ x,
+                                                             uint4* __restrict__ q, int64_t nchunk,
+                                                             const float* __restrict__ scale,
+                                                             float* __restrict__ amax) {
+  const float s = HAS_Q ? *scale : 1.0f;
+  const uint32_t m = flat_bf16_body<FMT, HAS_Q>(x, q, nchunk, s, blockIdx.x, gridDim.x);
+  if (amax) block_amax_commit<kFlatBlock>(m, amax);
+}
+
+// Several contiguous BF16 tensors in one launch: blocks [start[t], start[t+1])
+// run tensor t's flat cast; the first of them also converts its last
+// numel % 16 elements.
+template <bool HAS_Q_UNUSED>
+__global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16_batched(CastBatch batch) {
+  int t = 0;
+  while (t + 1 < batch.n && (int)blockIdx.x >= batch.block_start[t + 1]) ++t;
+  const int64_t block = (int64_t)blockIdx.x - batch.block_start[t];
+  const int64_t nblocks = (int64_t)batch.block_start[t + 1] - batch.block_start[t];
+  const bool has_q = batch.q[t] != nullptr;
+  const float s = has_q ? *batch.scale[t] : 1.0f;
+  const int64_t nchunk = batch.numel[t] / 16;
+  const uint4* x = static_cast<const uint4*>(batch.x[t]);
+  uint4* q = static_cast<uint4*>(batch.q[t]);
+  uint32_t m;
+  if (batch.fmt[t] == FP8MP_E4M3)
+    m = has_q ? flat_bf16_body<FP8MP_E4M3, true>(x, q, nchunk, s, block, nblocks)
+              : flat_bf16_body<FP8MP_E4M3, false>(x, q, nchunk, s, block, nblocks);
+  else
+    m = has_q ? flat_bf16_body<FP8MP_E5M2, true>(x, q, nchunk, s, block, nblocks)
+              : flat_bf16_body<FP8MP_E5M2, false>(x, q, nchunk, s, block, nblocks);
+  if (block == 0) {
+    const int64_t e = nchunk * 16 + threadIdx.x;
+    if (e < batch.numel[t]) {
+      const float v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(batch.x[t])[e] << 16);
+      m = amax_f32(m, v);
+      if (has_q) {
+        uint8_t* qb = static_cast<uint8_t*>(batch.q[t]);
+        qb[e] = batch.fmt[t] == FP8MP_E4M3 ? enc1<FP8MP_E4M3>(v, s) : enc1<FP8MP_E5M2>(v, s);
+      }
+    }
+  }
+  if (batch.amax[t] != nullptr) block_amax_commit<kFlatBlock>(canonical_nan(m), batch.amax[t]);
 }
 
 // Contiguous fp32 source, 16 elements (four 16-byte loads) -> one 16-byte store.
@@ -325,6 +366,25 @@ hipError_t launch_fmt(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols,
 }
 
 }  // namespace
+
+hipError_t launch_amax_cast_batched(CastBatch& batch, int num_cus, hipStream_t stream) {
+  // Share num_cus * 8 workgroups among the tensors by size, at least one each
+  // (measured: fewer, larger shares leave the tail of the launch under-filled).
+  int64_t total = 0;
+  for (int t = 0; t < batch.n; ++t) total += batch.numel[t] / 16 + 1;
+  const int64_t budget = (int64_t)num_cus * 8;
+  int start = 0;
+  for (int t = 0; t < batch.n; ++t) {
+    batch.block_start[t] = start;
+    const int64_t need = cdiv(batch.numel[t] / 16 + 1, (int64_t)kFlatBlock * kFlatUnroll);
+    int64_t share = (budget * (batch.numel[t] / 16 + 1) + total - 1) / total;
+    share = std::max<int64_t>(1, std::min<int64_t>(share, need));
+    start += (int)share;
+  }
+  batch.block_start[batch.n] = start;
+  hipLaunchKernelGGL((cast_flat_bf16_batched<true>), dim3(start), dim3(kFlatBlock), 0, stream, batch);
+  return hipGetLastError();
+}
 
 hipError_t launch_amax_cast(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
                             fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q,

@@ -166,6 +166,20 @@ __device__ __forceinline__ void block_amax_commit(uint32_t m, float* amax) {
   }
 }
 
+// Up to kMaxCastBatch contiguous BF16 tensors cast in one launch.
+constexpr int kMaxCastBatch = 8;
+struct CastBatch {
+  const void* x[kMaxCastBatch];
+  void* q[kMaxCastBatch];
+  const float* scale[kMaxCastBatch];
+  float* amax[kMaxCastBatch];
+  int64_t numel[kMaxCastBatch];
+  int32_t fmt[kMaxCastBatch];
+  int32_t block_start[kMaxCastBatch + 1];
+  int32_t n;
+};
+hipError_t launch_amax_cast_batched(CastBatch& batch, int num_cus, hipStream_t stream);
+
 // Largest GEMM leading dimension in bytes: a 256-row tile then spans less
 // than 2^30 bytes, so its copies use 32-bit buffer offsets.
 constexpr int64_t kGemmMaxLd = int64_t(1) << 22;

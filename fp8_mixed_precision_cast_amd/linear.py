@@ -32,8 +32,9 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (CurrentScalingState, DelayedScalingState, ScaleUpdateBatch, fp8_amax_cast, fp8_layernorm_amax_cast,
-               fp8_scale_update_batched, fp8_scaled_gemm, fp8_scaled_gemm_amax_cast)
+from . import (CastBatch, CurrentScalingState, DelayedScalingState, ScaleUpdateBatch, fp8_amax_cast,
+               fp8_amax_cast_batched, fp8_layernorm_amax_cast, fp8_scale_update_batched, fp8_scaled_gemm,
+               fp8_scaled_gemm_amax_cast)
 
 
 @dataclass(frozen=True)
@@ -95,6 +96,7 @@ class LayerPlan:
             self.q[o.name] = torch.empty(r, c, dtype=torch.uint8, device=device) if o.plain else None
             self.qt[o.name] = torch.empty(c, r, dtype=torch.uint8, device=device) if o.transposed else None
         self._batch = None
+        self._cast_batch = None
         self._gemm_args = []
         for g in self.gemms:
             a = self.qt[g.a] if g.a_transposed else self.q[g.a]
@@ -140,7 +142,23 @@ class LayerPlan:
                 ys.update(stream)
 
     def cast_all(self, inputs: Dict[str, torch.Tensor], stream=None) -> None:
+        """Every operand's cast. Under the delayed recipe the plain row-major casts of contiguous sources go
+        out as one batched launch (built on first use for these input tensors)."""
+        batched = set()
+        if self.recipe == "delayed":
+            names = [n for n, o in self.operands.items()
+                     if n not in self.ln and not o.transposed and inputs[n].is_contiguous()]
+            key = tuple((n, inputs[n].data_ptr()) for n in names)
+            if names and (self._cast_batch is None or self._cast_batch[0] != key):
+                items = [(inputs[n], self.state[n].fmt, self.state[n].scale, self.q[n], self.state[n].amax_slot)
+                         for n in names]
+                self._cast_batch = (key, CastBatch(items))
+            if names:
+                fp8_amax_cast_batched(self._cast_batch[1], stream)
+                batched = set(names)
         for name, st in self.state.items():
+            if name in batched:
+                continue
             if name in self.ln:
                 g, b, eps = self.ln[name]
                 fp8_layernorm_amax_cast(inputs[name], g, b, eps, st.fmt, None, st.scale, self.q[name], st.amax_slot,

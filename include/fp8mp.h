@@ -88,6 +88,29 @@ fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int
                            uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
                            float* amax, hipStream_t stream);
 
+/* One tensor of fp8_amax_cast_batched: a contiguous source of numel elements. */
+typedef struct {
+  const void* x;          /* numel source values (x_dtype), contiguous */
+  fp8mp_dtype x_dtype;
+  int64_t numel;
+  fp8mp_format fmt;
+  const float* scale;     /* required when q is given */
+  uint8_t* q;             /* numel codes, or NULL (amax only) */
+  float* amax;            /* max-accumulated, or NULL */
+} fp8mp_cast_item;
+
+/*
+ * fp8_amax_cast_batched: fp8_amax_cast for n_items contiguous tensors, with
+ * the same results as n_items separate calls. A layer casts all its operands
+ * at the start of a step ([TE] §動的スケーリングとFP8レシピの設定); contiguous BF16
+ * sources with 16-byte aligned x and q share one launch per 8 tensors, the
+ * workgroups split among them by size; other items take fp8_amax_cast's
+ * kernels one by one. items is a host array; each item is validated as
+ * fp8_amax_cast validates a rows = 1, cols = numel call. Items must not
+ * overlap one another's outputs.
+ */
+fp8mp_status fp8_amax_cast_batched(int32_t n_items, const fp8mp_cast_item* items, hipStream_t stream);
+
 /*
  * fp8_scale_update: the delayed-scaling update of one tensor's recipe state.
  *

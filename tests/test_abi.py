@@ -22,7 +22,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = fp8.exported_symbols()
-    assert names == ["fp8_amax_cast", "fp8_scale_update", "fp8_scale_update_batched", "fp8_scaled_gemm",
+    assert names == ["fp8_amax_cast", "fp8_amax_cast_batched", "fp8_scale_update", "fp8_scale_update_batched",
+                     "fp8_scaled_gemm",
                      "fp8_scaled_gemm_amax_cast",
                      "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step",
                      "fp8mp_status_string", "fp8mp_device_info"]
@@ -61,6 +62,24 @@ def test_scale_update_argument_validation(lib):
     assert f(A16, 4, 0, -1, A16, A16, None) == INVALID
     assert f(A16, 4, 5, 0, A16, A16, None) == INVALID
     assert f(A16, 4, 0, 0, None, A16, None) == INVALID
+
+
+def test_batched_cast_validation(lib):
+    from fp8_mixed_precision_cast_amd import _CastItem
+    f = lib.fp8_amax_cast_batched
+    arr = lambda *its: ctypes.cast((_CastItem * len(its))(*its), ctypes.c_void_p)
+    good = dict(x=4096, x_dtype=1, numel=64, fmt=0, scale=8192, q=12288, amax=16384)
+    item = lambda **kw: _CastItem(**dict(good, **kw))
+    assert f(-1, None, None) == INVALID
+    assert f(0, None, None) == OK
+    assert f(1, None, None) == INVALID
+    assert f(1, arr(item(x_dtype=7)), None) == INVALID
+    assert f(1, arr(item(fmt=2)), None) == INVALID                 # FP16 storage is not a cast format
+    assert f(1, arr(item(numel=-1)), None) == INVALID
+    assert f(2, arr(item(), item(x=None)), None) == INVALID       # every item is checked
+    assert f(1, arr(item(scale=None)), None) == INVALID           # codes need a scale
+    assert f(1, arr(item(x=4097)), None) == INVALID               # misaligned BF16 source
+    assert f(1, arr(item(amax=4098)), None) == INVALID
 
 
 def test_batched_scale_update_validation(lib):

@@ -216,3 +216,41 @@ def test_invalid_arguments_raise():
     x = torch.zeros(4, 4, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fp8.Fp8mpError):
         fp8.fp8_amax_cast(x, "e4m3", None, torch.empty(4, 4, dtype=torch.uint8, device="cuda"))
+
+
+def test_batched_cast_equals_separate_calls():
+    """fp8_amax_cast_batched over 11 items (two batched launches plus fallbacks): BF16 with ragged tails, an
+    unaligned view and an fp32 source (both take the single-tensor kernels), amax-only and codes-only items,
+    an empty one; codes and amax bit-identical to separate fp8_amax_cast calls and to the oracle."""
+    require_gpu()
+    import workloads as wl
+    rng = np.random.default_rng(77)
+    sizes = [16, 17, 1000, 4099, 65536, 300001, 5, 12345, 7, 0, 2048]
+    items, refs = [], []
+    for k, n in enumerate(sizes):
+        fmt = "e4m3" if k % 2 == 0 else "e5m2"
+        x = wl.small_normal(500 + k, (1, max(n, 1)), std=float(np.exp2(rng.uniform(-4, 4))), outlier_factor=20.0)
+        x = x[:, :n]
+        if k == 6:
+            src = torch.zeros(n + 1, dtype=torch.int16, device="cuda")
+            src[1:] = dev(x[0])
+            xt = src[1:]                                  # 2-byte aligned only: fallback kernels
+        elif k == 8:
+            xt = dev(oracle.bf16_to_f32(x[0]))            # fp32 source: fallback kernels
+        else:
+            xt = dev(x[0]) if n else torch.zeros(0, dtype=torch.int16, device="cuda")
+        s = np.float32(np.exp2(rng.uniform(-6, 6)))
+        q = torch.full((n,), 0x33, dtype=torch.uint8, device="cuda") if k != 3 else None       # k = 3: amax only
+        am = f32(0.0) if k != 5 else None                                                       # k = 5: codes only
+        items.append((xt, fmt, f32(s), q, am))
+        refs.append((x[0], fmt, s, k))
+    banner("batched-cast", len(items))
+    fp8.fp8_amax_cast_batched(items)
+    for (xt, fmt, ds, q, am), (x, _, s, k) in zip(items, refs):
+        dtype = "f32" if k == 8 else "bf16"
+        src = oracle.bf16_to_f32(x) if k == 8 else x
+        if q is not None:
+            want = oracle.cast(src, s, fmt, dtype)
+            assert np.array_equal(host(q), want), (k, first_diff(host(q), want))
+        if am is not None:
+            assert f32_bits(am)[0] == np.float32(oracle.amax(src, dtype)).view(np.uint32), k
