@@ -48,7 +48,11 @@ def parse():
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES three times (calibrates HBM counters)")
+                    help="only run a plain device copy of BYTES three times (calibrates HBM counters) and "
+                         "report its rate")
+    ap.add_argument("--gemm-data", default="", metavar="MxNxK",
+                    help="only time fp8_scaled_gemm at this shape on E4M3 operands of several kinds "
+                         "(all zero, all 1.0, uniform random codes, cast N(0,1) values): one JSON line per kind")
     return ap.parse_args()
 
 
@@ -60,14 +64,90 @@ def source_digest() -> str:
 
 
 def copy_reference(nbytes: int) -> None:
+    """Three device copies of nbytes; prints the fastest one's rate (bytes read + written per second)."""
     import torch
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
+    best = float("inf")
     for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_reference_bytes": nbytes}), flush=True)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    print(json.dumps({"copy_reference_bytes": nbytes, "copy_ms": round(best, 4),
+                      "copy_gbps": round(2 * nbytes / best / 1e6, 1)}), flush=True)
+
+
+def gemm_data(shape: str, iters: int = 20) -> None:
+    """fp8_scaled_gemm at one shape on operands of different content. The instruction stream does not
+    depend on the data, but the power it draws does: on a power-limited chip the clock, and with it
+    the rate, falls as the operands' bits toggle more."""
+    import torch
+    import fp8_mixed_precision_cast_amd as fp8
+    m, n, k = (int(v) for v in shape.lower().split("x"))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    one = torch.ones(1, device="cuda")
+
+    def codes(kind, rows):
+        if kind == "zero":
+            return torch.zeros(rows, k, dtype=torch.uint8, device="cuda")
+        if kind == "one":
+            return torch.full((rows, k), 0x38, dtype=torch.uint8, device="cuda")   # E4M3 1.0
+        if kind == "uniform":
+            q = torch.randint(0, 256, (rows, k), dtype=torch.uint8, device="cuda", generator=g)
+            q[(q & 0x7F) == 0x7F] = 0x7E   # no NaN codes
+            return q
+        x = torch.randn(rows, k, device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+        q = torch.empty(rows, k, dtype=torch.uint8, device="cuda")
+        fp8.fp8_amax_cast(x, "e4m3", torch.full((1,), 448.0 / 4.5, device="cuda"), q)
+        return q
+
+    for kind in ("zero", "one", "uniform", "normal"):
+        a, b = codes(kind, m), codes(kind, n)
+        for _ in range(5):
+            fp8.fp8_scaled_gemm(a, "e4m3", b, "e4m3", one, one, c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fp8.fp8_scaled_gemm(a, "e4m3", b, "e4m3", one, one, c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        print(json.dumps({"gemm_data": kind, "shape": [m, n, k], "us": round(ms * 1e3, 1),
+                          "tflops": round(2 * m * n * k / ms / 1e9, 1)}), flush=True)
+        del a, b
+    # Context: the vendor library through torch at the same shape on N(0,1) data, BF16 x BF16 (the
+    # same MFMA path as ours) and FP8 x FP8 (the FP8 MFMA, whose accumulation is coarser than the
+    # tolerance this library is held to).
+    a = torch.randn(m, k, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, k, device="cuda", generator=g).to(torch.bfloat16)
+    refs = {"torch_bf16_mm": lambda: a @ b.t()}
+    if hasattr(torch, "_scaled_mm"):
+        a8, b8 = (a * 0.25).to(torch.float8_e4m3fn), (b * 0.25).to(torch.float8_e4m3fn)
+        refs["torch_fp8_scaled_mm"] = lambda: torch._scaled_mm(a8, b8.t(), scale_a=one[0], scale_b=one[0],
+                                                                 out_dtype=torch.bfloat16)
+    for name, f in refs.items():
+        try:
+            for _ in range(5):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            print(json.dumps({"library": name, "shape": [m, n, k], "us": round(ms * 1e3, 1),
+                              "tflops": round(2 * m * n * k / ms / 1e9, 1)}), flush=True)
+        except RuntimeError as e:
+            print(json.dumps({"library": name, "error": str(e)[:120]}), flush=True)
 
 
 def cpu_baseline(w, inp, min_seconds: float = 10.0):
@@ -126,6 +206,9 @@ def main():
     args = parse()
     if args.copy_reference:
         copy_reference(args.copy_reference)
+        return
+    if args.gemm_data:
+        gemm_data(args.gemm_data)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); every box has one MI355X and this "
