@@ -284,6 +284,12 @@ def main():
             traffic = t.get("gemm_bytes_per_launch")
 
     g = w.gemms[0]
+
+    def describe(t):
+        dist = "N(0,{:g})".format(t.scale) if t.dist == "normal" else "t3 x{:g}".format(t.scale)
+        tail = " +0.1% x{:g}".format(t.outlier_factor) if t.outlier_factor else ""
+        return "{} {}x{} {}{} -> {}".format(t.dtype, t.shape[0], t.shape[1], dist, tail, w.formats[t.name])
+
     out = {
         "metric": "FP8 scaled-GEMM TFLOP/s (7B MLP shape) + amax/cast GB/s, % of roofline",
         "value": round(flops / step_s / 1e12, 3),
@@ -297,9 +303,11 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8-e4m3 operands; bf16 MFMA (exact on FP8 values), f32 accumulate, bf16 out",
         "data": "synthetic",
-        "config": {"workload": w.name, "m": g.m, "n": g.n, "k": g.k, "x": "bf16 N(0,1)+0.1% x20",
-                   "w": "bf16 N(0,0.02)", "history_len": w.history_len, "margin": w.margin, "recipe": args.recipe,
-                   "output_cast": args.output_cast, "layernorm_x": bool(args.layernorm),
+        "config": {"workload": w.name, "m": g.m, "n": g.n, "k": g.k,
+                   "gemms": ["{} {}x{}x{} {}x{}".format(x.name, x.m, x.n, x.k, x.a_fmt, x.b_fmt) for x in w.gemms],
+                   "tensors": {t.name: describe(t) for t in w.tensors},
+                   "transposed_casts": list(w.transposed), "history_len": w.history_len, "margin": w.margin,
+                   "recipe": args.recipe, "output_cast": args.output_cast, "layernorm_x": bool(args.layernorm),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_MFMA_TFLOPS, 4),
