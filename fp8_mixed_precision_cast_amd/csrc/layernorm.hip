@@ -56,21 +56,33 @@ __device__ __forceinline__ float ln_out(float x, float mu, float rstd, float g, 
   return ((x - mu) * rstd) * g + b;
 }
 
-// Sum over the WPR waves that share a row (WPR = 1: the wave's own sum).
-// Every thread of the workgroup must call it the same number of times.
+// Partial sums each thread keeps for one row: with two waves per row a thread
+// plays two of the 256 virtual lanes below, otherwise one.
 template <int WPR>
-__device__ __forceinline__ float row_sum(float v, float* red) {
-  v = wave_sum(v);
+constexpr int kParts = WPR == 2 ? 2 : 1;
+
+// Row sum. One wave per row: the wave's butterfly. Two or four waves per row:
+// one order for both, so the result does not depend on which of those launch
+// shapes a width gets. The row's 16-byte chunks are dealt to 256 virtual
+// lanes (chunk c to lane c % 256); each lane adds its chunks in order (the
+// caller's partials); each virtual wave of 64 lanes reduces by the butterfly;
+// the four wave sums are added as (w0 + w1) + (w2 + w3). Thread t of a row with
+// T = 64 WPR threads holds virtual lanes t + T p, p < kParts. Every thread of
+// the workgroup must call it the same number of times.
+template <int WPR>
+__device__ __forceinline__ float row_sum(float (&part)[kParts<WPR>], float* red) {
   if constexpr (WPR == 1) {
-    return v;
+    return wave_sum(part[0]);
   } else {
     const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wave] = v;
-    __syncthreads();
-    const int first = wave / WPR * WPR;
-    float t = red[first];
+    const int rg = wave / WPR, wr = wave % WPR;   // row group of the workgroup, wave within the row
 #pragma unroll
-    for (int w = 1; w < WPR; ++w) t += red[first + w];
+    for (int p = 0; p < kParts<WPR>; ++p) {
+      const float w = wave_sum(part[p]);
+      if ((threadIdx.x & 63) == 0) red[rg * 4 + wr + WPR * p] = w;   // virtual wave (t + T p) / 64
+    }
+    __syncthreads();
+    const float t = (red[rg * 4] + red[rg * 4 + 1]) + (red[rg * 4 + 2] + red[rg * 4 + 3]);
     __syncthreads();   // red is reused by the next sum
     return t;
   }
@@ -87,7 +99,9 @@ __global__ __launch_bounds__(kLnBlock) void ln_rows_bf16(
     float* __restrict__ mean_out, float* __restrict__ rstd_out) {
   constexpr int kRowsPerBlock = kLnBlock / 64 / WPR;
   constexpr int T = 64 * WPR;
-  __shared__ float red[kLnBlock / 64];
+  constexpr int P = kParts<WPR>;
+  static_assert(WPR == 1 || T * P == 256, "two or four waves per row deal chunks to 256 virtual lanes");
+  __shared__ float red[kLnBlock / 64 * 2];
   const int t = threadIdx.x % T, rg = threadIdx.x / T;
   const int nch = cols >> 3;
   uint32_t am = 0;   // packed BF16 magnitudes of this thread's outputs
@@ -105,22 +119,27 @@ __global__ __launch_bounds__(kLnBlock) void ln_rows_bf16(
       const int c = t + T * u;
       v[u] = (live && c < nch) ? xr[c] : uint4{0u, 0u, 0u, 0u};
     }
-    float s = 0.f;
+    // chunk u of this thread is chunk t + T u of the row, virtual lane t + T (u % P)
+    float s[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) s[p] = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + T * u < nch) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s += bf16_lo(w[e]);
-          s += bf16_hi(w[e]);
+          s[u % P] += bf16_lo(w[e]);
+          s[u % P] += bf16_hi(w[e]);
         }
       }
     }
     const float n = (float)cols;
     const float mu = row_sum<WPR>(s, red) / n;
     keep_packed<U>(v);
-    float ss = 0.f;
+    float ss[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) ss[p] = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + T * u < nch) {
@@ -128,8 +147,8 @@ __global__ __launch_bounds__(kLnBlock) void ln_rows_bf16(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float d0 = bf16_lo(w[e]) - mu, d1 = bf16_hi(w[e]) - mu;
-          ss += d0 * d0;
-          ss += d1 * d1;
+          ss[u % P] += d0 * d0;
+          ss[u % P] += d1 * d1;
         }
       }
     }
@@ -298,16 +317,23 @@ hipError_t launch_reg(const LnArgs& a, int num_cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// At most kMaxChunksPerThread chunks per thread: rows up to 4096 columns take
-// one wave, longer rows two or four.
+// Chunks per thread and waves per row, measured per width: rows up to 2048
+// columns take one wave. Wider rows take two or four; with codes (more
+// registers live, so fewer waves fit) the wider split keeps more rows in
+// flight per CU. At most kMaxChunksPerThread chunks per thread.
 template <int YF>
 hipError_t launch_reg_u(const LnArgs& a, int num_cus, hipStream_t stream) {
   const int nch = a.cols / 8;
   if (nch <= 64 * 1) return launch_reg<1, 1, YF>(a, num_cus, stream);
   if (nch <= 64 * 2) return launch_reg<2, 1, YF>(a, num_cus, stream);
   if (nch <= 64 * 4) return launch_reg<4, 1, YF>(a, num_cus, stream);
-  if (nch <= 64 * 8) return launch_reg<8, 1, YF>(a, num_cus, stream);
-  if (nch <= 128 * 8) return launch_reg<8, 2, YF>(a, num_cus, stream);
+  if constexpr (YF == kNoQ) {
+    if (nch <= 128 * 4) return launch_reg<4, 2, YF>(a, num_cus, stream);
+    if (nch <= 128 * 8) return launch_reg<8, 2, YF>(a, num_cus, stream);
+  } else {
+    if (nch <= 256 * 2) return launch_reg<2, 4, YF>(a, num_cus, stream);
+    if (nch <= 256 * 4) return launch_reg<4, 4, YF>(a, num_cus, stream);
+  }
   return launch_reg<kMaxChunksPerThread, 4, YF>(a, num_cus, stream);
 }
 

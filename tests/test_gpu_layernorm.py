@@ -90,6 +90,27 @@ def test_layernorm_shapes(fmt, shape):
         _check(x, g, beta, eps, fmt, s, *res)
 
 
+@pytest.mark.parametrize("cols", [2056, 3072, 4096, 4104, 6144, 8192])
+def test_layernorm_output_modes_agree(cols):
+    """BF16 only, codes only and both: each width and mode picks its own launch shape; y is the same
+    bits in every mode and matches the oracle, the codes and amax are the oracle's cast of that y."""
+    require_gpu()
+    rows = 24
+    x, g, b = _inputs(cols + 1, rows, cols)
+    s, fmt = 8.0, "e4m3"
+    banner("layernorm modes", rows, cols)
+    y_both, q_both, am_both, mu, rs = _run(x, g, b, 1e-5, fmt, s)
+    _check(x, g, b, 1e-5, fmt, s, y_both, q_both, am_both, mu, rs)
+    y_only = torch.full((rows, cols), 0x1234, dtype=torch.int16, device="cuda")
+    fp8.fp8_layernorm_amax_cast(dev(x), dev(g), dev(b), 1e-5, fmt, y_only)
+    assert np.array_equal(host(y_only), y_both), first_diff(host(y_only), y_both)
+    q_only = torch.full((rows, cols), 0x5A, dtype=torch.uint8, device="cuda")
+    am = f32(0.0)
+    fp8.fp8_layernorm_amax_cast(dev(x), dev(g), dev(b), 1e-5, fmt, None, f32(s), q_only, am)
+    assert np.array_equal(host(q_only), q_both), first_diff(host(q_only), q_both)
+    assert _bits(host(am)[0]) == _bits(am_both)
+
+
 def test_layernorm_layouts_and_sources():
     """Strided rows (register path), odd strides (generic path), fp32 sources, no BF16 output."""
     require_gpu()
