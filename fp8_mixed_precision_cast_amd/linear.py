@@ -148,7 +148,7 @@ class LayerPlan:
         if self.recipe == "delayed":
             names = [n for n, o in self.operands.items()
                      if n not in self.ln and not o.transposed and inputs[n].is_contiguous()]
-            key = tuple((n, inputs[n].data_ptr()) for n in names)
+            key = tuple((n, inputs[n].data_ptr(), inputs[n].dtype, inputs[n].numel()) for n in names)
             if names and (self._cast_batch is None or self._cast_batch[0] != key):
                 items = [(inputs[n], self.state[n].fmt, self.state[n].scale, self.q[n], self.state[n].amax_slot)
                          for n in names]
