@@ -49,7 +49,8 @@ from .recipe import (amax, cast, DelayedScaling, max_nan, primed_scale, update_s
 from .gemm import gemm_ref, gemm_abs_ref, gemm_bound, gemm_check, gemm_entry
 from .layernorm import layer_norm_bound, layer_norm_check, layer_norm_ref
 from .allreduce import reduce_bound, reduce_check, reduce_ref, shared_scale
-from .adam import adam_step_f64, adam_step_ref, f16_decode, f16_encode, update_fp16_scale
+from .adam import (adam_step_f64, adam_step_ref, adam_weight_codes_ref, f16_decode, f16_encode,
+                   update_fp16_scale)
 
 __all__ = [
     "FMT", "FP8Format", "decode", "decode_table", "encode", "encode_scalar", "bf16_to_f32",
@@ -57,5 +58,5 @@ __all__ = [
     "gemm_ref", "gemm_abs_ref", "gemm_bound", "gemm_check", "gemm_entry",
     "layer_norm_ref", "layer_norm_bound", "layer_norm_check",
     "shared_scale", "reduce_ref", "reduce_bound", "reduce_check",
-    "adam_step_ref", "adam_step_f64", "f16_encode", "f16_decode", "update_fp16_scale",
+    "adam_step_ref", "adam_step_f64", "adam_weight_codes_ref", "f16_encode", "f16_decode", "update_fp16_scale",
 ]

@@ -80,6 +80,21 @@ def adam_step_ref(grad, g_dtype, m_q, m_dq, m_scale, v_bits, w_bits, w_dq, w_sca
     return m_new, v_new, w_new, max_nan(np.abs(m)), max_nan(np.abs(w))
 
 
+def adam_weight_codes_ref(w_bits, w_scale_inv, wq_scale, fmt):
+    """The next forward's weight operand from the master weights as stored.
+
+    [MPT] §横断的知見 "FP8 への拡張": the GEMM operands are FP8, so the updated weights
+    are cast before the next forward, with their own delayed scale ([TE]
+    §動的スケーリングとFP8レシピの設定). Reading taken: the weight cast is the stored
+    master weight, read back the way the next step reads it,
+        W = fp32(fp16 w) * w_scale_inv   (binary32),
+    then the saturating cast of W with the forward weight's scale; amax = max |W|.
+    Returns (codes, amax)."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        W = f16_decode(w_bits) * np.float32(w_scale_inv)
+    return cast(W, np.float32(wq_scale), fmt, "f32"), max_nan(np.abs(W))
+
+
 def adam_step_f64(g, m, v, w, lr, beta1, beta2, eps, wd, c1, c2):
     """Textbook Adam with decoupled weight decay, float64. Returns (m, v, w)."""
     g, m, v, w = (np.asarray(a, dtype=np.float64) for a in (g, m, v, w))

@@ -93,3 +93,25 @@ def test_binary32_step_rejects_plausible_mistakes():
                      "weight decay sign": dict(HP, wd=-HP["wd"]),
                      "lr doubled": dict(HP, lr=2 * HP["lr"])}.items():
         assert not np.array_equal(oracle.adam_step_ref(*args, **hp)[2], ref), name
+
+
+def test_weight_codes_hand_cases():
+    """Stored FP16 weights read back with the inverse scale, then cast. OCP E4M3: 1.0 = 0x38, 2.0 = 0x40,
+    0.375 = 0x2C (1.5 * 2^-2: exponent field 5, mantissa 100), 448 = 0x7E (largest), the NaN code 0x7F; E5M2: 1.0 = 0x3C, 57344 = 0x7B."""
+    w = oracle.f16_encode([4.0, -4.0, 1.5, 0.0, 60000.0, np.nan])          # stored values of w * s_w
+    q, am = oracle.adam_weight_codes_ref(w, 0.5, 0.5, "e4m3")             # W = 2, -2, 0.75, 0, 30000, NaN
+    assert [int(x) for x in q[:5]] == [0x38, 0xB8, 0x2C, 0x00, 0x7E]     # W * 0.5 = 1, -1, 0.375, 0, 15000 -> 448
+    assert int(q[5]) & 0x7F == 0x7F and np.isnan(am)
+    q, am = oracle.adam_weight_codes_ref(w[:5], 0.5, 2.0, "e5m2")        # W * 2 = 4, -4, 1.5, 0, 60000 -> 57344
+    assert [int(x) for x in q] == [0x44, 0xC4, 0x3E, 0x00, 0x7B]
+    assert am == np.float32(30000.0)
+
+
+def test_weight_codes_follow_the_stored_value_not_the_fp32_one():
+    """W is read back from FP16: 1 + 2^-12 is stored as 1.0 (spacing 2^-10 there), so a scale that puts
+    1.0 exactly on an E4M3 code gives that code, while the unrounded value would sit above it."""
+    w = oracle.f16_encode([1.0 + 2.0 ** -12])
+    assert int(w[0]) == 0x3C00
+    q, am = oracle.adam_weight_codes_ref(w, 1.0, 1.0, "e4m3")
+    assert int(q[0]) == 0x38 and am == np.float32(1.0)
+
