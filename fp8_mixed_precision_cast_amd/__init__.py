@@ -80,6 +80,9 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_adam_step.argtypes = [i64, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   fl, fl, fl, fl, fl, fl, fl, vp]
     lib.fp8_adam_step.restype = ctypes.c_int
+    lib.fp8_adam_step_weight_cast.argtypes = [i64, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, fl, fl, fl, fl, fl, fl, fl, ctypes.c_int, vp, vp, vp, vp]
+    lib.fp8_adam_step_weight_cast.restype = ctypes.c_int
     lib.fp8mp_status_string.argtypes = [ctypes.c_int]
     lib.fp8mp_status_string.restype = ctypes.c_char_p
     lib.fp8mp_device_info.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -288,20 +291,28 @@ def fp8_reduce_shared_scale(q, fmt, scale_inv, out, stream=None) -> None:
 
 
 def fp8_adam_step(grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w, w_dq_in, w_dq_out, w_scale,
-                  w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2, stream=None) -> None:
-    """One Adam step over FP8 m (codes), FP16 v and tensor-scaled FP16 w (all updated in place)."""
+                  w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2, stream=None,
+                  wq=None, wq_fmt="e4m3", wq_scale=None, wq_amax=None) -> None:
+    """One Adam step over FP8 m (codes), FP16 v and tensor-scaled FP16 w (all updated in place).
+
+    With wq and/or wq_amax (fp8_adam_step_weight_cast): also wq = enc(W * wq_scale) and
+    wq_amax = max(wq_amax, max |W|) for the stored master weights W = fp16 w * w_scale_inv."""
     n = grad.numel()
-    for t, name in ((m_q, "m_q"), (v, "v"), (w, "w")):
+    for t, name in ((m_q, "m_q"), (v, "v"), (w, "w")) + (((wq, "wq"),) if wq is not None else ()):
         if t.numel() != n or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous with as many elements as grad")
     if not grad.is_contiguous():
         raise ValueError("grad must be contiguous")
-    st = load_library().fp8_adam_step(
-        n, _ptr(grad), _src_dtype(grad), _ptr(m_q), _ptr(m_dq_in), _ptr(m_dq_out), _ptr(m_scale), _ptr(m_scale_inv),
-        _ptr(m_amax), _ptr(v), _ptr(w), _ptr(w_dq_in), _ptr(w_dq_out), _ptr(w_scale), _ptr(w_scale_inv),
-        _ptr(w_amax), float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(bias_c1),
-        float(bias_c2), _stream(stream))
-    _check(st, "fp8_adam_step")
+    args = (n, _ptr(grad), _src_dtype(grad), _ptr(m_q), _ptr(m_dq_in), _ptr(m_dq_out), _ptr(m_scale),
+            _ptr(m_scale_inv), _ptr(m_amax), _ptr(v), _ptr(w), _ptr(w_dq_in), _ptr(w_dq_out), _ptr(w_scale),
+            _ptr(w_scale_inv), _ptr(w_amax), float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+            float(bias_c1), float(bias_c2))
+    if wq is None and wq_amax is None:
+        _check(load_library().fp8_adam_step(*args, _stream(stream)), "fp8_adam_step")
+    else:
+        st = load_library().fp8_adam_step_weight_cast(*args, FORMATS[wq_fmt], _ptr(wq_scale), _ptr(wq), _ptr(wq_amax),
+                                                      _stream(stream))
+        _check(st, "fp8_adam_step_weight_cast")
 
 
 class AdamFP8State:
@@ -314,7 +325,9 @@ class AdamFP8State:
     """
 
     def __init__(self, w0, history_len: int = 16, margin: int = 0, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
-                 weight_decay=0.0):
+                 weight_decay=0.0, weight_codes: Optional[str] = None, weight_history_len: int = 1024):
+        """weight_codes ("e4m3" or "e5m2"): every step also writes self.wq, the codes of the updated
+        master weights for the next forward, under their own delayed scaling (self.wq_state)."""
         import torch
         dev = w0.device
         self.n = w0.numel()
@@ -328,6 +341,10 @@ class AdamFP8State:
         self.m_dq = torch.ones(2, dtype=torch.float32, device=dev)
         self.w_dq = torch.ones(2, dtype=torch.float32, device=dev)
         self.cur = 0
+        self.wq = self.wq_state = None
+        if weight_codes is not None:
+            self.wq = torch.zeros(self.n, dtype=torch.uint8, device=dev)
+            self.wq_state = DelayedScalingState(weight_codes, weight_history_len, margin, dev)
 
     def step(self, grad, stream=None) -> None:
         self.t += 1
@@ -335,11 +352,16 @@ class AdamFP8State:
         c1, c2 = 1.0 / (1.0 - b1 ** self.t), 1.0 / (1.0 - b2 ** self.t)
         i, o = self.cur, 1 - self.cur
         ms, ws = self.m_state, self.w_state
+        qs = self.wq_state
         fp8_adam_step(grad.reshape(-1), self.m_q, self.m_dq[i:i + 1], self.m_dq[o:o + 1], ms.scale, ms.scale_inv,
                       ms.amax_slot, self.v, self.w, self.w_dq[i:i + 1], self.w_dq[o:o + 1], ws.scale, ws.scale_inv,
-                      ws.amax_slot, self.hp["lr"], b1, b2, self.hp["eps"], self.hp["weight_decay"], c1, c2, stream)
+                      ws.amax_slot, self.hp["lr"], b1, b2, self.hp["eps"], self.hp["weight_decay"], c1, c2, stream,
+                      wq=self.wq, wq_fmt=qs.fmt if qs else "e4m3", wq_scale=qs.scale if qs else None,
+                      wq_amax=qs.amax_slot if qs else None)
         ms.update(stream)
         ws.update(stream)
+        if qs is not None:
+            qs.update(stream)
         self.cur = o
 
     def master_weights(self):

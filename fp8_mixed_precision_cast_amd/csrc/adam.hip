@@ -18,6 +18,12 @@
 //   m_q = enc_e4m3(m * m_scale); v = fp16(v); w = fp16(w * w_scale)
 // FP16 stores round to nearest even and saturate at +-65504. HBM traffic per
 // parameter: grad 2 (BF16) or 4, m 1 + 1, v 2 + 2, w 2 + 2 bytes.
+//
+// With WQF (a format) the same pass also writes the next forward's weight
+// codes from the master weights as stored: W = fp32(fp16 w) * w_scale_inv
+// (what the next step reads back), wq = enc_WQF(W * wq_scale), and records
+// max |W| for that tensor's own delayed scale: one more byte per parameter
+// instead of a separate pass that reads the 2-byte master weights again.
 #include "common.h"
 
 namespace fp8mp {
@@ -57,16 +63,31 @@ __device__ __forceinline__ float load_grad(const void* grad, int64_t i) {
   return static_cast<const float*>(grad)[i];
 }
 
-template <int GD>
+// No forward weight codes (WQF of the plain step).
+constexpr int kNoWq = -1;
+
+// The forward weight codes' outputs.
+struct WqOut {
+  const float* scale;   // the forward weight's scale in force (read)
+  uint8_t* q;           // n codes or NULL
+  float* amax;          // max |W| accumulated, or NULL
+};
+
+template <int GD, int WQF>
 __global__ __launch_bounds__(kAdamBlock) void adam_kernel(
     int64_t n, const void* __restrict__ grad, uint8_t* __restrict__ m_q, const float* __restrict__ m_dq_in,
     float* __restrict__ m_dq_out, const float* __restrict__ m_scale, const float* __restrict__ m_scale_inv,
     float* __restrict__ m_amax, uint16_t* __restrict__ v16, uint16_t* __restrict__ w16,
     const float* __restrict__ w_dq_in, float* __restrict__ w_dq_out, const float* __restrict__ w_scale,
-    const float* __restrict__ w_scale_inv, float* __restrict__ w_amax, AdamHp hp, int vec) {
+    const float* __restrict__ w_scale_inv, float* __restrict__ w_amax, AdamHp hp, int vec, WqOut wqo) {
   const float mdq = *m_dq_in, wdq = *w_dq_in, ms = *m_scale, ws = *w_scale;
+  float wsi = 0.f, qs = 0.f;
+  if constexpr (WQF != kNoWq) {
+    wsi = *w_scale_inv;
+    qs = wqo.q != nullptr ? *wqo.scale : 0.f;
+  }
   const int64_t tid = (int64_t)blockIdx.x * kAdamBlock + threadIdx.x, nthreads = (int64_t)gridDim.x * kAdamBlock;
-  uint32_t am_m = 0, am_w = 0;
+  uint32_t am_m = 0, am_w = 0, am_q = 0;
   int64_t start = 0;
   if (vec) {
     // Eight parameters per thread and iteration: 16 B of BF16 gradient (32 B
@@ -125,6 +146,19 @@ __global__ __launch_bounds__(kAdamBlock) void adam_kernel(
       }
       reinterpret_cast<uint4*>(v16)[c] = uint4{vo[0], vo[1], vo[2], vo[3]};
       reinterpret_cast<uint4*>(w16)[c] = uint4{wo[0], wo[1], wo[2], wo[3]};
+      if constexpr (WQF != kNoWq) {
+        float W[8];   // the master weights as stored, read back
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          W[2 * k] = f16_to_f32((uint16_t)(wo[k] & 0xFFFFu)) * wsi;
+          W[2 * k + 1] = f16_to_f32((uint16_t)(wo[k] >> 16)) * wsi;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am_q = amax_f32(am_q, W[e]);
+        if (wqo.q != nullptr)
+          reinterpret_cast<uint2*>(wqo.q)[c] =
+              uint2{enc4<WQF>(W[0], W[1], W[2], W[3], qs), enc4<WQF>(W[4], W[5], W[6], W[7], qs)};
+      }
     }
     start = n8 * 8;
   }
@@ -138,7 +172,13 @@ __global__ __launch_bounds__(kAdamBlock) void adam_kernel(
     am_w = amax_f32(am_w, w);
     m_q[i] = enc1<FP8MP_E4M3>(m, ms);
     v16[i] = f32_to_f16_sat(v);
-    w16[i] = f32_to_f16_sat(w * ws);
+    const uint16_t wh = f32_to_f16_sat(w * ws);
+    w16[i] = wh;
+    if constexpr (WQF != kNoWq) {
+      const float W = f16_to_f32(wh) * wsi;
+      am_q = amax_f32(am_q, W);
+      if (wqo.q != nullptr) wqo.q[i] = enc1<WQF>(W, qs);
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     // the inverses of the scales this step wrote with, for the next step's reads
@@ -150,9 +190,46 @@ __global__ __launch_bounds__(kAdamBlock) void adam_kernel(
     __syncthreads();   // the block reduction's shared slots are reused
     block_amax_commit<kAdamBlock>(am_w, w_amax);
   }
+  if constexpr (WQF != kNoWq) {
+    if (wqo.amax != nullptr) {
+      __syncthreads();
+      block_amax_commit<kAdamBlock>(am_q, wqo.amax);
+    }
+  }
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+template <int GD, int WQF>
+void launch_kernel(int grid, hipStream_t stream, int64_t n, const void* grad, uint8_t* m_q, const float* m_dq_in,
+                   float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax, uint16_t* v,
+                   uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale, const float* w_scale_inv,
+                   float* w_amax, const AdamHp& hp, int vec, const WqOut& wqo) {
+  hipLaunchKernelGGL((adam_kernel<GD, WQF>), dim3(grid), dim3(kAdamBlock), 0, stream, n, grad, m_q, m_dq_in, m_dq_out,
+                     m_scale, m_scale_inv, m_amax, v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, hp, vec,
+                     wqo);
+}
+
+template <int WQF>
+hipError_t launch_fmt(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uint8_t* m_q, const float* m_dq_in,
+                      float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax, uint16_t* v,
+                      uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
+                      const float* w_scale_inv, float* w_amax, const AdamHp& hp, const WqOut& wqo, int num_cus,
+                      hipStream_t stream) {
+  const int vec = aligned(grad, 16) && aligned(m_q, 8) && aligned(v, 16) && aligned(w, 16) &&
+                  (wqo.q == nullptr || aligned(wqo.q, 8));
+  const int64_t work = vec ? (n + 7) / 8 : n;
+  const int64_t need = (work + kAdamBlock - 1) / kAdamBlock;
+  const int64_t cap = (int64_t)num_cus * 4;
+  const int grid = (int)(need < cap ? (need > 0 ? need : 1) : cap);
+  if (grad_dtype == FP8MP_BF16)
+    launch_kernel<FP8MP_BF16, WQF>(grid, stream, n, grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w,
+                                   w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, hp, vec, wqo);
+  else
+    launch_kernel<FP8MP_F32, WQF>(grid, stream, n, grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w,
+                                  w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, hp, vec, wqo);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -160,22 +237,18 @@ hipError_t launch_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype,
                             float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax,
                             uint16_t* v, uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
                             const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
-                            float weight_decay, float bias_c1, float bias_c2, int num_cus, hipStream_t stream) {
+                            float weight_decay, float bias_c1, float bias_c2, int wq_fmt, const float* wq_scale,
+                            uint8_t* wq, float* wq_amax, int num_cus, hipStream_t stream) {
   const AdamHp hp{lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2};
-  const int vec = aligned(grad, 16) && aligned(m_q, 8) && aligned(v, 16) && aligned(w, 16);
-  const int64_t work = vec ? (n + 7) / 8 : n;
-  const int64_t need = (work + kAdamBlock - 1) / kAdamBlock;
-  const int64_t cap = (int64_t)num_cus * 4;
-  const int grid = (int)(need < cap ? (need > 0 ? need : 1) : cap);
-  if (grad_dtype == FP8MP_BF16)
-    hipLaunchKernelGGL((adam_kernel<FP8MP_BF16>), dim3(grid), dim3(kAdamBlock), 0, stream, n, grad, m_q, m_dq_in,
-                       m_dq_out, m_scale, m_scale_inv, m_amax, v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax,
-                       hp, vec);
-  else
-    hipLaunchKernelGGL((adam_kernel<FP8MP_F32>), dim3(grid), dim3(kAdamBlock), 0, stream, n, grad, m_q, m_dq_in,
-                       m_dq_out, m_scale, m_scale_inv, m_amax, v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax,
-                       hp, vec);
-  return hipGetLastError();
+  const WqOut wqo{wq_scale, wq, wq_amax};
+  const bool with_wq = wq != nullptr || wq_amax != nullptr;
+#define FP8MP_ADAM(WQF)                                                                                              \
+  launch_fmt<WQF>(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w, w_dq_in, w_dq_out, \
+                  w_scale, w_scale_inv, w_amax, hp, wqo, num_cus, stream)
+  if (!with_wq) return FP8MP_ADAM(kNoWq);
+  if (wq_fmt == FP8MP_E5M2) return FP8MP_ADAM(FP8MP_E5M2);
+  return FP8MP_ADAM(FP8MP_E4M3);
+#undef FP8MP_ADAM
 }
 
 }  // namespace fp8mp

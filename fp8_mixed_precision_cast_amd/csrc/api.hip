@@ -285,13 +285,15 @@ fp8mp_status fp8_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t
                                                     cus, stream));
 }
 
-fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uint8_t* m_q, const float* m_dq_in,
-                           float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax,
-                           uint16_t* v, uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
-                           const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
-                           float weight_decay, float bias_c1, float bias_c2, hipStream_t stream) {
+namespace {
+
+// Validation shared by both Adam entry points (no device access).
+fp8mp_status check_adam(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uint8_t* m_q, const float* m_dq_in,
+                        float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax, uint16_t* v,
+                        uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
+                        const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, float bias_c1, float bias_c2) {
   if (!valid_dtype(grad_dtype) || n < 0) return FP8MP_ERR_INVALID_ARG;
-  if (n == 0) return FP8MP_OK;
   const void* required[] = {grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, v, w, w_dq_in, w_dq_out,
                             w_scale, w_scale_inv};
   for (const void* p : required)
@@ -306,12 +308,53 @@ fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype, 
   const float hp[] = {lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2};
   for (float x : hp)
     if (!std::isfinite(x)) return FP8MP_ERR_INVALID_ARG;
+  return FP8MP_OK;
+}
+
+}  // namespace
+
+fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uint8_t* m_q, const float* m_dq_in,
+                           float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax,
+                           uint16_t* v, uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
+                           const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
+                           float weight_decay, float bias_c1, float bias_c2, hipStream_t stream) {
+  fp8mp_status st = check_adam(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w,
+                               w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay,
+                               bias_c1, bias_c2);
+  if (st != FP8MP_OK || n == 0) return st;
   int cus = 0;
-  fp8mp_status st = check_device(&cus);
+  st = check_device(&cus);
   if (st != FP8MP_OK) return st;
   return from_hip(fp8mp::launch_adam_step(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax,
                                           v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2,
-                                          eps, weight_decay, bias_c1, bias_c2, cus, stream));
+                                          eps, weight_decay, bias_c1, bias_c2, -1, nullptr, nullptr, nullptr, cus,
+                                          stream));
+}
+
+fp8mp_status fp8_adam_step_weight_cast(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uint8_t* m_q,
+                                       const float* m_dq_in, float* m_dq_out, const float* m_scale,
+                                       const float* m_scale_inv, float* m_amax, uint16_t* v, uint16_t* w,
+                                       const float* w_dq_in, float* w_dq_out, const float* w_scale,
+                                       const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2,
+                                       float eps, float weight_decay, float bias_c1, float bias_c2,
+                                       fp8mp_format wq_fmt, const float* wq_scale, uint8_t* wq, float* wq_amax,
+                                       hipStream_t stream) {
+  fp8mp_status st = check_adam(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w,
+                               w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay,
+                               bias_c1, bias_c2);
+  if (st != FP8MP_OK) return st;
+  if (!valid_format(wq_fmt) || (wq == nullptr && wq_amax == nullptr) || (wq != nullptr && wq_scale == nullptr))
+    return FP8MP_ERR_INVALID_ARG;
+  if ((wq_scale != nullptr && !is_aligned(wq_scale, 4)) || (wq_amax != nullptr && !is_aligned(wq_amax, 4)))
+    return FP8MP_ERR_INVALID_ARG;
+  if (n == 0) return FP8MP_OK;
+  int cus = 0;
+  st = check_device(&cus);
+  if (st != FP8MP_OK) return st;
+  return from_hip(fp8mp::launch_adam_step(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax,
+                                          v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2,
+                                          eps, weight_decay, bias_c1, bias_c2, wq_fmt, wq_scale, wq, wq_amax, cus,
+                                          stream));
 }
 
 const char* fp8mp_status_string(fp8mp_status status) {

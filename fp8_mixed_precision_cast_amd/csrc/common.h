@@ -219,7 +219,8 @@ hipError_t launch_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype,
                             float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax,
                             uint16_t* v, uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
                             const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
-                            float weight_decay, float bias_c1, float bias_c2, int num_cus, hipStream_t stream);
+                            float weight_decay, float bias_c1, float bias_c2, int wq_fmt, const float* wq_scale,
+                            uint8_t* wq, float* wq_amax, int num_cus, hipStream_t stream);
 hipError_t launch_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t n_ranks, int64_t numel,
                                       int64_t rank_stride, const float* scale_inv, void* out,
                                       fp8mp_dtype out_dtype, int num_cus, hipStream_t stream);

@@ -310,6 +310,39 @@ fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype,
                            float lr, float beta1, float beta2, float eps, float weight_decay,
                            float bias_c1, float bias_c2, hipStream_t stream);
 
+/*
+ * fp8_adam_step_weight_cast: fp8_adam_step, and in the same pass the FP8
+ * codes of the updated master weights for the next forward GEMM.
+ *
+ * [MPT] §横断的知見 "FP8 への拡張": the GEMMs run on FP8 operands, so every
+ * optimizer step is followed by a cast of the new weights for the next
+ * forward; [TE] §動的スケーリングとFP8レシピの設定: that operand keeps its own
+ * amax history and delayed scale. Doing the cast here saves the pass that
+ * would read the 2-byte master weights again. The weight is taken as stored:
+ *   W = fp32(fp16 w) * *w_scale_inv   (binary32; what the next step reads back)
+ *   wq[i] = enc_wq_fmt(W[i] * *wq_scale)   (the saturating cast of fp8_amax_cast)
+ *   *wq_amax = max(*wq_amax, max |W|)
+ * Every other output is exactly fp8_adam_step's.
+ *
+ *   wq_fmt    FP8MP_E4M3 or FP8MP_E5M2 (FP8MP_FP16 is rejected).
+ *   wq_scale  one fp32 on the device: the forward weight's scale in force;
+ *             required when wq is given.
+ *   wq        n codes, or NULL (amax only).
+ *   wq_amax   one fp32, max-accumulated, or NULL; wq and wq_amax are not
+ *             both NULL.
+ * Errors and ownership as fp8_adam_step.
+ */
+fp8mp_status fp8_adam_step_weight_cast(int64_t n, const void* grad, fp8mp_dtype grad_dtype,
+                                       uint8_t* m_q, const float* m_dq_in, float* m_dq_out,
+                                       const float* m_scale, const float* m_scale_inv, float* m_amax,
+                                       uint16_t* v,
+                                       uint16_t* w, const float* w_dq_in, float* w_dq_out,
+                                       const float* w_scale, const float* w_scale_inv, float* w_amax,
+                                       float lr, float beta1, float beta2, float eps, float weight_decay,
+                                       float bias_c1, float bias_c2,
+                                       fp8mp_format wq_fmt, const float* wq_scale, uint8_t* wq, float* wq_amax,
+                                       hipStream_t stream);
+
 /* A static, human-readable name of a status code. Never NULL. */
 const char* fp8mp_status_string(fp8mp_status status);
 

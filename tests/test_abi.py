@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(lib):
                      "fp8_scaled_gemm",
                      "fp8_scaled_gemm_amax_cast",
                      "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step",
-                     "fp8mp_status_string", "fp8mp_device_info"]
+                     "fp8_adam_step_weight_cast", "fp8mp_status_string", "fp8mp_device_info"]
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {fp8.lib_path()}").read()
@@ -205,8 +205,35 @@ def test_adam_argument_validation(lib):
     assert lib.fp8_amax_cast(A16, 1, 4, 4, 4, 2, A16, A16, 4, None, 0, None, None) == INVALID   # not for casts
 
 
+def _adam_wq_args(B, **kw):
+    a = dict(n=64, g=B[0], gd=1, mq=B[1], mdi=B[2], mdo=B[3], ms=B[4], msi=B[5], ma=None, v=B[6], w=B[7],
+             wdi=B[8], wdo=B[9], ws=B[10], wsi=B[11], wa=None, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0,
+             c1=10.0, c2=1000.0, qf=0, qs=B[12], q=B[13], qa=B[14])
+    a.update(kw)
+    return [a[k] for k in ("n", "g", "gd", "mq", "mdi", "mdo", "ms", "msi", "ma", "v", "w", "wdi", "wdo", "ws",
+                           "wsi", "wa", "lr", "b1", "b2", "eps", "wd", "c1", "c2", "qf", "qs", "q", "qa")] + [None]
+
+
+def test_adam_weight_cast_argument_validation(lib):
+    f = lib.fp8_adam_step_weight_cast
+    B = [P(4096 + 16 * i) for i in range(15)]
+    assert f(*_adam_wq_args(B, gd=4)) == INVALID                  # the Adam step's own checks apply
+    assert f(*_adam_wq_args(B, mdo=B[2])) == INVALID
+    assert f(*_adam_wq_args(B, qf=2)) == INVALID                  # FP16 is a storage format, not a cast target
+    assert f(*_adam_wq_args(B, qf=7)) == INVALID
+    assert f(*_adam_wq_args(B, q=None, qa=None)) == INVALID       # nothing to write
+    assert f(*_adam_wq_args(B, qs=None)) == INVALID               # codes need the scale
+    assert f(*_adam_wq_args(B, qs=P(4098))) == INVALID
+    assert f(*_adam_wq_args(B, qa=P(4098))) == INVALID
+    assert f(*_adam_wq_args(B, n=0)) == OK
+    assert f(*_adam_wq_args(B, n=0, q=None, qs=None)) == OK     # amax only: no scale needed
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful without a device")
 def test_valid_calls_without_device_report_no_device(lib):
+    B = [P(4096 + 16 * i) for i in range(15)]
+    assert lib.fp8_adam_step_weight_cast(*_adam_wq_args(B)) == NO_DEVICE
+    assert lib.fp8_adam_step_weight_cast(*_adam_wq_args(B, qf=1, q=None, qs=None)) == NO_DEVICE
     assert lib.fp8_scale_update(A16, 4, 0, 0, A16, A16, None) == NO_DEVICE
     assert lib.fp8_amax_cast(A16, 1, 4, 4, 4, 0, A16, A16, 4, None, 0, A16, None) == NO_DEVICE
     assert lib.fp8_scaled_gemm(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE

@@ -98,14 +98,64 @@ def test_adam_special_values():
     assert _bits(got[3]) == _bits(ref[3]) and _bits(got[4]) == _bits(ref[4])   # NaN amaxes are canonical
 
 
+def _gpu_step_wq(g, g_dtype, m_q, v, w, m_dq, m_scale, w_dq, w_scale, hp, fmt, wq_scale, offset=0, codes=True):
+    """fp8_adam_step_weight_cast; the codes buffer sits `offset` bytes past an aligned start."""
+    n = m_q.size
+    dg = dev(g).view(torch.int16) if g_dtype == "bf16" else dev(g)
+    dm, dv, dw = dev(m_q), dev(v).view(torch.int16), dev(w).view(torch.int16)
+    scal = {k: f32(x) for k, x in dict(mdi=m_dq, ms=m_scale, msi=np.float32(1) / np.float32(m_scale), wdi=w_dq,
+                                       ws=w_scale, wsi=np.float32(1) / np.float32(w_scale), qs=wq_scale).items()}
+    mdo, wdo, ma, wa, qa = f32(-1.0), f32(-1.0), f32(0.0), f32(0.0), f32(0.0)
+    wq = None
+    if codes:
+        buf = torch.full((n + offset + 1,), 0x5A, dtype=torch.uint8, device="cuda")
+        wq = buf[offset:offset + n]
+    fp8.fp8_adam_step(dg, dm, scal["mdi"], mdo, scal["ms"], scal["msi"], ma, dv, dw, scal["wdi"], wdo, scal["ws"],
+                      scal["wsi"], wa, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"], hp["c1"], hp["c2"],
+                      wq=wq, wq_fmt=fmt, wq_scale=scal["qs"], wq_amax=qa)
+    if codes:
+        hb = host(buf)
+        assert (hb[:offset] == 0x5A).all() and hb[offset + n] == 0x5A, "wrote outside the codes"
+    got = (host(dm), host(dv), host(dw), host(ma)[0], host(wa)[0], host(mdo)[0], host(wdo)[0],
+           host(scal["msi"])[0], host(scal["wsi"])[0])
+    return got, (host(wq) if codes else None), host(qa)[0]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("n", [1, 9, 4099, 100000])
+def test_adam_weight_codes_bit_exact(fmt, n):
+    """The fused step's every other output is the plain step's; the codes and amax are the oracle's cast of
+    the master weights as this step stored them."""
+    require_gpu()
+    rng = np.random.default_rng(100 + n)
+    g, m_q, v, w = _state(rng, n, "bf16")
+    m_dq, w_dq = np.float32(2.0 ** -14), np.float32(1 / 1024)
+    for offset, w_scale, q_scale in ((0, 1024.0, 448.0 / 0.08), (3, 777.0, 60.0), (0, 1024.0, 1e9)):
+        banner("adam-wq", fmt, n, offset, w_scale, q_scale)
+        ref = oracle.adam_step_ref(g, "bf16", m_q, m_dq, 2.0 ** 14, v, w, w_dq, w_scale, **HP)
+        got, wq, qa = _gpu_step_wq(g, "bf16", m_q, v, w, m_dq, 2.0 ** 14, w_dq, w_scale, HP, fmt, q_scale, offset)
+        _compare(ref, got)
+        want_q, want_a = oracle.adam_weight_codes_ref(got[2], got[8], q_scale, fmt)
+        assert np.array_equal(wq, want_q), "weight codes: " + first_diff(wq, want_q)
+        assert _bits(qa) == _bits(oracle.max_nan([np.float32(0), want_a]))
+    got, wq, qa = _gpu_step_wq(g, "bf16", m_q, v, w, m_dq, 2.0 ** 14, w_dq, 1024.0, HP, fmt, 1.0, codes=False)
+    _compare(oracle.adam_step_ref(g, "bf16", m_q, m_dq, 2.0 ** 14, v, w, w_dq, 1024.0, **HP), got)
+    assert _bits(qa) == _bits(oracle.max_nan([np.float32(0), oracle.adam_weight_codes_ref(got[2], got[8], 1.0,
+                                                                                          fmt)[1]]))
+
+
 def test_adam_fp8_state_recipe_over_steps():
-    """AdamFP8State for 12 steps against the oracle's step plus delayed updates (E4M3 for m, FP16 for w)."""
+    """AdamFP8State for 12 steps against the oracle's step plus delayed updates (E4M3 for m, FP16 for w),
+    with the next forward's E4M3 weight codes and their own delayed scale."""
     require_gpu()
     rng = np.random.default_rng(11)
     n, L = 5003, 4
     w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
     hp = dict(lr=1e-2, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.1)
-    st = fp8.AdamFP8State(torch.from_numpy(w0).cuda(), history_len=L, **hp)
+    st = fp8.AdamFP8State(torch.from_numpy(w0).cuda(), history_len=L, weight_codes="e4m3", weight_history_len=L,
+                          **hp)
+    q_s = q_si = np.float32(1)
+    q_h = np.zeros(L, np.float32)
     # oracle state
     m_q = np.zeros(n, np.uint8)
     v = np.zeros(n, np.uint16)
@@ -119,6 +169,9 @@ def test_adam_fp8_state_recipe_over_steps():
         m_q, v, w, ma, wa = oracle.adam_step_ref(g, "bf16", m_q, m_dq, m_s, v, w, w_dq, w_s, hp["lr"], hp["beta1"],
                                                  hp["beta2"], hp["eps"], hp["weight_decay"], c1, c2)
         m_dq, w_dq = m_si, w_si
+        wq, qa = oracle.adam_weight_codes_ref(w, w_si, q_s, "e4m3")   # cast with the forward weight's scale in force
+        q_h[0] = oracle.max_nan([q_h[0], qa])
+        q_s, q_si, q_h = oracle.update_scale(q_h, q_s, q_si, "e4m3", 0)
         m_h[0] = oracle.max_nan([m_h[0], ma])
         w_h[0] = oracle.max_nan([w_h[0], wa])
         m_s, m_si, m_h = oracle.update_scale(m_h, m_s, m_si, "e4m3", 0)
@@ -130,6 +183,8 @@ def test_adam_fp8_state_recipe_over_steps():
         assert np.array_equal(host(st.w.view(torch.int16)), w), t
         assert _bits(host(st.m_state.scale))[0] == _bits(m_s) and _bits(host(st.w_state.scale))[0] == _bits(w_s)
         assert _bits(host(st.m_dq)[st.cur]) == _bits(m_dq) and _bits(host(st.w_dq)[st.cur]) == _bits(w_dq)
+        assert np.array_equal(host(st.wq), wq), (t, first_diff(host(st.wq), wq))
+        assert _bits(host(st.wq_state.scale))[0] == _bits(q_s)
     # the master weights moved against the mean gradient sign, as Adam does
     assert np.isfinite(host(st.master_weights())).all()
 
