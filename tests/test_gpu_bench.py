@@ -1,0 +1,44 @@
+"""bench.py end to end on the GPU with few steps, in this process: the one JSON line and its contract
+fields, and the diagnostic modes at small sizes."""
+import json
+import os
+import sys
+
+import pytest
+
+from tests.gpu_util import require_gpu
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(monkeypatch, capsys, *args):
+    sys.path.insert(0, ROOT)
+    import bench
+    monkeypatch.setattr(sys, "argv", ["bench.py", *args])
+    bench.main()
+    out = capsys.readouterr().out
+    return [json.loads(line) for line in out.splitlines() if line.startswith("{")]
+
+
+def test_bench_line_contract(monkeypatch, capsys):
+    require_gpu()
+    (line,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+                "vs_baseline", "dtype", "data", "config", "roofline", "components"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["steps"] == 2 and line["warmup"] == 1
+    assert line["config"]["workload"] == "mlp7b_up_fwd" and line["value"] > 0
+    roof = line["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+
+
+def test_bench_diagnostic_modes(monkeypatch, capsys):
+    require_gpu()
+    lines = _run(monkeypatch, capsys, "--gemm-data", "512x768x256")
+    kinds = {l.get("gemm_data") for l in lines if "gemm_data" in l}
+    assert kinds == {"zero", "one", "uniform", "normal"}
+    assert all(l["tflops"] > 0 for l in lines if "gemm_data" in l)
+    (copy,) = _run(monkeypatch, capsys, "--copy-reference", str(1 << 24))
+    assert copy["copy_reference_bytes"] == 1 << 24 and copy["copy_gbps"] > 0
