@@ -90,8 +90,10 @@ __device__ __forceinline__ float row_sum(float (&part)[kParts<WPR>], float* red)
 
 // Register path. WPR waves share a row (rows per workgroup = 4 / WPR); thread
 // t of a row holds the row's 16-byte chunks t, t + T, t + 2T, ... (T = 64 WPR
-// threads, at most U of them), so the row is read from HBM once.
-template <int U, int WPR, int YF>
+// threads, at most U of them), so the row is read from HBM once. PF: the next
+// row group's chunks are loaded while this one is normalised (twice the bytes
+// in flight per thread, for 4U more registers).
+template <int U, int WPR, int YF, bool PF>
 __global__ __launch_bounds__(kLnBlock) void ln_rows_bf16(
     const uint16_t* __restrict__ x, int64_t rows, int cols, int64_t ld_x, const float* __restrict__ gamma,
     const float* __restrict__ beta, float eps, uint16_t* __restrict__ y, int64_t ld_y,
@@ -109,15 +111,39 @@ __global__ __launch_bounds__(kLnBlock) void ln_rows_bf16(
   // whole workgroup (row_sum's barriers need it); a row past the end only
   // takes part in the sums. A bounded grid keeps the amax to one atomic per
   // workgroup.
-  for (int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock; r0 < rows; r0 += (int64_t)gridDim.x * kRowsPerBlock) {
-    const int64_t row = r0 + rg;
+  uint4 vn[PF ? U : 1];   // PF: the next row group's chunks, in flight
+  if constexpr (PF) {
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + rg;
     const bool live = row < rows;
     const uint4* xr = reinterpret_cast<const uint4*>(x + (live ? row : 0) * ld_x);
-    uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = t + T * u;
-      v[u] = (live && c < nch) ? xr[c] : uint4{0u, 0u, 0u, 0u};
+      vn[u] = (live && c < nch) ? xr[c] : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  for (int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock; r0 < rows; r0 += (int64_t)gridDim.x * kRowsPerBlock) {
+    const int64_t row = r0 + rg;
+    const bool live = row < rows;
+    uint4 v[U];
+    if constexpr (PF) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = vn[u];
+      const int64_t nrow = row + (int64_t)gridDim.x * kRowsPerBlock;
+      const bool nlive = nrow < rows;
+      const uint4* xn = reinterpret_cast<const uint4*>(x + (nlive ? nrow : 0) * ld_x);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = t + T * u;
+        vn[u] = (nlive && c < nch) ? xn[c] : uint4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const uint4* xr = reinterpret_cast<const uint4*>(x + (live ? row : 0) * ld_x);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = t + T * u;
+        v[u] = (live && c < nch) ? xr[c] : uint4{0u, 0u, 0u, 0u};
+      }
     }
     // chunk u of this thread is chunk t + T u of the row, virtual lane t + T (u % P)
     float s[P];
@@ -294,27 +320,42 @@ struct LnArgs {
 // 1; computed once per instantiation). The grid-stride kernels launch exactly
 // that many per CU, so every workgroup is resident from the start and there
 // is no second round.
-template <int U, int WPR, int YF>
+template <int U, int WPR, int YF, bool PF>
 int resident_blocks() {
   static const int n = []() {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, ln_rows_bf16<U, WPR, YF>, kLnBlock, 0) != hipSuccess || b < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, ln_rows_bf16<U, WPR, YF, PF>, kLnBlock, 0) != hipSuccess ||
+        b < 1)
       b = 1;
     return b;
   }();
   return n;
 }
 
-template <int U, int WPR, int YF>
-hipError_t launch_reg(const LnArgs& a, int num_cus, hipStream_t stream) {
+template <int U, int WPR, int YF, bool PF>
+hipError_t launch_reg_pf(const LnArgs& a, int num_cus, hipStream_t stream) {
   constexpr int kRowsPerBlock = kLnBlock / 64 / WPR;
   const int64_t need = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int64_t slots = (int64_t)num_cus * resident_blocks<U, WPR, YF>();
+  const int64_t slots = (int64_t)num_cus * resident_blocks<U, WPR, YF, PF>();
   const int64_t grid = need < slots ? need : slots;
-  hipLaunchKernelGGL((ln_rows_bf16<U, WPR, YF>), dim3((unsigned)grid), dim3(kLnBlock), 0, stream,
+  hipLaunchKernelGGL((ln_rows_bf16<U, WPR, YF, PF>), dim3((unsigned)grid), dim3(kLnBlock), 0, stream,
                      static_cast<const uint16_t*>(a.x), a.rows, a.cols, a.ld_x, a.gamma, a.beta, a.eps, a.y, a.ld_y,
                      a.scale, a.q, a.ld_q, a.amax, a.mean, a.rstd);
   return hipGetLastError();
+}
+
+// Row prefetch where it measured faster (6-10%): four waves per row with codes,
+// at 6145-8192 columns (four chunks per thread, nearly all used) and, beyond
+// 8192, when both y and the codes are written. Elsewhere its registers cost
+// more occupancy than the extra bytes in flight win (up to 7% slower at
+// 5120-6144 columns).
+template <int U, int WPR, int YF>
+hipError_t launch_reg(const LnArgs& a, int num_cus, hipStream_t stream) {
+  if constexpr (WPR == 4 && YF != kNoQ && (U == 4 || U == 8)) {
+    const bool pf = U == 4 ? a.cols > 6144 : (a.y != nullptr && a.q != nullptr);
+    if (pf) return launch_reg_pf<U, WPR, YF, true>(a, num_cus, stream);
+  }
+  return launch_reg_pf<U, WPR, YF, false>(a, num_cus, stream);
 }
 
 // Chunks per thread and waves per row, measured per width: rows up to 2048

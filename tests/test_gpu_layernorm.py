@@ -90,7 +90,7 @@ def test_layernorm_shapes(fmt, shape):
         _check(x, g, beta, eps, fmt, s, *res)
 
 
-@pytest.mark.parametrize("cols", [2056, 3072, 4096, 4104, 6144, 8192])
+@pytest.mark.parametrize("cols", [2056, 3072, 4096, 4104, 6144, 8192, 16384])
 def test_layernorm_output_modes_agree(cols):
     """BF16 only, codes only and both: each width and mode picks its own launch shape; y is the same
     bits in every mode and matches the oracle, the codes and amax are the oracle's cast of that y."""
