@@ -254,3 +254,57 @@ def test_batched_cast_equals_separate_calls():
             assert np.array_equal(host(q), want), (k, first_diff(host(q), want))
         if am is not None:
             assert f32_bits(am)[0] == np.float32(oracle.amax(src, dtype)).view(np.uint32), k
+
+
+def test_beyond_two_to_the_31_elements():
+    """A 32769 x 65537 BF16 tensor (2^31 + 98305 elements): 64-bit indexing in the flat, batched and
+    cast-transpose paths. A repeating pattern of small values with one larger value planted past
+    element 2^31 gives the amax exactly; codes are compared with the oracle around the 2^31 boundary,
+    at both ends and at random positions, and q^T with q at sampled positions."""
+    require_gpu()
+    rows, cols = 32769, 65537
+    n = rows * cols
+    assert n > 2 ** 31
+    rng = np.random.default_rng(31)
+    pattern = wl.f32_to_bf16_bits((rng.standard_normal(4099) * 20).astype(np.float32))
+    reps = -(-n // pattern.size)
+    x = dev(pattern).view(torch.int16).repeat(reps)[:n].contiguous()
+    peak = n - 5
+    x[peak] = int(wl.f32_to_bf16_bits(np.array([1000.0], np.float32))[0].astype(np.int16))
+    x2 = x.view(rows, cols)
+    idx = np.unique(np.concatenate([np.arange(2 ** 31 - 40, 2 ** 31 + 40), np.arange(0, 40), np.arange(n - 40, n),
+                                    rng.integers(0, n, 4000)]))
+    ti = torch.from_numpy(idx).cuda()
+    xs = host(x[ti]).view(np.uint16)
+    s = 4.25
+    want_amax = np.float32(1000.0)
+    for fmt in FORMATS:
+        want = oracle.cast(xs, np.float32(s), fmt, "bf16")
+        banner("cast >2^31 flat", fmt)
+        q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+        am = f32(0.0)
+        fp8.fp8_amax_cast(x2, fmt, f32(s), q, None, am)
+        got = host(q.view(-1)[ti])
+        assert np.array_equal(got, want), first_diff(got, want)
+        assert f32_bits(am)[0] == _amax_bits(want_amax)
+        banner("cast >2^31 batched", fmt)
+        q.fill_(0x5A)
+        am = f32(0.0)
+        fp8.fp8_amax_cast_batched([(x, fmt, f32(s), q.view(-1), am)])
+        got = host(q.view(-1)[ti])
+        assert np.array_equal(got, want), first_diff(got, want)
+        assert f32_bits(am)[0] == _amax_bits(want_amax)
+        del q
+        torch.cuda.empty_cache()
+    banner("cast-transpose >2^31")
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+    am = f32(0.0)
+    fp8.fp8_amax_cast(x2, "e4m3", f32(s), q, qt, am)
+    r, c = idx // cols, idx % cols
+    got_q = host(q.view(-1)[ti])
+    got_qt = host(qt[torch.from_numpy(c).cuda(), torch.from_numpy(r).cuda()])
+    want = oracle.cast(xs, np.float32(s), "e4m3", "bf16")
+    assert np.array_equal(got_q, want), first_diff(got_q, want)
+    assert np.array_equal(got_qt, want), first_diff(got_qt, want)
+    assert f32_bits(am)[0] == _amax_bits(want_amax)

@@ -110,3 +110,29 @@ def test_gemm_rejects_unsupported_k():
     with pytest.raises(fp8.Fp8mpError) as ei:
         fp8.fp8_scaled_gemm(a, "e4m3", a, "e4m3", f32(1.0), f32(1.0), c)
     assert ei.value.status == 2
+
+
+def test_gemm_output_beyond_two_to_the_31_elements():
+    """C of 65536 x 32800 (2^31 + 2^21 elements, ragged in N): 64-bit addressing in the epilogue.
+    Rows and columns on both sides of the 2^31-th element, the edges and random entries are compared
+    with the oracle's entries."""
+    require_gpu()
+    m, n, k = 65536, 32800, 32
+    assert m * n > 2 ** 31
+    rng = np.random.default_rng(2031)
+    a = _codes(rng, (m, k), "e4m3", spread=40)
+    b = _codes(rng, (n, k), "e4m3", spread=40)
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    c = torch.empty(m, n, dtype=torch.int16, device="cuda")
+    banner("gemm >2^31 outputs")
+    fp8.fp8_scaled_gemm(dev(a), "e4m3", dev(b), "e4m3", f32(sa), f32(sb), c)
+    flat = np.concatenate([np.arange(2 ** 31 - 64, 2 ** 31 + 64), rng.integers(0, m * n, 3000),
+                           np.arange(m * n - 64, m * n), np.arange(0, 64)])
+    rows, cols = flat // n, flat % n
+    got = host(c.view(-1)[torch.from_numpy(flat).cuda()]).view(np.uint16)
+    ref = np.empty(flat.size)
+    absr = np.empty(flat.size)
+    for t, (i, j) in enumerate(zip(rows, cols)):
+        ref[t], absr[t] = oracle.gemm_entry(a, "e4m3", b, "e4m3", sa, sb, i, j)
+    ok, worst = oracle.gemm_check(got, ref, absr)
+    assert ok, f"worst |err|/bound = {worst}"
