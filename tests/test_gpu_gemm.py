@@ -136,3 +136,26 @@ def test_gemm_output_beyond_two_to_the_31_elements():
         ref[t], absr[t] = oracle.gemm_entry(a, "e4m3", b, "e4m3", sa, sb, i, j)
     ok, worst = oracle.gemm_check(got, ref, absr)
     assert ok, f"worst |err|/bound = {worst}"
+
+
+def test_gemm_at_the_largest_leading_dimension():
+    """lda = ldb = 4 MiB, the largest supported: a tile's rows then span almost 2^30 bytes of the
+    buffer resource. One byte more is refused as unsupported."""
+    require_gpu()
+    m, n, k = 300, 290, 48
+    ld = 1 << 22
+    rng = np.random.default_rng(22)
+    a = _codes(rng, (m, k), "e4m3", spread=40)
+    b = _codes(rng, (n, k), "e5m2", spread=40)
+    sa, sb = np.float32(0.75), np.float32(2.0)
+    a_store = torch.zeros(m, ld, dtype=torch.uint8, device="cuda")
+    b_store = torch.zeros(n, ld, dtype=torch.uint8, device="cuda")
+    a_store[:, :k] = dev(a)
+    b_store[:, :k] = dev(b)
+    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    banner("gemm max ld")
+    fp8.fp8_scaled_gemm(a_store[:, :k], "e4m3", b_store[:, :k], "e5m2", f32(sa), f32(sb), c)
+    _check(a, "e4m3", b, "e5m2", sa, sb, host(c), "max ld")
+    wide = torch.zeros(2, ld + 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fp8.Fp8mpError):
+        fp8.fp8_scaled_gemm(wide[:, :k], "e4m3", b_store[:2, :k], "e5m2", f32(sa), f32(sb), c[:2, :2])
