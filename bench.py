@@ -40,8 +40,9 @@ def parse():
     ap.add_argument("--workload", default="mlp7b_up_fwd")
     ap.add_argument("--recipe", default="delayed", choices=["delayed", "current"],
                     help="delayed scaling (the pages' default recipe) or just-in-time scaling")
-    ap.add_argument("--output-cast", default="none", choices=["none", "fused", "separate"],
-                    help="also cast the GEMM output to E4M3 for a next layer: in the GEMM epilogue or as a second pass")
+    ap.add_argument("--output-cast", default="none", choices=["none", "fused", "fused_codes", "separate"],
+                    help="also cast the GEMM output to E4M3 for a next layer: in the GEMM epilogue (fused_codes: "
+                         "without storing the BF16 output) or as a second pass")
     ap.add_argument("--layernorm", action="store_true",
                     help="X is LayerNorm(X) (gamma ~ N(1, 0.2), beta ~ N(0, 0.2), eps 1e-5), normalised and cast in one pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -20,7 +20,9 @@ With ``output_cast`` the GEMM outputs are also cast to E4M3 for a following
 layer ([TE] §基本的なFP8トレーニングコードの構成 chains te.Linear layers), under the
 same delayed recipe with a state of their own: "fused" does it in the GEMM's
 epilogue (fp8_scaled_gemm_amax_cast), "separate" with a second pass over the
-BF16 output (fp8_amax_cast), the unfused reference.
+BF16 output (fp8_amax_cast), the unfused reference. "fused_codes" is "fused"
+without storing the BF16 output, for a following layer that reads the codes
+only.
 
 The plan owns its device buffers (allocated once, through torch); a step
 allocates nothing and never synchronises.
@@ -58,14 +60,14 @@ class GemmOp:
 
 class LayerPlan:
     """recipe "delayed" (the default) or "current" (just-in-time scaling: amax pass, update, cast);
-    output_cast None, "fused" or "separate" (delayed recipe only)."""
+    output_cast None, "fused", "fused_codes" (no BF16 output stored) or "separate" (delayed recipe only)."""
 
     def __init__(self, operands: Sequence[OperandSpec], gemms: Sequence[GemmOp], history_len: int = 1024,
                  margin: int = 0, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None,
                  ln_params: Optional[Dict[str, tuple]] = None):
         if recipe not in ("delayed", "current"):
             raise ValueError(recipe)
-        if output_cast not in (None, "fused", "separate"):
+        if output_cast not in (None, "fused", "fused_codes", "separate"):
             raise ValueError(output_cast)
         if output_cast and recipe != "delayed":
             raise ValueError("the output cast follows the delayed recipe (its amax is taken while casting)")
@@ -137,7 +139,8 @@ class LayerPlan:
                     st.cast(inputs[name], self.q[name], self.qt[name], False, stream)
             for g, (a, af, b, bf, sa, sb, c) in zip(self.gemms, self._gemm_args):
                 ys = self.ystate[g.name]
-                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c, ys.fmt, None, None, ys.amax_slot, stream)
+                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c if self.output_cast != "fused_codes" else None,
+                                          ys.fmt, None, None, ys.amax_slot, stream)
             for ys in self.ystate.values():
                 ys.update(stream)
 
@@ -170,10 +173,10 @@ class LayerPlan:
 
     def gemm_all(self, stream=None) -> None:
         for g, (a, af, b, bf, sa, sb, c) in zip(self.gemms, self._gemm_args):
-            if self.output_cast == "fused":
+            if self.output_cast in ("fused", "fused_codes"):
                 ys = self.ystate[g.name]
-                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c, ys.fmt, ys.scale, self.yq[g.name], ys.amax_slot,
-                                          stream)
+                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c if self.output_cast == "fused" else None, ys.fmt,
+                                          ys.scale, self.yq[g.name], ys.amax_slot, stream)
             else:
                 fp8_scaled_gemm(a, af, b, bf, sa, sb, c, stream)
 
@@ -214,7 +217,8 @@ class LayerPlan:
 
     def output_cast_bytes(self) -> int:
         """Algorithmic bytes of the output casts beyond the BF16 outputs themselves: the codes
-        written, plus (separate only) a second read of each output."""
+        written, plus (separate only) a second read of each output. With "fused_codes" the GEMM
+        writes the codes instead of the BF16 output."""
         total = 0
         for c in self.out.values() if self.output_cast else ():
             total += c.numel() * (1 + (2 if self.output_cast == "separate" else 0))

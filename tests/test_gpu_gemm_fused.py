@@ -133,8 +133,9 @@ def test_fused_full_size_mlp_shape():
 
 
 def test_layer_plan_output_cast_fused_equals_separate():
-    """A chained layer step: the fused output cast and the separate second pass give the same codes,
-    histories and scales, and the codes are the oracle's cast of the BF16 output with the delayed scale."""
+    """A chained layer step: the fused output cast, the separate second pass and the fused cast without
+    the BF16 output give the same codes, histories and scales, and the codes are the oracle's cast of
+    the BF16 output with the delayed scale."""
     require_gpu()
     from fp8_mixed_precision_cast_amd.linear import GemmOp, LayerPlan, OperandSpec
     import workloads as wl
@@ -143,7 +144,9 @@ def test_layer_plan_output_cast_fused_equals_separate():
     inp = {"X": dev(x), "W": dev(w)}
     ops = [OperandSpec("X", (300, 256), "e4m3"), OperandSpec("W", (520, 256), "e4m3")]
     gem = [GemmOp("fwd", "X", False, "W", False)]
-    plans = {mode: LayerPlan(ops, gem, history_len=8, output_cast=mode) for mode in ("fused", "separate")}
+    plans = {mode: LayerPlan(ops, gem, history_len=8, output_cast=mode) for mode in ("fused", "separate",
+                                                                                     "fused_codes")}
+    plans["fused_codes"].out["fwd"].view(torch.int16).fill_(0x1234)   # never stored in that mode
     for mode, plan in plans.items():
         banner("plan-output-cast", mode)
         plan.prime(inp)
@@ -153,16 +156,21 @@ def test_layer_plan_output_cast_fused_equals_separate():
             s_before = host(ys.scale)[0]
             banner("plan-output-cast", mode, step)
             plan.step(inp)
+            if mode == "fused_codes":
+                assert (host(plan.out["fwd"].view(torch.int16)) == 0x1234).all(), "BF16 output stored"
+                continue
             cb = host(plan.out["fwd"].view(torch.int16))
             want = oracle.cast(cb, s_before, "e4m3", "bf16")
             got = host(plan.yq["fwd"])
             assert np.array_equal(got, want), (mode, step, first_diff(got, want))
-        f, s = plans["fused"], plans["separate"]
-        assert np.array_equal(host(f.yq["fwd"]), host(s.yq["fwd"]))
-        for attr in ("history", "scale", "scale_inv"):
-            a = host(getattr(f.ystate["fwd"], attr)).view(np.uint32)
-            b = host(getattr(s.ystate["fwd"], attr)).view(np.uint32)
-            assert np.array_equal(a, b), attr
+        f = plans["fused"]
+        for other in ("separate", "fused_codes"):
+            s = plans[other]
+            assert np.array_equal(host(f.yq["fwd"]), host(s.yq["fwd"])), other
+            for attr in ("history", "scale", "scale_inv"):
+                a = host(getattr(f.ystate["fwd"], attr)).view(np.uint32)
+                b = host(getattr(s.ystate["fwd"], attr)).view(np.uint32)
+                assert np.array_equal(a, b), (other, attr)
 
 
 def test_fused_without_bf16_output():
