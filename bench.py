@@ -45,6 +45,9 @@ def parse():
                          "without storing the BF16 output) or as a second pass")
     ap.add_argument("--layernorm", action="store_true",
                     help="X is LayerNorm(X) (gamma ~ N(1, 0.2), beta ~ N(0, 0.2), eps 1e-5), normalised and cast in one pass")
+    ap.add_argument("--gemm-accum", default="exact", choices=["exact", "fast"],
+                    help="exact: FP32 accumulation (BF16 MFMA on exactly widened FP8); fast: the FP8 MFMA's own "
+                         "reduced-precision accumulation (within 2^-9 of sum|a*b|)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
@@ -52,7 +55,8 @@ def parse():
                     help="only run a plain device copy of BYTES three times (calibrates HBM counters) and "
                          "report its rate")
     ap.add_argument("--gemm-data", default="", metavar="MxNxK",
-                    help="only time fp8_scaled_gemm at this shape on E4M3 operands of several kinds "
+                    help="only time fp8_scaled_gemm (and its fast-accumulation form) at this shape on E4M3 "
+                         "operands of several kinds "
                          "(all zero, all 1.0, uniform random codes, cast N(0,1) values): one JSON line per kind")
     return ap.parse_args()
 
@@ -110,18 +114,19 @@ def gemm_data(shape: str, iters: int = 20) -> None:
 
     for kind in ("zero", "one", "uniform", "normal"):
         a, b = codes(kind, m), codes(kind, n)
-        for _ in range(5):
-            fp8.fp8_scaled_gemm(a, "e4m3", b, "e4m3", one, one, c)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fp8.fp8_scaled_gemm(a, "e4m3", b, "e4m3", one, one, c)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / iters
-        print(json.dumps({"gemm_data": kind, "shape": [m, n, k], "us": round(ms * 1e3, 1),
-                          "tflops": round(2 * m * n * k / ms / 1e9, 1)}), flush=True)
+        for accum, call in (("exact", fp8.fp8_scaled_gemm), ("fast", fp8.fp8_scaled_gemm_fast_accum)):
+            for _ in range(5):
+                call(a, "e4m3", b, "e4m3", one, one, c)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                call(a, "e4m3", b, "e4m3", one, one, c)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            print(json.dumps({"gemm_data": kind, "accum": accum, "shape": [m, n, k], "us": round(ms * 1e3, 1),
+                              "tflops": round(2 * m * n * k / ms / 1e9, 1)}), flush=True)
         del a, b
     # Context: the vendor library through torch at the same shape on N(0,1) data, BF16 x BF16 (the
     # same MFMA path as ours) and FP8 x FP8 (the FP8 MFMA, whose accumulation is coarser than the
@@ -203,6 +208,27 @@ def cold_cast_gbps(plan, dinp, reps: int = 5):
     return plan.cast_bytes(dinp) / (ms * 1e-3) / 1e9, ms
 
 
+def other_gemm_tflops(plan, accum: str, iters: int = 20) -> float:
+    """The plan's GEMMs, on the codes of the last step, in the other accumulation mode: TFLOP/s per
+    launch from HIP events around iters rounds (outside the timed steps)."""
+    import torch
+    import fp8_mixed_precision_cast_amd as fp8
+    call = fp8.fp8_scaled_gemm_fast_accum if accum == "fast" else fp8.fp8_scaled_gemm
+    stream = torch.cuda.current_stream()
+    outs = [torch.empty_like(c) for (_, _, _, _, _, _, c) in plan._gemm_args]
+    for _ in range(3):
+        for (a, af, b, bf, sa, sb, _), c in zip(plan._gemm_args, outs):
+            call(a, af, b, bf, sa, sb, c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        for (a, af, b, bf, sa, sb, _), c in zip(plan._gemm_args, outs):
+            call(a, af, b, bf, sa, sb, c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return plan.gemm_flops() * iters / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def main():
     args = parse()
     if args.copy_reference:
@@ -236,7 +262,8 @@ def main():
                            torch.from_numpy(rng.normal(0.0, 0.2, cols).astype(np.float32)).cuda(), 1e-5)}
     plan = plan_from_workload(w, recipe=args.recipe,
                               output_cast=None if args.output_cast == "none" else args.output_cast,
-                              layernorm=("X",) if args.layernorm else (), ln_params=ln_params)
+                              layernorm=("X",) if args.layernorm else (), ln_params=ln_params,
+                              gemm_accum=args.gemm_accum)
     stream = torch.cuda.current_stream()
     plan.prime(dinp)
     for _ in range(args.warmup):
@@ -276,13 +303,17 @@ def main():
     cast_gbps = cast_bytes / (cast_ms * 1e-3) / 1e9
 
     cold_gbps, cold_ms = cold_cast_gbps(plan, dinp)
+    other = "fast" if args.gemm_accum == "exact" else "exact"
+    other_tflops = other_gemm_tflops(plan, other)
 
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
-            t = json.load(f).get(w.name, {})
+            t = json.load(f).get(w.name if args.gemm_accum == "exact" else w.name + ":fast", {})
         if t.get("gemm_source") == source_digest():
             traffic = t.get("gemm_bytes_per_launch")
+    fast = args.gemm_accum == "fast"
+    peak = PEAK_FP8_MFMA_TFLOPS if fast else PEAK_BF16_MFMA_TFLOPS
 
     g = w.gemms[0]
 
@@ -302,17 +333,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 operands; bf16 MFMA (exact on FP8 values), f32 accumulate, bf16 out",
+        "dtype": ("fp8-e4m3 operands; fp8 MFMA (fast accumulation, within 2^-9 of sum|ab|), bf16 out" if fast else
+                  "fp8-e4m3 operands; bf16 MFMA (exact on FP8 values), f32 accumulate, bf16 out"),
         "data": "synthetic",
         "config": {"workload": w.name, "m": g.m, "n": g.n, "k": g.k,
                    "gemms": ["{} {}x{}x{} {}x{}".format(x.name, x.m, x.n, x.k, x.a_fmt, x.b_fmt) for x in w.gemms],
                    "tensors": {t.name: describe(t) for t in w.tensors},
                    "transposed_casts": list(w.transposed), "history_len": w.history_len, "margin": w.margin,
                    "recipe": args.recipe, "output_cast": args.output_cast, "layernorm_x": bool(args.layernorm),
+                   "gemm_accum": args.gemm_accum,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_MFMA_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "gemm_fp8_kernel (bf16 MFMA on widened FP8)",
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
+                     "traffic": traffic,
+                     "kernel": ("gemm_fp8_kernel (fp8 MFMA, fast accumulation)" if fast else
+                                "gemm_fp8_kernel (bf16 MFMA on widened FP8)"),
                      "frac_of_fp8_mfma_peak": round(gemm_tflops / PEAK_FP8_MFMA_TFLOPS, 4)},
         "components": {
             "gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(gemm_tflops, 2),
@@ -320,6 +355,9 @@ def main():
             "cast_frac_of_hbm": round(cast_gbps / PEAK_HBM_GBPS, 4),
             "scale_update_ms": round(upd_ms, 4),
             "cast_cold_ms": round(cold_ms, 4), "cast_cold_gbps": round(cold_gbps, 1),
+            f"gemm_{other}_accum_tflops": round(other_tflops, 2),
+            f"gemm_{other}_accum_frac_of_peak": round(other_tflops / (PEAK_FP8_MFMA_TFLOPS if other == "fast"
+                                                                      else PEAK_BF16_MFMA_TFLOPS), 4),
         },
         "device": info,
     }

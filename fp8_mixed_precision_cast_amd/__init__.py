@@ -23,7 +23,7 @@ from typing import Optional
 
 __all__ = [
     "E4M3", "E5M2", "F32", "BF16", "Fp8mpError", "lib_path", "load_library",
-    "fp8_amax_cast", "fp8_amax_cast_batched", "CastBatch", "fp8_scale_update", "fp8_scale_update_batched", "ScaleUpdateBatch", "fp8_scaled_gemm", "fp8_scaled_gemm_amax_cast", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step", "AdamFP8State",
+    "fp8_amax_cast", "fp8_amax_cast_batched", "CastBatch", "fp8_scale_update", "fp8_scale_update_batched", "ScaleUpdateBatch", "fp8_scaled_gemm", "fp8_scaled_gemm_fast_accum", "fp8_scaled_gemm_amax_cast", "fp8_scaled_gemm_amax_cast_fast_accum", "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step", "AdamFP8State",
     "fp8mp_status_string",
     "fp8mp_device_info", "exported_symbols", "DelayedScalingState", "CurrentScalingState",
 ]
@@ -65,12 +65,15 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_scale_update.restype = ctypes.c_int
     lib.fp8_scale_update_batched.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp]
     lib.fp8_scale_update_batched.restype = ctypes.c_int
-    lib.fp8_scaled_gemm.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp,
-                                    i64, vp]
-    lib.fp8_scaled_gemm.restype = ctypes.c_int
-    lib.fp8_scaled_gemm_amax_cast.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp,
-                                              vp, i64, ctypes.c_int, vp, vp, i64, vp, vp]
-    lib.fp8_scaled_gemm_amax_cast.restype = ctypes.c_int
+    for name in ("fp8_scaled_gemm", "fp8_scaled_gemm_fast_accum"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, i64, vp]
+        fn.restype = ctypes.c_int
+    for name in ("fp8_scaled_gemm_amax_cast", "fp8_scaled_gemm_amax_cast_fast_accum"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, i64, ctypes.c_int,
+                       vp, vp, i64, vp, vp]
+        fn.restype = ctypes.c_int
     lib.fp8_layernorm_amax_cast.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, ctypes.c_float, vp, i64,
                                             ctypes.c_int, vp, vp, i64, vp, vp, vp, vp]
     lib.fp8_layernorm_amax_cast.restype = ctypes.c_int
@@ -219,8 +222,7 @@ def fp8_scale_update_batched(batch, stream=None) -> None:
     _check(st, "fp8_scale_update_batched")
 
 
-def fp8_scaled_gemm(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None) -> None:
-    """c = (a . b^T) * a_scale_inv * b_scale_inv; a[m,k], b[n,k] uint8 codes; c[m,n] BF16."""
+def _gemm(call, a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream) -> None:
     m, k, lda = _rows_ld(a, "a")
     n, kb, ldb = _rows_ld(b, "b")
     if kb != k:
@@ -228,15 +230,23 @@ def fp8_scaled_gemm(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None
     mc, nc, ldc = _rows_ld(c, "c")
     if (mc, nc) != (m, n):
         raise ValueError("c must be m x n")
-    st = load_library().fp8_scaled_gemm(_ptr(a), FORMATS[a_fmt], lda, _ptr(b), FORMATS[b_fmt], ldb, m, n, k,
-                                        _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(c), ldc, _stream(stream))
-    _check(st, "fp8_scaled_gemm")
+    st = getattr(load_library(), call)(_ptr(a), FORMATS[a_fmt], lda, _ptr(b), FORMATS[b_fmt], ldb, m, n, k,
+                                       _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(c), ldc, _stream(stream))
+    _check(st, call)
 
 
-def fp8_scaled_gemm_amax_cast(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt, y_scale=None, y_q=None,
-                              y_amax=None, stream=None) -> None:
-    """fp8_scaled_gemm, and in the same kernel y_amax = max(y_amax, max|c|), y_q = enc(c * y_scale);
-    c may be None when y_q or y_amax is given (the BF16 output is then not stored)."""
+def fp8_scaled_gemm(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None) -> None:
+    """c = (a . b^T) * a_scale_inv * b_scale_inv; a[m,k], b[n,k] uint8 codes; c[m,n] BF16; FP32 accumulation."""
+    _gemm("fp8_scaled_gemm", a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream)
+
+
+def fp8_scaled_gemm_fast_accum(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream=None) -> None:
+    """fp8_scaled_gemm on the FP8 MFMA's reduced-precision accumulation (within 2^-9 of sum|a*b|)."""
+    _gemm("fp8_scaled_gemm_fast_accum", a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, stream)
+
+
+def _gemm_amax_cast(call, a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt, y_scale, y_q, y_amax,
+                    stream) -> None:
     m, k, lda = _rows_ld(a, "a")
     n, kb, ldb = _rows_ld(b, "b")
     if kb != k:
@@ -251,10 +261,25 @@ def fp8_scaled_gemm_amax_cast(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y
         mq, nq, ld_yq = _rows_ld(y_q, "y_q")
         if (mq, nq) != (m, n):
             raise ValueError("y_q must be m x n")
-    st = load_library().fp8_scaled_gemm_amax_cast(
+    st = getattr(load_library(), call)(
         _ptr(a), FORMATS[a_fmt], lda, _ptr(b), FORMATS[b_fmt], ldb, m, n, k, _ptr(a_scale_inv), _ptr(b_scale_inv),
         _ptr(c), ldc, FORMATS[y_fmt], _ptr(y_scale), _ptr(y_q), ld_yq, _ptr(y_amax), _stream(stream))
-    _check(st, "fp8_scaled_gemm_amax_cast")
+    _check(st, call)
+
+
+def fp8_scaled_gemm_amax_cast(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt, y_scale=None, y_q=None,
+                              y_amax=None, stream=None) -> None:
+    """fp8_scaled_gemm, and in the same kernel y_amax = max(y_amax, max|c|), y_q = enc(c * y_scale);
+    c may be None when y_q or y_amax is given (the BF16 output is then not stored)."""
+    _gemm_amax_cast("fp8_scaled_gemm_amax_cast", a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt, y_scale,
+                    y_q, y_amax, stream)
+
+
+def fp8_scaled_gemm_amax_cast_fast_accum(a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt, y_scale=None,
+                                         y_q=None, y_amax=None, stream=None) -> None:
+    """fp8_scaled_gemm_amax_cast on the FP8 MFMA's reduced-precision accumulation."""
+    _gemm_amax_cast("fp8_scaled_gemm_amax_cast_fast_accum", a, a_fmt, b, b_fmt, a_scale_inv, b_scale_inv, c, y_fmt,
+                    y_scale, y_q, y_amax, stream)
 
 
 def fp8_layernorm_amax_cast(x, gamma, beta, eps, fmt, y=None, scale=None, q=None, amax=None, mean=None, rstd=None,

@@ -208,24 +208,27 @@ fp8mp_status fp8_scale_update_batched(int32_t n_tensors, float* const* amax_hist
   return FP8MP_OK;
 }
 
-fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
-                             fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
-                             const float* a_scale_inv, const float* b_scale_inv, uint16_t* c, int64_t ldc,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fp8mp_status scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b, fp8mp_format b_fmt,
+                         int64_t ldb, int64_t m, int64_t n, int64_t k, const float* a_scale_inv,
+                         const float* b_scale_inv, uint16_t* c, int64_t ldc, bool fast_accum, hipStream_t stream) {
   fp8mp_status st = check_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc);
   if (st != FP8MP_OK || m == 0 || n == 0) return st;
   int cus = 0;
   st = check_device(&cus);
   if (st != FP8MP_OK) return st;
   return from_hip(fp8mp::launch_scaled_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv,
-                                            c, ldc, cus, stream));
+                                            c, ldc, fast_accum, cus, stream));
 }
 
-fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
-                                       fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
-                                       const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
-                                       int64_t ldc, fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
-                                       int64_t ld_yq, float* y_amax, hipStream_t stream) {
+fp8mp_status scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
+                                   fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                                   const float* a_scale_inv, const float* b_scale_inv, uint16_t* c, int64_t ldc,
+                                   fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q, int64_t ld_yq,
+                                   float* y_amax, bool fast_accum, hipStream_t stream) {
   fp8mp_status st = check_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc,
                                /*c_optional=*/y_q != nullptr || y_amax != nullptr);
   if (st != FP8MP_OK) return st;
@@ -240,7 +243,44 @@ fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int
   if (st != FP8MP_OK) return st;
   return from_hip(fp8mp::launch_scaled_gemm_amax_cast(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv,
                                                       b_scale_inv, c, ldc, y_fmt, y_scale, y_q, ld_yq, y_amax,
-                                                      cus, stream));
+                                                      fast_accum, cus, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
+                             fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                             const float* a_scale_inv, const float* b_scale_inv, uint16_t* c, int64_t ldc,
+                             hipStream_t stream) {
+  return scaled_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, false, stream);
+}
+
+fp8mp_status fp8_scaled_gemm_fast_accum(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
+                                        fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                                        const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
+                                        int64_t ldc, hipStream_t stream) {
+  return scaled_gemm(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, true, stream);
+}
+
+fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
+                                       fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                                       const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
+                                       int64_t ldc, fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
+                                       int64_t ld_yq, float* y_amax, hipStream_t stream) {
+  return scaled_gemm_amax_cast(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, y_fmt,
+                               y_scale, y_q, ld_yq, y_amax, false, stream);
+}
+
+fp8mp_status fp8_scaled_gemm_amax_cast_fast_accum(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
+                                                  const uint8_t* b, fp8mp_format b_fmt, int64_t ldb, int64_t m,
+                                                  int64_t n, int64_t k, const float* a_scale_inv,
+                                                  const float* b_scale_inv, uint16_t* c, int64_t ldc,
+                                                  fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
+                                                  int64_t ld_yq, float* y_amax, hipStream_t stream) {
+  return scaled_gemm_amax_cast(a, a_fmt, lda, b, b_fmt, ldb, m, n, k, a_scale_inv, b_scale_inv, c, ldc, y_fmt,
+                               y_scale, y_q, ld_yq, y_amax, true, stream);
 }
 
 fp8mp_status fp8_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,

@@ -205,12 +205,13 @@ hipError_t launch_scale_update_batched(const ScaleUpdateBatch& batch, int n, hip
 hipError_t launch_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
                               fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
                               const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
-                              int64_t ldc, int num_cus, hipStream_t stream);
+                              int64_t ldc, bool fast_accum, int num_cus, hipStream_t stream);
 hipError_t launch_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const uint8_t* b,
                                         fp8mp_format b_fmt, int64_t ldb, int64_t m, int64_t n, int64_t k,
                                         const float* a_scale_inv, const float* b_scale_inv, uint16_t* c,
                                         int64_t ldc, fp8mp_format y_fmt, const float* y_scale, uint8_t* y_q,
-                                        int64_t ld_yq, float* y_amax, int num_cus, hipStream_t stream);
+                                        int64_t ld_yq, float* y_amax, bool fast_accum, int num_cus,
+                                        hipStream_t stream);
 hipError_t launch_layernorm_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                                       const float* gamma, const float* beta, float eps, uint16_t* y, int64_t ld_y,
                                       fp8mp_format fmt, const float* scale, uint8_t* q, int64_t ld_q, float* amax,

@@ -24,6 +24,10 @@ BF16 output (fp8_amax_cast), the unfused reference. "fused_codes" is "fused"
 without storing the BF16 output, for a following layer that reads the codes
 only.
 
+``gemm_accum`` "exact" (the default) multiplies with FP32 accumulation;
+"fast" uses the FP8 matrix instruction's reduced-precision accumulation
+(fp8_scaled_gemm_fast_accum, within 2**-9 of sum|a*b|) for every GEMM.
+
 The plan owns its device buffers (allocated once, through torch); a step
 allocates nothing and never synchronises.
 """
@@ -36,7 +40,7 @@ import torch
 
 from . import (CastBatch, CurrentScalingState, DelayedScalingState, ScaleUpdateBatch, fp8_amax_cast,
                fp8_amax_cast_batched, fp8_layernorm_amax_cast, fp8_scale_update_batched, fp8_scaled_gemm,
-               fp8_scaled_gemm_amax_cast)
+               fp8_scaled_gemm_amax_cast, fp8_scaled_gemm_amax_cast_fast_accum, fp8_scaled_gemm_fast_accum)
 
 
 @dataclass(frozen=True)
@@ -60,13 +64,20 @@ class GemmOp:
 
 class LayerPlan:
     """recipe "delayed" (the default) or "current" (just-in-time scaling: amax pass, update, cast);
-    output_cast None, "fused", "fused_codes" (no BF16 output stored) or "separate" (delayed recipe only)."""
+    output_cast None, "fused", "fused_codes" (no BF16 output stored) or "separate" (delayed recipe only);
+    gemm_accum "exact" (FP32 accumulation) or "fast" (the FP8 matrix instruction's own accumulation)."""
 
     def __init__(self, operands: Sequence[OperandSpec], gemms: Sequence[GemmOp], history_len: int = 1024,
                  margin: int = 0, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None,
-                 ln_params: Optional[Dict[str, tuple]] = None):
+                 ln_params: Optional[Dict[str, tuple]] = None, gemm_accum: str = "exact"):
         if recipe not in ("delayed", "current"):
             raise ValueError(recipe)
+        if gemm_accum not in ("exact", "fast"):
+            raise ValueError(gemm_accum)
+        self.gemm_accum = gemm_accum
+        fast = gemm_accum == "fast"
+        self._gemm = fp8_scaled_gemm_fast_accum if fast else fp8_scaled_gemm
+        self._gemm_cast = fp8_scaled_gemm_amax_cast_fast_accum if fast else fp8_scaled_gemm_amax_cast
         if output_cast not in (None, "fused", "fused_codes", "separate"):
             raise ValueError(output_cast)
         if output_cast and recipe != "delayed":
@@ -139,8 +150,8 @@ class LayerPlan:
                     st.cast(inputs[name], self.q[name], self.qt[name], False, stream)
             for g, (a, af, b, bf, sa, sb, c) in zip(self.gemms, self._gemm_args):
                 ys = self.ystate[g.name]
-                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c if self.output_cast != "fused_codes" else None,
-                                          ys.fmt, None, None, ys.amax_slot, stream)
+                self._gemm_cast(a, af, b, bf, sa, sb, c if self.output_cast != "fused_codes" else None,
+                                ys.fmt, None, None, ys.amax_slot, stream)
             for ys in self.ystate.values():
                 ys.update(stream)
 
@@ -175,10 +186,10 @@ class LayerPlan:
         for g, (a, af, b, bf, sa, sb, c) in zip(self.gemms, self._gemm_args):
             if self.output_cast in ("fused", "fused_codes"):
                 ys = self.ystate[g.name]
-                fp8_scaled_gemm_amax_cast(a, af, b, bf, sa, sb, c if self.output_cast == "fused" else None, ys.fmt,
-                                          ys.scale, self.yq[g.name], ys.amax_slot, stream)
+                self._gemm_cast(a, af, b, bf, sa, sb, c if self.output_cast == "fused" else None, ys.fmt,
+                                ys.scale, self.yq[g.name], ys.amax_slot, stream)
             else:
-                fp8_scaled_gemm(a, af, b, bf, sa, sb, c, stream)
+                self._gemm(a, af, b, bf, sa, sb, c, stream)
 
     def output_cast_all(self, stream=None) -> None:
         """The unfused output cast (a no-op unless output_cast == "separate")."""
@@ -226,7 +237,8 @@ class LayerPlan:
 
 
 def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed", output_cast: Optional[str] = None,
-                       layernorm: Sequence[str] = (), ln_params: Optional[Dict[str, tuple]] = None) -> LayerPlan:
+                       layernorm: Sequence[str] = (), ln_params: Optional[Dict[str, tuple]] = None,
+                       gemm_accum: str = "exact") -> LayerPlan:
     """A LayerPlan from a workload description with the attributes
     ``tensors`` (``name``, ``shape``), ``formats``, ``transposed``, ``gemms``
     (``name``, ``a``, ``a_transposed``, ``b``, ``b_transposed``), ``history_len``
@@ -234,4 +246,4 @@ def plan_from_workload(w, device: str = "cuda", recipe: str = "delayed", output_
     ops = [OperandSpec(t.name, tuple(t.shape), w.formats[t.name], t.name in w.transposed, True, t.name in layernorm)
            for t in w.tensors]
     gemms = [GemmOp(g.name, g.a, g.a_transposed, g.b, g.b_transposed) for g in w.gemms]
-    return LayerPlan(ops, gemms, w.history_len, w.margin, device, recipe, output_cast, ln_params)
+    return LayerPlan(ops, gemms, w.history_len, w.margin, device, recipe, output_cast, ln_params, gemm_accum)

@@ -179,6 +179,27 @@ fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
                              uint16_t* c, int64_t ldc, hipStream_t stream);
 
 /*
+ * fp8_scaled_gemm_fast_accum: fp8_scaled_gemm with every argument, rule and
+ * error the same, run on gfx950's FP8 matrix instruction
+ * (v_mfma_f32_32x32x64_f8f6f4) instead of exactly widened BF16 operands.
+ *
+ * [TE] §NVIDIA Transformer EngineとFP8混合精度とは: FP8 runs the matrix units at
+ * twice the 16-bit rate. That instruction does not accumulate in FP32: it
+ * aligns its 64 products to the largest and keeps about 16 bits below it
+ * (measured on gfx950: errors up to 2^-10.9 of the largest product per
+ * instruction). The result is therefore guaranteed only within
+ *   |y - y_ref| <= 2^-7 |y_ref| + 2^-9 sum_k |a_k b_k|
+ * (a_k, b_k the dequantised operands), not within the FP32-accumulation bound
+ * of fp8_scaled_gemm. Rows whose products in each 64-wide K block share one
+ * magnitude are summed exactly. Opt-in for callers that accept that error.
+ */
+fp8mp_status fp8_scaled_gemm_fast_accum(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
+                                        const uint8_t* b, fp8mp_format b_fmt, int64_t ldb,
+                                        int64_t m, int64_t n, int64_t k,
+                                        const float* a_scale_inv, const float* b_scale_inv,
+                                        uint16_t* c, int64_t ldc, hipStream_t stream);
+
+/*
  * fp8_scaled_gemm_amax_cast: fp8_scaled_gemm, and in the same kernel the cast
  * of its BF16 output C for the next layer, with exactly the result of
  * fp8_amax_cast(C, FP8MP_BF16, m, n, ldc, y_fmt, y_scale, y_q, ld_yq, NULL, 0,
@@ -209,6 +230,21 @@ fp8mp_status fp8_scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int
                                        fp8mp_format y_fmt, const float* y_scale,
                                        uint8_t* y_q, int64_t ld_yq, float* y_amax,
                                        hipStream_t stream);
+
+/*
+ * fp8_scaled_gemm_amax_cast_fast_accum: fp8_scaled_gemm_amax_cast on the FP8
+ * matrix instruction, with the accumulation and error bound of
+ * fp8_scaled_gemm_fast_accum. The epilogue is unchanged: y_q and y_amax are
+ * exactly fp8_amax_cast of the BF16 output this call produces.
+ */
+fp8mp_status fp8_scaled_gemm_amax_cast_fast_accum(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
+                                                  const uint8_t* b, fp8mp_format b_fmt, int64_t ldb,
+                                                  int64_t m, int64_t n, int64_t k,
+                                                  const float* a_scale_inv, const float* b_scale_inv,
+                                                  uint16_t* c, int64_t ldc,
+                                                  fp8mp_format y_fmt, const float* y_scale,
+                                                  uint8_t* y_q, int64_t ld_yq, float* y_amax,
+                                                  hipStream_t stream);
 
 /*
  * fp8_layernorm_amax_cast: LayerNorm over each row of x, its BF16 output, and

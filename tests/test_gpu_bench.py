@@ -32,6 +32,10 @@ def test_bench_line_contract(monkeypatch, capsys):
     roof = line["roofline"]
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert roof["peak"] == 2500.0 and line["components"]["gemm_fast_accum_tflops"] > 0
+    (fast,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--gemm-accum", "fast")
+    assert fast["config"]["gemm_accum"] == "fast" and fast["roofline"]["peak"] == 5000.0
+    assert fast["components"]["gemm_exact_accum_tflops"] > 0
 
 
 def test_bench_diagnostic_modes(monkeypatch, capsys):
@@ -39,6 +43,7 @@ def test_bench_diagnostic_modes(monkeypatch, capsys):
     lines = _run(monkeypatch, capsys, "--gemm-data", "512x768x256")
     kinds = {l.get("gemm_data") for l in lines if "gemm_data" in l}
     assert kinds == {"zero", "one", "uniform", "normal"}
+    assert {l.get("accum") for l in lines if "gemm_data" in l} == {"exact", "fast"}
     assert all(l["tflops"] > 0 for l in lines if "gemm_data" in l)
     (copy,) = _run(monkeypatch, capsys, "--copy-reference", str(1 << 24))
     assert copy["copy_reference_bytes"] == 1 << 24 and copy["copy_gbps"] > 0

@@ -1,0 +1,170 @@
+"""GPU parity of the fast-accumulation GEMM (FP8 matrix instruction) against the oracle.
+
+fp8_scaled_gemm_fast_accum is graded with the fast-accumulation bound
+|y - y_ref| <= 2**-7 |y_ref| + 2**-9 * sum_k |a_k b_k| on full-range codes and
+ragged shapes. Where every product of a 64-wide K block has one magnitude the
+instruction sums exactly, so there the fast GEMM must give the FP32 GEMM's
+bits: this pins the operand pairing, the K blocking and the zero fill of a
+ragged K independently of the looser bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.codec import FMT
+from oracle.gemm import FAST_ACCUM_SUM_COEF
+from tests.gpu_util import banner, dev, f32, first_diff, host, require_gpu
+
+import fp8_mixed_precision_cast_amd as fp8
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")]
+SHAPES = [(128, 128, 128), (256, 256, 256), (300, 200, 272), (257, 129, 16), (1, 1, 16), (17, 300, 48),
+          (640, 384, 1024), (129, 257, 4096 + 16)]
+
+
+def _codes(rng, shape, fmt):
+    top = FMT[fmt].max_code
+    c = rng.integers(0, top + 1, shape, dtype=np.int64)
+    sign = rng.integers(0, 2, shape, dtype=np.int64) << 7
+    return (c | sign).astype(np.uint8)
+
+
+def _pow2_rows(rng, shape, fmt):
+    """+-2**e codes with one exponent per row (zero mantissa), random signs."""
+    f = FMT[fmt]
+    rows = shape[0]
+    e = rng.integers(1, (1 << f.exp_bits) - 1, rows, dtype=np.int64)
+    c = np.repeat((e << f.man_bits)[:, None], shape[1], axis=1)
+    sign = rng.integers(0, 2, shape, dtype=np.int64) << 7
+    return (c | sign).astype(np.uint8)
+
+
+def _gemm(call, a, af, b, bf, sa, sb):
+    m, n = a.shape[0], b.shape[0]
+    c_store = torch.zeros(m, n + 8, dtype=torch.int16, device="cuda")
+    call(dev(a), af, dev(b), bf, f32(sa), f32(sb), c_store[:, :n])
+    out = host(c_store)
+    assert not out[:, n:].any(), "wrote past n"
+    return out[:, :n]
+
+
+@pytest.mark.parametrize("af,bf", PAIRS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fast_gemm_within_fast_bound(af, bf, shape):
+    require_gpu()
+    m, n, k = shape
+    rng = np.random.default_rng(m * 13 + n * 5 + k)
+    a, b = _codes(rng, (m, k), af), _codes(rng, (n, k), bf)
+    sa, sb = np.float32(1 / 3.0), np.float32(0.0625)
+    banner("gemm-fast", af, bf, shape)
+    y = _gemm(fp8.fp8_scaled_gemm_fast_accum, a, af, b, bf, sa, sb)
+    ref = oracle.gemm_ref(a, af, b, bf, sa, sb)
+    absr = oracle.gemm_abs_ref(a, af, b, bf, sa, sb)
+    ok, worst = oracle.gemm_check(y, ref, absr, FAST_ACCUM_SUM_COEF)
+    assert ok, f"worst |err|/bound = {worst}"
+
+
+@pytest.mark.parametrize("af,bf", PAIRS)
+@pytest.mark.parametrize("shape", [(300, 200, 272), (257, 129, 16), (17, 300, 48), (129, 257, 4096 + 16)])
+def test_fast_gemm_exact_when_products_share_a_magnitude(af, bf, shape):
+    require_gpu()
+    m, n, k = shape
+    rng = np.random.default_rng(m + n * 3 + k * 7)
+    a, b = _pow2_rows(rng, (m, k), af), _pow2_rows(rng, (n, k), bf)
+    sa, sb = np.float32(0.75), np.float32(2.0 ** -3)
+    banner("gemm-fast-exact", af, bf, shape)
+    y_fast = _gemm(fp8.fp8_scaled_gemm_fast_accum, a, af, b, bf, sa, sb)
+    y_exact = _gemm(fp8.fp8_scaled_gemm, a, af, b, bf, sa, sb)
+    assert np.array_equal(y_fast, y_exact), first_diff(y_fast, y_exact)
+    ref = oracle.gemm_ref(a, af, b, bf, sa, sb)
+    absr = oracle.gemm_abs_ref(a, af, b, bf, sa, sb)
+    ok, worst = oracle.gemm_check(y_fast, ref, absr)
+    assert ok, f"worst |err|/bound (FP32 bound) = {worst}"
+
+
+def test_fast_gemm_strided_and_degenerate():
+    require_gpu()
+    rng = np.random.default_rng(15)
+    m, n, k = 192, 160, 512
+    a_full = _codes(rng, (m, k + 64), "e5m2")
+    b_full = _codes(rng, (n, k + 32), "e4m3")
+    ad, bd = dev(a_full)[:, 16:16 + k], dev(b_full)[:, 32:32 + k]
+    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    banner("gemm-fast-strided")
+    fp8.fp8_scaled_gemm_fast_accum(ad, "e5m2", bd, "e4m3", f32(2.0 ** -10), f32(3.0), c)
+    a, b = a_full[:, 16:16 + k], b_full[:, 32:32 + k]
+    ref = oracle.gemm_ref(a, "e5m2", b, "e4m3", 2.0 ** -10, 3.0)
+    absr = oracle.gemm_abs_ref(a, "e5m2", b, "e4m3", 2.0 ** -10, 3.0)
+    ok, worst = oracle.gemm_check(host(c), ref, absr, FAST_ACCUM_SUM_COEF)
+    assert ok, f"worst |err|/bound = {worst}"
+    banner("gemm-fast-k0")
+    c = torch.full((5, 8), 7, dtype=torch.int16, device="cuda")
+    fp8.fp8_scaled_gemm_fast_accum(torch.zeros(5, 0, dtype=torch.uint8, device="cuda"), "e4m3",
+                                   torch.zeros(8, 0, dtype=torch.uint8, device="cuda"), "e4m3",
+                                   f32(1.0), f32(1.0), c)
+    assert not host(c).any()
+    with pytest.raises(fp8.Fp8mpError) as ei:
+        a24 = torch.zeros(16, 24, dtype=torch.uint8, device="cuda")
+        fp8.fp8_scaled_gemm_fast_accum(a24, "e4m3", a24, "e4m3", f32(1.0), f32(1.0), c[:, :0].new_zeros(16, 16))
+    assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("y_fmt", ["e4m3", "e5m2"])
+def test_fast_gemm_fused_output_cast_matches_its_own_output(y_fmt):
+    """The fused fast call's C equals the plain fast call's C bit for bit, and its codes and amax are
+    the oracle's cast of that C."""
+    require_gpu()
+    rng = np.random.default_rng(16)
+    m, n, k = 300, 520, 384
+    a, b = _codes(rng, (m, k), "e4m3"), _codes(rng, (n, k), "e4m3")
+    sa, sb = np.float32(2.0 ** -6), np.float32(2.0 ** -5)
+    banner("gemm-fast-fused", y_fmt)
+    c_plain = _gemm(fp8.fp8_scaled_gemm_fast_accum, a, "e4m3", b, "e4m3", sa, sb)
+    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    yq = torch.zeros(m, n, dtype=torch.uint8, device="cuda")
+    yamax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ys = np.float32(0.37)
+    fp8.fp8_scaled_gemm_amax_cast_fast_accum(dev(a), "e4m3", dev(b), "e4m3", f32(sa), f32(sb), c, y_fmt,
+                                             f32(ys), yq, yamax)
+    cb = host(c)
+    assert np.array_equal(cb, c_plain), first_diff(cb, c_plain)
+    want_q = oracle.cast(cb, ys, y_fmt, "bf16")
+    assert np.array_equal(host(yq), want_q), first_diff(host(yq), want_q)
+    want_amax = oracle.amax(cb, "bf16")
+    assert host(yamax)[0].view(np.uint32) == np.float32(want_amax).view(np.uint32)
+
+
+def test_fast_gemm_full_7b_shape_sampled():
+    """The 7B up-projection shape (4096 x 11008 x 4096) on seeded codes of the upper 48 code values
+    (mixed signs): sampled 64 x 64 output blocks within the fast bound, and the whole output close to
+    the FP32-accumulation GEMM's."""
+    require_gpu()
+    m, n, k = 4096, 11008, 4096
+    rng = np.random.default_rng(4096)
+    top = FMT["e4m3"].max_code
+    qx = ((rng.integers(top - 47, top + 1, (m, k), dtype=np.int64)) |
+          (rng.integers(0, 2, (m, k), dtype=np.int64) << 7)).astype(np.uint8)
+    qw = ((rng.integers(top - 47, top + 1, (n, k), dtype=np.int64)) |
+          (rng.integers(0, 2, (n, k), dtype=np.int64) << 7)).astype(np.uint8)
+    sxi, swi = np.float32(2.0 ** -8), np.float32(2.0 ** -14)
+    banner("gemm-fast-7b")
+    yf = torch.empty(m, n, dtype=torch.int16, device="cuda")
+    ye = torch.empty(m, n, dtype=torch.int16, device="cuda")
+    dq_x, dq_w = dev(qx), dev(qw)
+    fp8.fp8_scaled_gemm_fast_accum(dq_x, "e4m3", dq_w, "e4m3", f32(sxi), f32(swi), yf)
+    fp8.fp8_scaled_gemm(dq_x, "e4m3", dq_w, "e4m3", f32(sxi), f32(swi), ye)
+    yfh = host(yf)
+    blocks = [(0, 0), (m // 64 - 1, n // 64 - 1)] + [tuple(t) for t in rng.integers(0, [m // 64, n // 64], (4, 2))]
+    for bi, bj in blocks:
+        rows, cols = slice(64 * bi, 64 * bi + 64), slice(64 * bj, 64 * bj + 64)
+        ref = oracle.gemm_ref(qx[rows], "e4m3", qw[cols], "e4m3", sxi, swi)
+        absr = oracle.gemm_abs_ref(qx[rows], "e4m3", qw[cols], "e4m3", sxi, swi)
+        ok, worst = oracle.gemm_check(yfh[rows, cols], ref, absr, FAST_ACCUM_SUM_COEF)
+        assert ok, f"block {(bi, bj)}: worst |err|/bound = {worst}"
+    d = (yf.view(torch.bfloat16).float() - ye.view(torch.bfloat16).float()).abs()
+    rel = (d / ye.view(torch.bfloat16).float().abs().clamp_min(1e-3)).median().item()
+    print(f"fast vs FP32 accumulation: median relative difference {rel:.3g}", flush=True)
+    assert rel < 2.0 ** -7

@@ -123,3 +123,80 @@ def test_nan_codes_propagate_and_are_graded():
 
 def test_bf16_output_widening():
     assert bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0000], np.uint16)).tolist() == [1.0, -2.0, 0.0]
+
+
+def _aligned_block_gemm(A, af, B, bf, sa, sb, block=64, frac_bits=16):
+    """A model of a reduced-precision matrix instruction: each block of `block` products is aligned
+    to the binade of its largest |product|, truncated toward zero to frac_bits bits below it and summed
+    exactly; the block sums are added in FP32; the result is scaled in FP32. Written here from that
+    description (not from the oracle) to exercise the fast-accumulation bound."""
+    from oracle.codec import decode_table
+    da = decode_table(FMT[af].name)[A].astype(np.float64)
+    db = decode_table(FMT[bf].name)[B].astype(np.float64)
+    m, k = da.shape
+    n = db.shape[0]
+    out = np.zeros((m, n), np.float32)
+    for i in range(m):
+        p = da[i][None, :] * db            # n x k exact products
+        acc = np.zeros(n, np.float32)
+        for k0 in range(0, k, block):
+            blk = p[:, k0:k0 + block]
+            mx = np.abs(blk).max(axis=1)
+            e = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
+            q = np.ldexp(1.0, (e - frac_bits).astype(int))[:, None]
+            s = (np.trunc(blk / q) * q).sum(axis=1)
+            acc = (acc.astype(np.float64) + s).astype(np.float32)
+        out[i] = acc * (np.float32(sa) * np.float32(sb))
+    return out.astype(np.float64)
+
+
+def test_fast_accumulation_bound_holds_for_the_aligned_block_model():
+    """The fast-accumulation bound (2**-9 * sum|ab|) accepts the aligned-block reduction on
+    full-range random codes and on blocks with one dominant product, while the FP32 bound rejects the
+    latter; exact sums come out when every product of a block has one magnitude."""
+    from oracle.gemm import FAST_ACCUM_SUM_COEF
+    rng = np.random.default_rng(11)
+    for af, bf in [("e4m3", "e4m3"), ("e5m2", "e4m3")]:
+        A = _finite_codes(rng, (12, 256), af)
+        B = _finite_codes(rng, (10, 256), bf)
+        sa, sb = np.float32(1 / 16), np.float32(3.0)
+        y = _aligned_block_gemm(A, af, B, bf, sa, sb)
+        ref = gemm_ref(A, af, B, bf, sa, sb)
+        absr = gemm_abs_ref(A, af, B, bf, sa, sb)
+        assert gemm_check(_to_bf16_bits(y), ref, absr, FAST_ACCUM_SUM_COEF)[0]
+    # one dominant product per block, +448*448 in the first and -448*448 in the second so they cancel,
+    # and 63 products of 1.5 per block that the alignment (quantum 2 at 448*448) truncates to zero
+    A = np.full((4, 128), 0x38, np.uint8)     # E4M3 1.0
+    B = np.full((3, 128), 0x3C, np.uint8)     # E4M3 1.5
+    A[:, ::64] = 0x7E
+    B[:, 0] = 0x7E
+    B[:, 64] = 0xFE
+    B[1, 1::2] |= 0x80                          # mixed signs among the small products
+    y = _aligned_block_gemm(A, "e4m3", B, "e4m3", 1.0, 1.0)
+    ref = gemm_ref(A, "e4m3", B, "e4m3", 1.0, 1.0)
+    absr = gemm_abs_ref(A, "e4m3", B, "e4m3", 1.0, 1.0)
+    assert not np.array_equal(y, ref)
+    assert gemm_check(_to_bf16_bits(y), ref, absr, FAST_ACCUM_SUM_COEF)[0]
+    assert not gemm_check(_to_bf16_bits(y), ref, absr)[0]
+    # equal magnitudes within each block: the model is exact
+    A = (np.full((5, 192), 0x30, np.uint8) | (rng.integers(0, 2, (5, 192)) << 7).astype(np.uint8))
+    B = (np.full((6, 192), 0x48, np.uint8) | (rng.integers(0, 2, (6, 192)) << 7).astype(np.uint8))
+    assert np.array_equal(_aligned_block_gemm(A, "e4m3", B, "e4m3", 1.0, 1.0),
+                          gemm_ref(A, "e4m3", B, "e4m3", 1.0, 1.0))
+
+
+def test_fast_accumulation_bound_rejects_wrong_results():
+    """Under the looser bound a transposed pairing, a doubled inverse scale and a sign flip still fail."""
+    from oracle.gemm import FAST_ACCUM_SUM_COEF
+    rng = np.random.default_rng(12)
+    K = 256
+    A = _finite_codes(rng, (16, K), "e4m3")
+    Bs = _finite_codes(rng, (16, K), "e4m3")
+    sa, sb = np.float32(1 / 64), np.float32(1 / 32)
+    ref = gemm_ref(A, "e4m3", Bs, "e4m3", sa, sb)
+    absr = gemm_abs_ref(A, "e4m3", Bs, "e4m3", sa, sb)
+    c = FAST_ACCUM_SUM_COEF
+    assert gemm_check(_to_bf16_bits(ref), ref, absr, c)[0]
+    assert not gemm_check(_to_bf16_bits(ref.T), ref, absr, c)[0]
+    assert not gemm_check(_to_bf16_bits(ref * float(sa)), ref, absr, c)[0]
+    assert not gemm_check(_to_bf16_bits(-ref), ref, absr, c)[0]
