@@ -23,8 +23,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = fp8.exported_symbols()
     assert names == ["fp8_amax_cast", "fp8_amax_cast_batched", "fp8_scale_update", "fp8_scale_update_batched",
-                     "fp8_scaled_gemm",
-                     "fp8_scaled_gemm_amax_cast",
+                     "fp8_scaled_gemm", "fp8_scaled_gemm_fast_accum",
+                     "fp8_scaled_gemm_amax_cast", "fp8_scaled_gemm_amax_cast_fast_accum",
                      "fp8_layernorm_amax_cast", "fp8_reduce_shared_scale", "fp8_adam_step",
                      "fp8_adam_step_weight_cast", "fp8mp_status_string", "fp8mp_device_info"]
     for n in names:
@@ -101,8 +101,9 @@ def test_batched_scale_update_validation(lib):
     assert call(s=ptrs(12289, 12292)) == INVALID
 
 
-def test_gemm_argument_validation(lib):
-    f = lib.fp8_scaled_gemm
+@pytest.mark.parametrize("name", ["fp8_scaled_gemm", "fp8_scaled_gemm_fast_accum"])
+def test_gemm_argument_validation(lib, name):
+    f = getattr(lib, name)
     args = lambda **kw: [kw.get("a", A16), kw.get("af", 0), kw.get("lda", 32), kw.get("b", A16), kw.get("bf", 0),
                          kw.get("ldb", 32), kw.get("m", 4), kw.get("n", 8), kw.get("k", 32),
                          kw.get("sa", A16), kw.get("sb", A16), kw.get("c", A16), kw.get("ldc", 8), None]
@@ -121,8 +122,9 @@ def test_gemm_argument_validation(lib):
     assert f(*args(ldb=2**22 + 16)) == UNSUPPORTED
 
 
-def test_fused_gemm_argument_validation(lib):
-    f = lib.fp8_scaled_gemm_amax_cast
+@pytest.mark.parametrize("name", ["fp8_scaled_gemm_amax_cast", "fp8_scaled_gemm_amax_cast_fast_accum"])
+def test_fused_gemm_argument_validation(lib, name):
+    f = getattr(lib, name)
     args = lambda **kw: [kw.get("a", A16), kw.get("af", 0), kw.get("lda", 32), kw.get("b", A16), kw.get("bf", 0),
                          kw.get("ldb", 32), kw.get("m", 4), kw.get("n", 8), kw.get("k", 32),
                          kw.get("sa", A16), kw.get("sb", A16), kw.get("c", A16), kw.get("ldc", 8),
@@ -239,6 +241,9 @@ def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_scaled_gemm(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE
     assert lib.fp8_scaled_gemm_amax_cast(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, 0, A16, A16, 8, A16,
                                          None) == NO_DEVICE
+    assert lib.fp8_scaled_gemm_fast_accum(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE
+    assert lib.fp8_scaled_gemm_amax_cast_fast_accum(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, 0, A16, A16,
+                                                    8, A16, None) == NO_DEVICE
     assert lib.fp8_layernorm_amax_cast(A16, 1, 4, 8, 8, A16, None, 1e-5, A16, 8, 0, A16, A16, 8, A16, None, None,
                                        None) == NO_DEVICE
     assert lib.fp8_reduce_shared_scale(A16, 1, 4, 64, 64, A16, A16, 1, None) == NO_DEVICE
