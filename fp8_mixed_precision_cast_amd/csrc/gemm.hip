@@ -51,18 +51,28 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kThreads = 512;             // 8 waves, two per SIMD
-constexpr int kWavesN = 4;                // waves laid out 2 (M) x 4 (N)
-constexpr int kWM = 128, kWN = 64;        // wave tile
-constexpr int kPM = kWM / 32, kPN = kWN / 32;   // 32 x 32 MFMA blocks per wave
 constexpr int kTileBytes = kBM * kBK;     // one operand's K step in LDS: 32 KB
-constexpr int kSlabs = kTileBytes / (kThreads * 16);   // 1 KB LDS slabs each wave fills per operand
-constexpr int kRowsPerPass = kThreads / 32;            // epilogue write-out: 32 threads per 512-byte row
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
 // Accumulation modes: FP32-accurate (BF16 MFMA on exactly widened codes) or
 // the FP8 MFMA's own reduced-precision reduction.
 constexpr int kAccExact = 0, kAccFast = 1;
+
+// Wave geometry of each mode: 8 waves (two per SIMD) of 128 x 64. For the FP8
+// MFMA, 4 waves (one per SIMD) of 128 x 128 with the 256 accumulators in AGPRs
+// read a third less LDS per MFMA but measured 12-17% slower at 4096 x 11008 x
+// 4096 (one wave per SIMD hides less latency), so both modes share the layout.
+template <int ACC>
+struct Geo {
+  static constexpr int kThreads = 512;
+  static constexpr int kWavesN = 4;                                 // waves laid out (kThreads/64/kWavesN) x kWavesN
+  static constexpr int kWM = 128, kWN = 64;                         // wave tile
+  static constexpr int kPM = kWM / 32, kPN = kWN / 32;              // 32 x 32 MFMA blocks per wave
+  static constexpr int kSlabs = kTileBytes / (kThreads * 16);      // 1 KB LDS slabs each wave fills per operand
+  static constexpr int kRowsPerPass = kThreads / 32;                // epilogue write-out: 32 threads per 512-byte row
+  static_assert(kSlabs % 2 == 0, "slab parity must equal j parity");
+  static_assert((kThreads / 64 / kWavesN) * kWM == kBM && kWavesN * kWN == kBN, "waves must tile the block");
+};
 constexpr int kCRow = kBN * 2;            // bytes of one BF16 output row of the tile in LDS
 static_assert(kBM * kCRow <= 4 * kTileBytes, "the BF16 output tile must fit in the two stages");
 
@@ -124,7 +134,6 @@ struct TileCopy {
   uint32_t kc0, kc1;             // c * 16 on even and odd slabs
   uint32_t row_ok;               // bit j: slab j's row exists
 };
-static_assert(kSlabs % 2 == 0, "slab parity must equal j parity");
 static_assert(kBM == kBN, "one copy geometry serves both operands");
 
 // Leading dimensions are at most kGemmMaxLd bytes, so a tile's rows span less
@@ -135,8 +144,10 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
 // The buffer resource starts at the tile's first row, so operands of any size
 // are addressed with 32-bit offsets.
+template <class GEO>
 __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int64_t row0, int64_t rows, int64_t K,
                                               int wave, int lane) {
+  constexpr int kSlabs = GEO::kSlabs;
   TileCopy t;
   const int64_t here = rows - row0 < kBM ? rows - row0 : kBM;   // rows of this tile that exist (>= 1)
   const uint32_t bytes = (uint32_t)((here - 1) * ld + K);
@@ -155,7 +166,9 @@ __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int6
 
 // Copies K step [k0, k0 + 128) of one operand into an LDS tile. Chunks of
 // missing rows or past K are read out of range, which stores zeros.
+template <class GEO>
 __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32_t K, uint8_t* lds, int wave) {
+  constexpr int kSlabs = GEO::kSlabs;
   // all-ones where the chunk exists: a branch-free choice between its offset and out of range
   const uint32_t km0 = 0u - (uint32_t)(k0 + t.kc0 < K), km1 = 0u - (uint32_t)(k0 + t.kc1 < K);
 #pragma unroll
@@ -169,7 +182,8 @@ __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32
 
 // Accumulators of one wave's 128 x 64 tile: 4 x 2 blocks of 32 x 32, each
 // held transposed (see mma_step), 128 floats per lane.
-struct Acc { v16f v[kPM][kPN]; };
+template <class GEO>
+struct Acc { v16f v[GEO::kPM][GEO::kPN]; };
 
 // One K step (32 x 32 x 16 BF16 MFMAs). Lane group G = lane / 32 owns
 // chunks 4G .. 4G+3 (k bytes 64G .. 64G+63) of its row; sub-step s (0..7)
@@ -186,9 +200,10 @@ struct Acc { v16f v[kPM][kPN]; };
 // issued after the first two sub-steps' MFMAs (`issue_copies`): their LDS
 // writes then no longer compete with the first fragment reads of the step
 // (measured 2-5% faster than issuing them at the top).
-template <int FA, int FB, typename Issue>
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc& acc, int wm, int wn, int lane,
-                                         Issue&& issue_copies) {
+template <class GEO, int FA, int FB, typename Issue>
+__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<GEO>& acc, int wm, int wn,
+                                         int lane, Issue&& issue_copies) {
+  constexpr int kWM = GEO::kWM, kWN = GEO::kWN, kPM = GEO::kPM, kPN = GEO::kPN;
   const int G = lane >> 5;
   const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
   uint4 aq[2][kPM], bq[2][kPN];
@@ -250,9 +265,10 @@ constexpr int mfma_fmt() { return FMT == FP8MP_E4M3 ? 0 : 1; }
 // transposed (B first), giving the same accumulator layout as mma_step.
 // Both sub-steps' fragments are read up front; the next K step's copies are
 // issued after the first sub-step's MFMAs.
-template <int FA, int FB, typename Issue>
-__device__ __forceinline__ void mma_step_fast(const uint8_t* As, const uint8_t* Bs, Acc& acc, int wm, int wn,
+template <class GEO, int FA, int FB, typename Issue>
+__device__ __forceinline__ void mma_step_fast(const uint8_t* As, const uint8_t* Bs, Acc<GEO>& acc, int wm, int wn,
                                               int lane, Issue&& issue_copies) {
+  constexpr int kWM = GEO::kWM, kWN = GEO::kWN, kPM = GEO::kPM, kPN = GEO::kPN;
   const int G = lane >> 5;
   const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
   v8i af[2][kPM], bf[2][kPN];
@@ -290,17 +306,18 @@ __device__ __forceinline__ void mma_step_fast(const uint8_t* As, const uint8_t* 
 template <int FA, int FB, int ACC>
 __device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bool more,
                                                const TileCopy& ca, const TileCopy& cb, uint32_t k_next, uint32_t K,
-                                               Acc& acc, int wm, int wn, int wave, int lane) {
+                                               Acc<Geo<ACC>>& acc, int wm, int wn, int wave, int lane) {
+  using GEO = Geo<ACC>;
   auto issue = [&]() {
     if (more) {
-      load_tile(ca, k_next, K, nxt, wave);
-      load_tile(cb, k_next, K, nxt + kTileBytes, wave);
+      load_tile<GEO>(ca, k_next, K, nxt, wave);
+      load_tile<GEO>(cb, k_next, K, nxt + kTileBytes, wave);
     }
   };
   if constexpr (ACC == kAccFast)
-    mma_step_fast<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
+    mma_step_fast<GEO, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
   else
-    mma_step<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
+    mma_step<GEO, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
 }
 
 // No FP8 copy of the output (YF of the plain GEMM).
@@ -311,11 +328,14 @@ constexpr int kNoY = -1;
 // *y_amax = max(*y_amax, max|C|) (if y_amax) and y_q = enc_YF(C * *y_scale)
 // (if y_q).
 template <int FA, int FB, int YF, int ACC>
-__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
+__global__ __launch_bounds__(Geo<ACC>::kThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, const float* __restrict__ sb,
     uint16_t* __restrict__ C, int64_t ldc, int tm, int tn, const float* __restrict__ y_scale,
     uint8_t* __restrict__ y_q, int64_t ld_yq, float* __restrict__ y_amax) {
+  using GEO = Geo<ACC>;
+  constexpr int kThreads = GEO::kThreads, kWavesN = GEO::kWavesN, kWM = GEO::kWM, kWN = GEO::kWN;
+  constexpr int kPM = GEO::kPM, kPN = GEO::kPN, kRowsPerPass = GEO::kRowsPerPass;
   // Two stages, each an A tile followed by a B tile.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
 
@@ -331,16 +351,16 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   tile_coords(blockIdx.x, tm, tn, bm, bn);
   const int64_t m0 = (int64_t)bm * kBM, n0 = (int64_t)bn * kBN;
 
-  Acc acc;
+  Acc<GEO> acc;
   float* accf = reinterpret_cast<float*>(&acc);
 #pragma unroll
   for (int e = 0; e < (int)(sizeof(acc) / sizeof(float)); ++e) accf[e] = 0.f;
 
-  const TileCopy ca = make_copy(A, lda, m0, M, K, wave, lane);
-  const TileCopy cb = make_copy(B, ldb, n0, N, K, wave, lane);
+  const TileCopy ca = make_copy<GEO>(A, lda, m0, M, K, wave, lane);
+  const TileCopy cb = make_copy<GEO>(B, ldb, n0, N, K, wave, lane);
   if (nk > 0) {
-    load_tile(ca, 0, Ku, smem, wave);
-    load_tile(cb, 0, Ku, smem + kTileBytes, wave);
+    load_tile<GEO>(ca, 0, Ku, smem, wave);
+    load_tile<GEO>(cb, 0, Ku, smem + kTileBytes, wave);
   }
   // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
   // step kt + 1. The barrier at the top of a step both publishes the stage to
@@ -388,42 +408,47 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   uint32_t am = 0;   // packed BF16 magnitudes of the in-range outputs
   const bool full = m0 + kBM <= M && n0 + kBN <= N && vec && (!do_q || vq);
   if (full) {
-    // Interior tile: all sixteen chunks are read first (the accumulators are
-    // dead, so the registers are free), then stored with 16-byte stores and
-    // converted without branches.
-    uint4 v[kBM / kRowsPerPass];
+    // Interior tile: the chunks of up to 16 passes are read first (the
+    // accumulators are dead, so the registers are free), then stored with
+    // 16-byte stores and converted without branches.
+    constexpr int kPasses = kBM / kRowsPerPass, kBatch = kPasses < 16 ? kPasses : 16;
+    static_assert(kPasses % kBatch == 0, "passes split into equal batches");
 #pragma unroll
-    for (int p = 0; p < kBM / kRowsPerPass; ++p) {
-      const int row = p * kRowsPerPass + (tid >> 5);
-      v[p] = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
-    }
-    if (do_c) {
+    for (int p0 = 0; p0 < kPasses; p0 += kBatch) {
+      uint4 v[kBatch];
 #pragma unroll
-      for (int p = 0; p < kBM / kRowsPerPass; ++p)
-        *reinterpret_cast<uint4*>(C + (m0 + p * kRowsPerPass + (tid >> 5)) * ldc + gn) = v[p];
-    }
-    if constexpr (YF != kNoY) {
-      // Magnitude max of this thread's 128 values: the amax contribution,
-      // and the test for NaN sources.
-      uint32_t mx = 0;
+      for (int p = 0; p < kBatch; ++p) {
+        const int row = (p0 + p) * kRowsPerPass + (tid >> 5);
+        v[p] = *reinterpret_cast<const uint4*>(smem + row * kCRow + ((c ^ (row & 31)) << 4));
+      }
+      if (do_c) {
 #pragma unroll
-      for (int p = 0; p < kBM / kRowsPerPass; ++p)
-        mx = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(mx, v[p].x), v[p].y), v[p].z), v[p].w);
-      if (do_amax) am = mx;
-      if (do_q) {
-        const uint32_t sb = __float_as_uint(ys) & 0x7FFFFFFFu;
-        const bool no_nan = (mx & 0xFFFFu) <= 0x7F80u && (mx >> 16) <= 0x7F80u && sb != 0u && sb < 0x7F800000u;
-        if (no_nan) {
+        for (int p = 0; p < kBatch; ++p)
+          *reinterpret_cast<uint4*>(C + (m0 + (p0 + p) * kRowsPerPass + (tid >> 5)) * ldc + gn) = v[p];
+      }
+      if constexpr (YF != kNoY) {
+        // Magnitude max of this batch's values: the amax contribution, and
+        // the test for NaN sources (the two encoders agree on every other value).
+        uint32_t mx = 0;
 #pragma unroll
-          for (int p = 0; p < kBM / kRowsPerPass; ++p) {
-            const uint2 qq = {enc4_bf16_nonan<YF>(v[p].x, v[p].y, ys), enc4_bf16_nonan<YF>(v[p].z, v[p].w, ys)};
-            *reinterpret_cast<uint2*>(y_q + (m0 + p * kRowsPerPass + (tid >> 5)) * ld_yq + gn) = qq;
-          }
-        } else {
+        for (int p = 0; p < kBatch; ++p)
+          mx = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(mx, v[p].x), v[p].y), v[p].z), v[p].w);
+        if (do_amax) am = amax_bf16x2(am, mx);
+        if (do_q) {
+          const uint32_t sb = __float_as_uint(ys) & 0x7FFFFFFFu;
+          const bool no_nan = (mx & 0xFFFFu) <= 0x7F80u && (mx >> 16) <= 0x7F80u && sb != 0u && sb < 0x7F800000u;
+          if (no_nan) {
 #pragma unroll
-          for (int p = 0; p < kBM / kRowsPerPass; ++p) {
-            const uint2 qq = {enc4_bf16_sel<YF>(v[p].x, v[p].y, ys), enc4_bf16_sel<YF>(v[p].z, v[p].w, ys)};
-            *reinterpret_cast<uint2*>(y_q + (m0 + p * kRowsPerPass + (tid >> 5)) * ld_yq + gn) = qq;
+            for (int p = 0; p < kBatch; ++p) {
+              const uint2 qq = {enc4_bf16_nonan<YF>(v[p].x, v[p].y, ys), enc4_bf16_nonan<YF>(v[p].z, v[p].w, ys)};
+              *reinterpret_cast<uint2*>(y_q + (m0 + (p0 + p) * kRowsPerPass + (tid >> 5)) * ld_yq + gn) = qq;
+            }
+          } else {
+#pragma unroll
+            for (int p = 0; p < kBatch; ++p) {
+              const uint2 qq = {enc4_bf16_sel<YF>(v[p].x, v[p].y, ys), enc4_bf16_sel<YF>(v[p].z, v[p].w, ys)};
+              *reinterpret_cast<uint2*>(y_q + (m0 + (p0 + p) * kRowsPerPass + (tid >> 5)) * ld_yq + gn) = qq;
+            }
           }
         }
       }
@@ -490,7 +515,8 @@ struct GemmArgs {
 template <int FA, int FB, int YF, int ACC>
 hipError_t launch_one(const GemmArgs& g, hipStream_t stream) {
   const int tm = (int)((g.m + kBM - 1) / kBM), tn = (int)((g.n + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, YF, ACC>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream, g.a,
+  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, YF, ACC>), dim3((unsigned)(tm * tn)), dim3(Geo<ACC>::kThreads), 0,
+                     stream, g.a,
                      g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, tm, tn, g.y_scale, g.y_q, g.ld_yq,
                      g.y_amax);
   return hipGetLastError();
