@@ -58,21 +58,16 @@ constexpr int kXcds = 8;
 // the FP8 MFMA's own reduced-precision reduction.
 constexpr int kAccExact = 0, kAccFast = 1;
 
-// Wave geometry of each mode: 8 waves (two per SIMD) of 128 x 64. For the FP8
-// MFMA, 4 waves (one per SIMD) of 128 x 128 with the 256 accumulators in AGPRs
-// read a third less LDS per MFMA but measured 12-17% slower at 4096 x 11008 x
-// 4096 (one wave per SIMD hides less latency), so both modes share the layout.
-template <int ACC>
-struct Geo {
-  static constexpr int kThreads = 512;
-  static constexpr int kWavesN = 4;                                 // waves laid out (kThreads/64/kWavesN) x kWavesN
-  static constexpr int kWM = 128, kWN = 64;                         // wave tile
-  static constexpr int kPM = kWM / 32, kPN = kWN / 32;              // 32 x 32 MFMA blocks per wave
-  static constexpr int kSlabs = kTileBytes / (kThreads * 16);      // 1 KB LDS slabs each wave fills per operand
-  static constexpr int kRowsPerPass = kThreads / 32;                // epilogue write-out: 32 threads per 512-byte row
-  static_assert(kSlabs % 2 == 0, "slab parity must equal j parity");
-  static_assert((kThreads / 64 / kWavesN) * kWM == kBM && kWavesN * kWN == kBN, "waves must tile the block");
-};
+constexpr int kThreads = 512;             // 8 waves, two per SIMD
+constexpr int kWavesN = 4;                // waves laid out 2 (M) x 4 (N)
+constexpr int kWM = 128, kWN = 64;        // wave tile
+constexpr int kPM = kWM / 32, kPN = kWN / 32;   // 32 x 32 MFMA blocks per wave
+constexpr int kSlabs = kTileBytes / (kThreads * 16);   // 1 KB LDS slabs each wave fills per operand
+constexpr int kRowsPerPass = kThreads / 32;            // epilogue write-out: 32 threads per 512-byte row
+static_assert(kSlabs % 2 == 0, "slab parity must equal j parity");
+// Both accumulation modes use this layout. (For the fast mode, 4 waves of
+// 128 x 128 with the accumulators in AGPRs read a third less LDS per MFMA but
+// measured 12-17% slower at 4096 x 11008 x 4096.)
 constexpr int kCRow = kBN * 2;            // bytes of one BF16 output row of the tile in LDS
 static_assert(kBM * kCRow <= 4 * kTileBytes, "the BF16 output tile must fit in the two stages");
 
@@ -144,10 +139,8 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
 // The buffer resource starts at the tile's first row, so operands of any size
 // are addressed with 32-bit offsets.
-template <class GEO>
 __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int64_t row0, int64_t rows, int64_t K,
                                               int wave, int lane) {
-  constexpr int kSlabs = GEO::kSlabs;
   TileCopy t;
   const int64_t here = rows - row0 < kBM ? rows - row0 : kBM;   // rows of this tile that exist (>= 1)
   const uint32_t bytes = (uint32_t)((here - 1) * ld + K);
@@ -166,9 +159,7 @@ __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int6
 
 // Copies K step [k0, k0 + 128) of one operand into an LDS tile. Chunks of
 // missing rows or past K are read out of range, which stores zeros.
-template <class GEO>
 __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32_t K, uint8_t* lds, int wave) {
-  constexpr int kSlabs = GEO::kSlabs;
   // all-ones where the chunk exists: a branch-free choice between its offset and out of range
   const uint32_t km0 = 0u - (uint32_t)(k0 + t.kc0 < K), km1 = 0u - (uint32_t)(k0 + t.kc1 < K);
 #pragma unroll
@@ -182,8 +173,7 @@ __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32
 
 // Accumulators of one wave's 128 x 64 tile: 4 x 2 blocks of 32 x 32, each
 // held transposed (see mma_step), 128 floats per lane.
-template <class GEO>
-struct Acc { v16f v[GEO::kPM][GEO::kPN]; };
+struct Acc { v16f v[kPM][kPN]; };
 
 // One K step (32 x 32 x 16 BF16 MFMAs). Lane group G = lane / 32 owns
 // chunks 4G .. 4G+3 (k bytes 64G .. 64G+63) of its row; sub-step s (0..7)
@@ -200,10 +190,9 @@ struct Acc { v16f v[GEO::kPM][GEO::kPN]; };
 // issued after the first two sub-steps' MFMAs (`issue_copies`): their LDS
 // writes then no longer compete with the first fragment reads of the step
 // (measured 2-5% faster than issuing them at the top).
-template <class GEO, int FA, int FB, typename Issue>
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<GEO>& acc, int wm, int wn,
-                                         int lane, Issue&& issue_copies) {
-  constexpr int kWM = GEO::kWM, kWN = GEO::kWN, kPM = GEO::kPM, kPN = GEO::kPN;
+template <int FA, int FB, typename Issue>
+__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc& acc, int wm, int wn, int lane,
+                                         Issue&& issue_copies) {
   const int G = lane >> 5;
   const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
   uint4 aq[2][kPM], bq[2][kPN];
@@ -265,10 +254,9 @@ constexpr int mfma_fmt() { return FMT == FP8MP_E4M3 ? 0 : 1; }
 // transposed (B first), giving the same accumulator layout as mma_step.
 // Both sub-steps' fragments are read up front; the next K step's copies are
 // issued after the first sub-step's MFMAs.
-template <class GEO, int FA, int FB, typename Issue>
-__device__ __forceinline__ void mma_step_fast(const uint8_t* As, const uint8_t* Bs, Acc<GEO>& acc, int wm, int wn,
+template <int FA, int FB, typename Issue>
+__device__ __forceinline__ void mma_step_fast(const uint8_t* As, const uint8_t* Bs, Acc& acc, int wm, int wn,
                                               int lane, Issue&& issue_copies) {
-  constexpr int kWM = GEO::kWM, kWN = GEO::kWN, kPM = GEO::kPM, kPN = GEO::kPN;
   const int G = lane >> 5;
   const int ra = wm * kWM + (lane & 31), rb = wn * kWN + (lane & 31);
   v8i af[2][kPM], bf[2][kPN];
@@ -306,18 +294,17 @@ __device__ __forceinline__ void mma_step_fast(const uint8_t* As, const uint8_t* 
 template <int FA, int FB, int ACC>
 __device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bool more,
                                                const TileCopy& ca, const TileCopy& cb, uint32_t k_next, uint32_t K,
-                                               Acc<Geo<ACC>>& acc, int wm, int wn, int wave, int lane) {
-  using GEO = Geo<ACC>;
+                                               Acc& acc, int wm, int wn, int wave, int lane) {
   auto issue = [&]() {
     if (more) {
-      load_tile<GEO>(ca, k_next, K, nxt, wave);
-      load_tile<GEO>(cb, k_next, K, nxt + kTileBytes, wave);
+      load_tile(ca, k_next, K, nxt, wave);
+      load_tile(cb, k_next, K, nxt + kTileBytes, wave);
     }
   };
   if constexpr (ACC == kAccFast)
-    mma_step_fast<GEO, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
+    mma_step_fast<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
   else
-    mma_step<GEO, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
+    mma_step<FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
 }
 
 // No FP8 copy of the output (YF of the plain GEMM).
@@ -328,14 +315,11 @@ constexpr int kNoY = -1;
 // *y_amax = max(*y_amax, max|C|) (if y_amax) and y_q = enc_YF(C * *y_scale)
 // (if y_q).
 template <int FA, int FB, int YF, int ACC>
-__global__ __launch_bounds__(Geo<ACC>::kThreads) void gemm_fp8_kernel(
+__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, const float* __restrict__ sb,
     uint16_t* __restrict__ C, int64_t ldc, int tm, int tn, const float* __restrict__ y_scale,
     uint8_t* __restrict__ y_q, int64_t ld_yq, float* __restrict__ y_amax) {
-  using GEO = Geo<ACC>;
-  constexpr int kThreads = GEO::kThreads, kWavesN = GEO::kWavesN, kWM = GEO::kWM, kWN = GEO::kWN;
-  constexpr int kPM = GEO::kPM, kPN = GEO::kPN, kRowsPerPass = GEO::kRowsPerPass;
   // Two stages, each an A tile followed by a B tile.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
 
@@ -351,16 +335,16 @@ __global__ __launch_bounds__(Geo<ACC>::kThreads) void gemm_fp8_kernel(
   tile_coords(blockIdx.x, tm, tn, bm, bn);
   const int64_t m0 = (int64_t)bm * kBM, n0 = (int64_t)bn * kBN;
 
-  Acc<GEO> acc;
+  Acc acc;
   float* accf = reinterpret_cast<float*>(&acc);
 #pragma unroll
   for (int e = 0; e < (int)(sizeof(acc) / sizeof(float)); ++e) accf[e] = 0.f;
 
-  const TileCopy ca = make_copy<GEO>(A, lda, m0, M, K, wave, lane);
-  const TileCopy cb = make_copy<GEO>(B, ldb, n0, N, K, wave, lane);
+  const TileCopy ca = make_copy(A, lda, m0, M, K, wave, lane);
+  const TileCopy cb = make_copy(B, ldb, n0, N, K, wave, lane);
   if (nk > 0) {
-    load_tile<GEO>(ca, 0, Ku, smem, wave);
-    load_tile<GEO>(cb, 0, Ku, smem + kTileBytes, wave);
+    load_tile(ca, 0, Ku, smem, wave);
+    load_tile(cb, 0, Ku, smem + kTileBytes, wave);
   }
   // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
   // step kt + 1. The barrier at the top of a step both publishes the stage to
@@ -515,9 +499,8 @@ struct GemmArgs {
 template <int FA, int FB, int YF, int ACC>
 hipError_t launch_one(const GemmArgs& g, hipStream_t stream) {
   const int tm = (int)((g.m + kBM - 1) / kBM), tn = (int)((g.n + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, YF, ACC>), dim3((unsigned)(tm * tn)), dim3(Geo<ACC>::kThreads), 0,
-                     stream, g.a,
-                     g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, tm, tn, g.y_scale, g.y_q, g.ld_yq,
+  hipLaunchKernelGGL((gemm_fp8_kernel<FA, FB, YF, ACC>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream,
+                     g.a, g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, tm, tn, g.y_scale, g.y_q, g.ld_yq,
                      g.y_amax);
   return hipGetLastError();
 }

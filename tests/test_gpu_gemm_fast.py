@@ -168,3 +168,86 @@ def test_fast_gemm_full_7b_shape_sampled():
     rel = (d / ye.view(torch.bfloat16).float().abs().clamp_min(1e-3)).median().item()
     print(f"fast vs FP32 accumulation: median relative difference {rel:.3g}", flush=True)
     assert rel < 2.0 ** -7
+
+
+def test_fast_gemm_non_finite_codes_propagate():
+    """NaN codes (E4M3 0x7F / 0xFF) give NaN rows and columns, and an E5M2 +-Inf code gives +-Inf
+    (or NaN against a zero), exactly as the oracle's float64 sum does; the rest stays within the
+    fast bound."""
+    require_gpu()
+    rng = np.random.default_rng(17)
+    a = _codes(rng, (64, 128), "e4m3")
+    b = _codes(rng, (80, 128), "e4m3")
+    a[3, 77] = 0x7F
+    b[10, 5] = 0xFF
+    banner("gemm-fast-nan")
+    y = _gemm(fp8.fp8_scaled_gemm_fast_accum, a, "e4m3", b, "e4m3", 1.0, 1.0)
+    ref = oracle.gemm_ref(a, "e4m3", b, "e4m3", 1.0, 1.0)
+    absr = oracle.gemm_abs_ref(a, "e4m3", b, "e4m3", 1.0, 1.0)
+    ok, worst = oracle.gemm_check(y, ref, absr, FAST_ACCUM_SUM_COEF)
+    assert ok, f"worst |err|/bound = {worst}"
+    yf = oracle.gemm.bf16_bits_to_f64(y)
+    assert np.isnan(yf[3]).all() and np.isnan(yf[:, 10]).all()
+    # E5M2 infinities: row 5 holds +Inf at k = 9, B column 9 is nonzero except in row 2 of B
+    a5 = _codes(rng, (40, 64), "e5m2")
+    b5 = _codes(rng, (24, 64), "e4m3")
+    a5[5, 9] = 0x7C
+    a5[6, 9] = 0xFC
+    b5[:, 9] = np.where((b5[:, 9] & 0x7F) == 0, 0x38, b5[:, 9])
+    b5[2, 9] = 0x00
+    banner("gemm-fast-inf")
+    y5 = _gemm(fp8.fp8_scaled_gemm_fast_accum, a5, "e5m2", b5, "e4m3", 0.5, 2.0)
+    ref5 = oracle.gemm_ref(a5, "e5m2", b5, "e4m3", 0.5, 2.0)
+    absr5 = oracle.gemm_abs_ref(a5, "e5m2", b5, "e4m3", 0.5, 2.0)
+    assert np.isinf(ref5[5]).sum() == 23 and np.isnan(ref5[5, 2])
+    ok, worst = oracle.gemm_check(y5, ref5, absr5, FAST_ACCUM_SUM_COEF)
+    assert ok, f"worst |err|/bound = {worst}"
+
+
+def test_fast_gemm_output_beyond_two_to_the_31_elements():
+    """C of 65536 x 32800 (2^31 + 2^21 elements, ragged in N) from the fast GEMM: entries on both sides
+    of the 2^31-th, the edges and random entries against the oracle's, within the fast bound."""
+    require_gpu()
+    m, n, k = 65536, 32800, 32
+    rng = np.random.default_rng(2032)
+    a = _codes(rng, (m, k), "e4m3")
+    b = _codes(rng, (n, k), "e4m3")
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    c = torch.empty(m, n, dtype=torch.int16, device="cuda")
+    banner("gemm-fast >2^31 outputs")
+    fp8.fp8_scaled_gemm_fast_accum(dev(a), "e4m3", dev(b), "e4m3", f32(sa), f32(sb), c)
+    flat = np.concatenate([np.arange(2 ** 31 - 64, 2 ** 31 + 64), rng.integers(0, m * n, 3000),
+                           np.arange(m * n - 64, m * n), np.arange(0, 64)])
+    rows, cols = flat // n, flat % n
+    got = host(c.view(-1)[torch.from_numpy(flat).cuda()]).view(np.uint16)
+    ref = np.empty(flat.size)
+    absr = np.empty(flat.size)
+    for t, (i, j) in enumerate(zip(rows, cols)):
+        ref[t], absr[t] = oracle.gemm_entry(a, "e4m3", b, "e4m3", sa, sb, i, j)
+    ok, worst = oracle.gemm_check(got, ref, absr, FAST_ACCUM_SUM_COEF)
+    assert ok, f"worst |err|/bound = {worst}"
+
+
+def test_fast_gemm_at_the_largest_leading_dimension():
+    """lda = ldb = 4 MiB (the largest supported) through the fast GEMM; one byte more is refused."""
+    require_gpu()
+    m, n, k = 300, 290, 48
+    ld = 1 << 22
+    rng = np.random.default_rng(23)
+    a = _codes(rng, (m, k), "e4m3")
+    b = _codes(rng, (n, k), "e5m2")
+    sa, sb = np.float32(0.75), np.float32(2.0)
+    a_store = torch.zeros(m, ld, dtype=torch.uint8, device="cuda")
+    b_store = torch.zeros(n, ld, dtype=torch.uint8, device="cuda")
+    a_store[:, :k] = dev(a)
+    b_store[:, :k] = dev(b)
+    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    banner("gemm-fast max ld")
+    fp8.fp8_scaled_gemm_fast_accum(a_store[:, :k], "e4m3", b_store[:, :k], "e5m2", f32(sa), f32(sb), c)
+    ref = oracle.gemm_ref(a, "e4m3", b, "e5m2", sa, sb)
+    absr = oracle.gemm_abs_ref(a, "e4m3", b, "e5m2", sa, sb)
+    ok, worst = oracle.gemm_check(host(c), ref, absr, FAST_ACCUM_SUM_COEF)
+    assert ok, f"worst |err|/bound = {worst}"
+    wide = torch.zeros(2, ld + 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fp8.Fp8mpError):
+        fp8.fp8_scaled_gemm_fast_accum(wide[:, :k], "e4m3", b_store[:2, :k], "e5m2", f32(sa), f32(sb), c[:2, :2])
