@@ -44,8 +44,15 @@ __device__ __forceinline__ uint32_t flat_bf16_body(const uint4* __restrict__ x, 
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t i = base + u * stride;
       if (i < nchunk) {
-        a[u] = __builtin_nontemporal_load(xv + 2 * i);
-        b[u] = __builtin_nontemporal_load(xv + 2 * i + 1);
+        if constexpr (HAS_Q) {
+          a[u] = __builtin_nontemporal_load(xv + 2 * i);
+          b[u] = __builtin_nontemporal_load(xv + 2 * i + 1);
+        } else {
+          // an amax-only pass is followed by the cast of the same source
+          // (just-in-time scaling): ordinary loads leave it in the MALL
+          a[u] = xv[2 * i];
+          b[u] = xv[2 * i + 1];
+        }
       } else {
         a[u] = u32x4{0, 0, 0, 0};
         b[u] = a[u];
