@@ -169,20 +169,28 @@ def cpu_baseline(w, inp, min_seconds: float = 10.0):
     g = w.gemms[0]
     x, wt = inp["X"], inp["W"]
     reps, total = 0, 0.0
+    stages = {"amax_cast": 0.0, "fp64_gemm": 0.0, "update": 0.0}
     while total < min_seconds and reps < 20:
         t0 = time.perf_counter()
         rx = oracle.DelayedScaling("e4m3", w.history_len, w.margin)
         rw = oracle.DelayedScaling("e4m3", w.history_len, w.margin)
         qx = rx.cast_step(x, "bf16")
         qw = rw.cast_step(wt, "bf16")
+        t1 = time.perf_counter()
         y = oracle.gemm_ref(qx, "e4m3", qw, "e4m3", rx.scale_inv, rw.scale_inv)
+        t2 = time.perf_counter()
         rx.update()
         rw.update()
-        total += time.perf_counter() - t0
+        t3 = time.perf_counter()
+        stages["amax_cast"] += t1 - t0
+        stages["fp64_gemm"] += t2 - t1
+        stages["update"] += t3 - t2
+        total += t3 - t0
         reps += 1
         del y
     flops = 2.0 * g.m * g.n * g.k
     return {"value": flops * reps / total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "stage_seconds_per_step": {k: round(v / reps, 4) for k, v in stages.items()},
             "sample": f"{reps} full oracle steps (amax, cast of X and W, FP64 GEMM {g.m}x{g.n}x{g.k}, "
                       f"update) in {total:.1f} s; elementwise stages single-threaded, BLAS on {threads} threads"}
 
@@ -294,6 +302,15 @@ def main():
     ocast_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
     upd_ms = sum(e[3].elapsed_time(e[4]) for e in ev) / K
 
+    def pct(vals):
+        v = sorted(vals)
+        at = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+        return {"p10": round(at(0.1), 4), "p50": round(at(0.5), 4), "p90": round(at(0.9), 4)}
+
+    step_pct = pct([e[0].elapsed_time(e[4]) for e in ev])
+    gemm_pct = pct([e[1].elapsed_time(e[2]) for e in ev])
+    cast_pct = pct([e[0].elapsed_time(e[1]) for e in ev])
+
     flops = plan.gemm_flops()
     n_gemm = len(plan.gemms)
     gemm_launch_ms = gemm_ms / n_gemm
@@ -359,7 +376,9 @@ def main():
             f"gemm_{other}_accum_frac_of_peak": round(other_tflops / (PEAK_FP8_MFMA_TFLOPS if other == "fast"
                                                                       else PEAK_BF16_MFMA_TFLOPS), 4),
         },
+        "percentiles_ms": {"step": step_pct, "gemm": gemm_pct, "cast": cast_pct},
         "device": info,
+        "rocm": {"hip": torch.version.hip, "torch": torch.__version__},
     }
     if args.output_cast != "none":
         out["components"]["output_cast"] = args.output_cast
