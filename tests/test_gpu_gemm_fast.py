@@ -251,3 +251,34 @@ def test_fast_gemm_at_the_largest_leading_dimension():
     wide = torch.zeros(2, ld + 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(fp8.Fp8mpError):
         fp8.fp8_scaled_gemm_fast_accum(wide[:, :k], "e4m3", b_store[:2, :k], "e5m2", f32(sa), f32(sb), c[:2, :2])
+
+
+def test_layer_plan_fast_accum_tiny_recipe():
+    """The 16-step tiny workload (fp32 X and W, E4M3, history 16) through LayerPlan(gemm_accum="fast"):
+    codes, amax histories and scales bit for bit with the oracle's delayed recipe at every step (the
+    GEMM mode does not touch them), the GEMM within the fast bound."""
+    require_gpu()
+    import workloads as wl
+    from fp8_mixed_precision_cast_amd.linear import plan_from_workload
+    w = wl.BY_NAME["tiny_fwd_256"]
+    inp = wl.load(w.name)
+    xs = wl.tiny_step_inputs(inp["X"], wl.step_factors(w.config_id, w.steps))
+    plan = plan_from_workload(w, gemm_accum="fast")
+    recs = {n: oracle.DelayedScaling("e4m3", w.history_len, w.margin) for n in ("X", "W")}
+    wd = torch.from_numpy(inp["W"]).cuda()
+    for t, xt in enumerate(xs):
+        banner("plan-fast tiny step", t)
+        plan.step({"X": torch.from_numpy(xt).cuda(), "W": wd})
+        qx = recs["X"].cast_step(xt, "f32")
+        qw = recs["W"].cast_step(inp["W"], "f32")
+        assert np.array_equal(host(plan.q["X"]), qx), f"step {t}: X codes"
+        assert np.array_equal(host(plan.q["W"]), qw), f"step {t}: W codes"
+        ref = oracle.gemm_ref(qx, "e4m3", qw, "e4m3", recs["X"].scale_inv, recs["W"].scale_inv)
+        absr = oracle.gemm_abs_ref(qx, "e4m3", qw, "e4m3", recs["X"].scale_inv, recs["W"].scale_inv)
+        ok, worst = oracle.gemm_check(host(plan.out["fwd"].view(torch.int16)), ref, absr, FAST_ACCUM_SUM_COEF)
+        assert ok, f"step {t}: worst |err|/bound = {worst}"
+        for n, r in recs.items():
+            r.update()
+            st = plan.state[n]
+            assert np.array_equal(host(st.history).view(np.uint32), r.history.view(np.uint32)), (t, n)
+            assert host(st.scale)[0] == r.scale and host(st.scale_inv)[0] == r.scale_inv, (t, n)

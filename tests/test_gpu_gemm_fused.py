@@ -132,10 +132,11 @@ def test_fused_full_size_mlp_shape():
     assert ok, worst
 
 
-def test_layer_plan_output_cast_fused_equals_separate():
+@pytest.mark.parametrize("accum", ["exact", "fast"])
+def test_layer_plan_output_cast_fused_equals_separate(accum):
     """A chained layer step: the fused output cast, the separate second pass and the fused cast without
     the BF16 output give the same codes, histories and scales, and the codes are the oracle's cast of
-    the BF16 output with the delayed scale."""
+    the BF16 output with the delayed scale; under either GEMM accumulation."""
     require_gpu()
     from fp8_mixed_precision_cast_amd.linear import GemmOp, LayerPlan, OperandSpec
     import workloads as wl
@@ -144,8 +145,8 @@ def test_layer_plan_output_cast_fused_equals_separate():
     inp = {"X": dev(x), "W": dev(w)}
     ops = [OperandSpec("X", (300, 256), "e4m3"), OperandSpec("W", (520, 256), "e4m3")]
     gem = [GemmOp("fwd", "X", False, "W", False)]
-    plans = {mode: LayerPlan(ops, gem, history_len=8, output_cast=mode) for mode in ("fused", "separate",
-                                                                                     "fused_codes")}
+    plans = {mode: LayerPlan(ops, gem, history_len=8, output_cast=mode, gemm_accum=accum)
+             for mode in ("fused", "separate", "fused_codes")}
     plans["fused_codes"].out["fwd"].view(torch.int16).fill_(0x1234)   # never stored in that mode
     for mode, plan in plans.items():
         banner("plan-output-cast", mode)
@@ -154,7 +155,7 @@ def test_layer_plan_output_cast_fused_equals_separate():
         for mode, plan in plans.items():
             ys = plan.ystate["fwd"]
             s_before = host(ys.scale)[0]
-            banner("plan-output-cast", mode, step)
+            banner("plan-output-cast", accum, mode, step)
             plan.step(inp)
             if mode == "fused_codes":
                 assert (host(plan.out["fwd"].view(torch.int16)) == 0x1234).all(), "BF16 output stored"
