@@ -223,14 +223,14 @@ def other_gemm_tflops(plan, accum: str, iters: int = 20) -> float:
     import fp8_mixed_precision_cast_amd as fp8
     call = fp8.fp8_scaled_gemm_fast_accum if accum == "fast" else fp8.fp8_scaled_gemm
     stream = torch.cuda.current_stream()
-    outs = [torch.empty_like(c) for (_, _, _, _, _, _, c) in plan._gemm_args]
+    outs = [torch.empty_like(c) for (_, _, _, _, _, _, c) in plan.gemm_operands()]
     for _ in range(3):
-        for (a, af, b, bf, sa, sb, _), c in zip(plan._gemm_args, outs):
+        for (a, af, b, bf, sa, sb, _), c in zip(plan.gemm_operands(), outs):
             call(a, af, b, bf, sa, sb, c)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(iters):
-        for (a, af, b, bf, sa, sb, _), c in zip(plan._gemm_args, outs):
+        for (a, af, b, bf, sa, sb, _), c in zip(plan.gemm_operands(), outs):
             call(a, af, b, bf, sa, sb, c)
     e1.record(stream)
     torch.cuda.synchronize()

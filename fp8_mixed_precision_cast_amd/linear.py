@@ -213,6 +213,11 @@ class LayerPlan:
         self.output_cast_all(stream)
         self.update_all(stream)
 
+    def gemm_operands(self) -> List[tuple]:
+        """Per GEMM: (a codes, a format, b codes, b format, a scale_inv, b scale_inv, BF16 output), the
+        arguments the step passes to the GEMM call."""
+        return list(self._gemm_args)
+
     def gemm_flops(self) -> int:
         return sum(2 * a.shape[0] * b.shape[0] * a.shape[1] for a, _, b, _, _, _, _ in self._gemm_args)
 
