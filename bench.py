@@ -8,7 +8,7 @@ default workload is the 7B-class MLP up-projection (X[4096x4096] BF16 with
 0.1% outliers x20, W[11008x4096] BF16 N(0, 0.02); GEMM M=4096, N=11008,
 K=4096; amax history 1024, margin 0).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mlp7b_up_fwd]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp7b_up_fwd]
 
 Prints one JSON line. `value` is the step's GEMM FLOPs divided by the
 measured step time (TFLOP/s, higher is better); `roofline` describes the
@@ -35,8 +35,8 @@ PEAK_FP8_MFMA_TFLOPS = 5000.0   # dense
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mlp7b_up_fwd")
     ap.add_argument("--recipe", default="delayed", choices=["delayed", "current"],
                     help="delayed scaling (the pages' default recipe) or just-in-time scaling")
