@@ -10,11 +10,14 @@ K=4096; amax history 1024, margin 0).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp7b_up_fwd]
 
-Prints one JSON line. `value` is the step's GEMM FLOPs divided by the
-measured step time (TFLOP/s, higher is better); `roofline` describes the
-dominant kernel (the GEMM) from HIP events recorded around every launch in the
-timed region; `components` gives the cast kernels' GB/s against HBM;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Prints one JSON line. After W warm-up steps, K eager steps are timed with HIP
+events around every phase on the launch stream; they give `roofline` (the
+dominant kernel, the GEMM, per launch) and the per-phase `components`. Then the
+step is captured once as a HIP graph and K replays are timed, synchronized on
+both sides: `value` is the step's GEMM FLOPs divided by that step time (TFLOP/s,
+higher is better; `--no-graph` takes the eager steps instead, and the eager
+figure is reported either way). `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -48,6 +51,9 @@ def parse():
     ap.add_argument("--gemm-accum", default="exact", choices=["exact", "fast"],
                     help="exact: FP32 accumulation (BF16 MFMA on exactly widened FP8); fast: the FP8 MFMA's own "
                          "reduced-precision accumulation (within 2^-9 of sum|a*b|)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager steps only (by default the timed steps are replays of the step captured "
+                         "as a HIP graph, after the eager steps that give the per-kernel figures)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
@@ -216,6 +222,27 @@ def cold_cast_gbps(plan, dinp, reps: int = 5):
     return plan.cast_bytes(dinp) / (ms * 1e-3) / 1e9, ms
 
 
+def graph_steps(plan, dinp, steps: int):
+    """The step captured once as a HIP graph and replayed `steps` times, synchronized on both sides.
+    Returns (wall seconds per replay, per-replay milliseconds from HIP events recorded between the
+    replays on the launch stream)."""
+    import torch
+    g = plan.capture(dinp)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        g.replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
 def other_gemm_tflops(plan, accum: str, iters: int = 20) -> float:
     """The plan's GEMMs, on the codes of the last step, in the other accumulation mode: TFLOP/s per
     launch from HIP events around iters rounds (outside the timed steps)."""
@@ -319,6 +346,12 @@ def main():
     cast_bytes = plan.cast_bytes(dinp)
     cast_gbps = cast_bytes / (cast_ms * 1e-3) / 1e9
 
+    eager_step_s = step_s
+    if args.no_graph:
+        graph_pct = None
+    else:
+        step_s, graph_ms = graph_steps(plan, dinp, K)
+        graph_pct = pct(graph_ms)
     cold_gbps, cold_ms = cold_cast_gbps(plan, dinp)
     other = "fast" if args.gemm_accum == "exact" else "exact"
     other_tflops = other_gemm_tflops(plan, other)
@@ -359,6 +392,7 @@ def main():
                    "transposed_casts": list(w.transposed), "history_len": w.history_len, "margin": w.margin,
                    "recipe": args.recipe, "output_cast": args.output_cast, "layernorm_x": bool(args.layernorm),
                    "gemm_accum": args.gemm_accum,
+                   "step_launch": "eager" if args.no_graph else "hip_graph",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
@@ -372,11 +406,13 @@ def main():
             "cast_frac_of_hbm": round(cast_gbps / PEAK_HBM_GBPS, 4),
             "scale_update_ms": round(upd_ms, 4),
             "cast_cold_ms": round(cold_ms, 4), "cast_cold_gbps": round(cold_gbps, 1),
+            "eager_ms_per_step": round(eager_step_s * 1e3, 4),
+            "eager_step_tflops": round(flops / eager_step_s / 1e12, 3),
             f"gemm_{other}_accum_tflops": round(other_tflops, 2),
             f"gemm_{other}_accum_frac_of_peak": round(other_tflops / (PEAK_FP8_MFMA_TFLOPS if other == "fast"
                                                                       else PEAK_BF16_MFMA_TFLOPS), 4),
         },
-        "percentiles_ms": {"step": step_pct, "gemm": gemm_pct, "cast": cast_pct},
+        "percentiles_ms": {"step": graph_pct or step_pct, "eager_step": step_pct, "gemm": gemm_pct, "cast": cast_pct},
         "device": info,
         "rocm": {"hip": torch.version.hip, "torch": torch.__version__},
     }

@@ -213,6 +213,18 @@ class LayerPlan:
         self.output_cast_all(stream)
         self.update_all(stream)
 
+    def capture(self, inputs: Dict[str, torch.Tensor]) -> "torch.cuda.CUDAGraph":
+        """One step captured as a HIP graph (through torch's graph API): replaying it runs the step's
+        launches without host launch overhead or gaps between kernels. The graph reads `inputs` and
+        writes the plan's buffers at the addresses they have now; every replay advances the recipe by
+        one step, like step(). The step issues only kernel launches (no memset or copy nodes). Call
+        prime() (and, for the batched cast, one eager step) first, so nothing is allocated during
+        capture."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(inputs)
+        return g
+
     def gemm_operands(self) -> List[tuple]:
         """Per GEMM: (a codes, a format, b codes, b format, a scale_inv, b scale_inv, BF16 output), the
         arguments the step passes to the GEMM call."""

@@ -17,6 +17,6 @@ def test_help_lists_the_workload_switches():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0
-    for flag in ("--steps", "--warmup", "--workload", "--recipe", "--output-cast", "--layernorm", "--gemm-accum", "--gemm-data",
+    for flag in ("--steps", "--warmup", "--workload", "--recipe", "--output-cast", "--layernorm", "--gemm-accum", "--no-graph", "--gemm-data",
                  "--copy-reference"):
         assert flag in r.stdout

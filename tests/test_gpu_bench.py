@@ -33,6 +33,11 @@ def test_bench_line_contract(monkeypatch, capsys):
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert roof["peak"] == 2500.0 and line["components"]["gemm_fast_accum_tflops"] > 0
+    assert line["config"]["step_launch"] == "hip_graph"
+    assert 0 < line["ms_per_step"] and 0 < line["components"]["eager_ms_per_step"]
+    (eager,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--no-graph")
+    assert eager["config"]["step_launch"] == "eager"
+    assert eager["ms_per_step"] == eager["components"]["eager_ms_per_step"]
     pc = line["percentiles_ms"]["step"]
     assert 0 < pc["p10"] <= pc["p50"] <= pc["p90"] and line["rocm"]["hip"]
     (fast,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--gemm-accum", "fast")
