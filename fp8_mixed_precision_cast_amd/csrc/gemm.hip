@@ -136,6 +136,9 @@ static_assert(kBM == kBN, "one copy geometry serves both operands");
 // kOutOfRange lies above all of them.
 static_assert(kBM * kGemmMaxLd <= (int64_t(1) << 30), "tile span must fit 32-bit offsets");
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+// s_waitcnt operand (gfx9 encoding): vmcnt = 0, expcnt and lgkmcnt left at
+// their maxima (not waited on).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // The buffer resource starts at the tile's first row, so operands of any size
 // are addressed with 32-bit offsets.
@@ -347,11 +350,15 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     load_tile(cb, 0, Ku, smem + kTileBytes, wave);
   }
   // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
-  // step kt + 1. The barrier at the top of a step both publishes the stage to
-  // be read and retires every read of the stage about to be overwritten.
+  // step kt + 1. At the top of a step each thread waits for its own copies
+  // into the stage to be read (buffer-to-LDS loads count in vmcnt; the wait
+  // is written out because the compiler does not insert it in every
+  // instantiation of such a loop), and the barrier then both publishes the
+  // stage and retires every read of the stage about to be overwritten.
   for (int kt = 0; kt < nk; ++kt) {
     uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
     uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     pipelined_step<FA, FB, ACC>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn, wave, lane);
   }
