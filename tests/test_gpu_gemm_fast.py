@@ -170,6 +170,36 @@ def test_fast_gemm_full_7b_shape_sampled():
     assert rel < 2.0 ** -7
 
 
+def test_gemm_full_7b_shape_every_output_and_repeatable():
+    """The bench's GEMM launch (4096 x 11008 x 4096: 688 tiles, every CU busy for three rounds) on
+    +-2**e rows, where every sum is exact in both modes: every output of both modes within the FP32
+    bound against the oracle, the fast GEMM's bits equal to the FP32 GEMM's, and three calls of each
+    give the same bits. A K step read before its buffer-to-LDS copies have landed (which only a
+    fully loaded chip shows) makes outputs wrong or vary from call to call."""
+    require_gpu()
+    m, n, k = 4096, 11008, 4096
+    rng = np.random.default_rng(77)
+    a, b = _pow2_rows(rng, (m, k), "e4m3"), _pow2_rows(rng, (n, k), "e4m3")
+    sa, sb = np.float32(0.75), np.float32(2.0 ** -3)
+    da, db = dev(a), dev(b)
+    outs = {}
+    for name, call in (("exact", fp8.fp8_scaled_gemm), ("fast", fp8.fp8_scaled_gemm_fast_accum)):
+        banner("gemm-7b-every-output", name)
+        ys = []
+        for _ in range(3):
+            c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+            call(da, "e4m3", db, "e4m3", f32(sa), f32(sb), c)
+            ys.append(host(c))
+        for y in ys[1:]:
+            assert np.array_equal(y, ys[0]), f"{name}: calls differ: " + first_diff(y, ys[0])
+        outs[name] = ys[0]
+    assert np.array_equal(outs["fast"], outs["exact"]), first_diff(outs["fast"], outs["exact"])
+    ref = oracle.gemm_ref(a, "e4m3", b, "e4m3", sa, sb)
+    absr = oracle.gemm_abs_ref(a, "e4m3", b, "e4m3", sa, sb)
+    ok, worst = oracle.gemm_check(outs["exact"], ref, absr)
+    assert ok, f"worst |err|/bound (FP32 bound) = {worst}"
+
+
 def test_fast_gemm_non_finite_codes_propagate():
     """NaN codes (E4M3 0x7F / 0xFF) give NaN rows and columns, and an E5M2 +-Inf code gives +-Inf
     (or NaN against a zero), exactly as the oracle's float64 sum does; the rest stays within the
