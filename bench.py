@@ -55,6 +55,7 @@ def parse():
                     help="time the eager steps only (by default the timed steps are replays of the step captured "
                          "as a HIP graph, after the eager steps that give the per-kernel figures)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the clock window (amdsmi)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (JSON), if present")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
@@ -169,9 +170,11 @@ def cpu_baseline(w, inp, min_seconds: float = 10.0):
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info})) or "unknown"
     except Exception:
-        threads = 1
+        threads, blas = 1, "unknown"
     g = w.gemms[0]
     x, wt = inp["X"], inp["W"]
     reps, total = 0, 0.0
@@ -196,6 +199,7 @@ def cpu_baseline(w, inp, min_seconds: float = 10.0):
         del y
     flops = 2.0 * g.m * g.n * g.k
     return {"value": flops * reps / total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
             "stage_seconds_per_step": {k: round(v / reps, 4) for k, v in stages.items()},
             "sample": f"{reps} full oracle steps (amax, cast of X and W, FP64 GEMM {g.m}x{g.n}x{g.k}, "
                       f"update) in {total:.1f} s; elementwise stages single-threaded, BLAS on {threads} threads"}
@@ -264,6 +268,151 @@ def other_gemm_tflops(plan, accum: str, iters: int = 20) -> float:
     return plan.gemm_flops() * iters / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
+class ClockSampler:
+    """Samples the GPU's graphics (SCLK) and memory (MCLK) clocks and the socket power through the amdsmi
+    library while the step runs: a background thread polls the device's metrics table. Reports the
+    median, min and max of what it saw, or the reason it could not read them."""
+
+    def __init__(self):
+        self.samples, self.error, self._stop, self._thread, self._h, self._smi = [], None, False, None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handle")
+            self._h = handles[0]
+            if len(handles) > 1:
+                import torch
+                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+                for h in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        self._h = h
+            self._smi = amdsmi
+        except Exception as e:  # the numbers are context; their absence is reported, not fatal
+            self.error = f"{type(e).__name__}: {str(e)[:100]}"
+
+    def _poll(self):
+        smi = self._smi
+        while not self._stop:
+            try:
+                m = smi.amdsmi_get_gpu_metrics_info(self._h)
+                g = m.get("current_gfxclks")
+                gfx = [v for v in g if isinstance(v, (int, float))] if isinstance(g, (list, tuple)) else []
+                if not gfx and isinstance(m.get("current_gfxclk"), (int, float)):
+                    gfx = [m["current_gfxclk"]]
+                uclk = m.get("current_uclk")
+                pw = m.get("current_socket_power", m.get("average_socket_power"))
+                self.samples.append((sum(gfx) / len(gfx) if gfx else None,
+                                     uclk if isinstance(uclk, (int, float)) else None,
+                                     pw if isinstance(pw, (int, float)) else None))
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {str(e)[:100]}"
+                return
+            time.sleep(0.002)
+
+    def __enter__(self):
+        if self._smi is not None:
+            import threading
+            self._thread = threading.Thread(target=self._poll, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def summary(self):
+        def stats(vals):
+            v = sorted(x for x in vals if x is not None)
+            if not v:
+                return None
+            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1]}
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        return {"samples": len(self.samples), "sclk_mhz": stats(s[0] for s in self.samples),
+                "mclk_mhz": stats(s[1] for s in self.samples), "socket_power_w": stats(s[2] for s in self.samples),
+                "source": "amdsmi gpu metrics, polled every 2 ms during the clock window"}
+
+
+def parity(w, inp, plan, n_updates: int, recorded_after: bool, fast: bool, seed: int = 7):
+    """Parity of what the timed steps left in the plan against the oracle, outside the timed region.
+    Under the delayed recipe with plain operands, every step casts the same data, so after n_updates
+    updates the oracle's recipe (record amax, update, n_updates times; one more record when casts
+    ran after the last update) gives the history, scale and scale_inv, which must match bit for bit;
+    the codes of sampled rows of every tensor must equal the oracle's cast with that scale; a
+    sampled block of every GEMM's output is graded against the oracle's FP64 GEMM on the oracle's
+    codes under the FP32-accumulation bound (and, for the fast GEMM, its own bound)."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle.gemm import FAST_ACCUM_SUM_COEF
+    rng = np.random.default_rng(seed)
+    res = {"checked": [], "ok": True}
+
+    def fail(msg):
+        res["ok"] = False
+        res.setdefault("failures", []).append(msg)
+
+    used = {}
+    for t in w.tensors:
+        fmt = w.formats[t.name]
+        x = inp[t.name]
+        rec = oracle.DelayedScaling(fmt, w.history_len, w.margin)
+        a = oracle.amax(x, t.dtype)
+        for _ in range(n_updates):
+            rec.record(a)
+            rec.update()
+        if recorded_after:
+            rec.record(a)
+        used[t.name] = (rec.scale, rec.scale_inv)
+        st = plan.state[t.name]
+        hist = st.history.cpu().numpy().view(np.uint32)
+        if not np.array_equal(hist, rec.history.view(np.uint32)):
+            fail(f"{t.name}: history")
+        if st.scale.cpu().numpy().view(np.uint32)[0] != np.float32(rec.scale).view(np.uint32):
+            fail(f"{t.name}: scale")
+        if st.scale_inv.cpu().numpy().view(np.uint32)[0] != np.float32(rec.scale_inv).view(np.uint32):
+            fail(f"{t.name}: scale_inv")
+        rows = np.unique(np.concatenate([[0, x.shape[0] - 1], rng.choice(x.shape[0], 62, replace=False)]))
+        got = plan.q[t.name][torch.from_numpy(rows).cuda()].cpu().numpy()
+        if not np.array_equal(got, oracle.cast(x[rows], rec.scale, fmt, t.dtype)):
+            fail(f"{t.name}: codes of sampled rows")
+        if plan.qt[t.name] is not None and not torch.equal(plan.qt[t.name], plan.q[t.name].t()):
+            fail(f"{t.name}: q_t != q^T")
+        res["checked"].append(f"{t.name}: history, scale, scale_inv bit-exact; {rows.size} code rows exact")
+    for g in w.gemms:
+        ii = np.unique(np.concatenate([[0, g.m - 1], rng.choice(g.m, 62, replace=False)]))
+        jj = np.unique(np.concatenate([[0, g.n - 1], rng.choice(g.n, 62, replace=False)]))
+
+        def rows_of(name, transposed, idx):
+            x = inp[name]
+            src = np.ascontiguousarray(x[:, idx].T) if transposed else x[idx]
+            return oracle.cast(src, used[name][0], w.formats[name], w.tensor(name).dtype)
+
+        qa, qb = rows_of(g.a, g.a_transposed, ii), rows_of(g.b, g.b_transposed, jj)
+        sa, sb = used[g.a][1], used[g.b][1]
+        ref = oracle.gemm_ref(qa, g.a_fmt, qb, g.b_fmt, sa, sb)
+        absr = oracle.gemm_abs_ref(qa, g.a_fmt, qb, g.b_fmt, sa, sb)
+        y = plan.out[g.name].view(torch.int16)[torch.from_numpy(ii).cuda()][:, torch.from_numpy(jj).cuda()]
+        yb = y.cpu().numpy().view(np.uint16)
+        ok32, worst32 = oracle.gemm_check(yb, ref, absr)
+        entry = {"gemm": g.name, "block": [int(ii.size), int(jj.size)], "fp32_bound_ok": ok32,
+                 "fp32_bound_worst": round(worst32, 4)}
+        if fast:
+            okf, worstf = oracle.gemm_check(yb, ref, absr, FAST_ACCUM_SUM_COEF)
+            entry.update({"fast_bound_ok": okf, "fast_bound_worst": round(worstf, 4)})
+            if not okf:
+                fail(f"{g.name}: outside the fast-accumulation bound")
+        elif not ok32:
+            fail(f"{g.name}: outside the FP32-accumulation bound")
+        res["checked"].append(entry)
+    return res
+
+
 def main():
     args = parse()
     if args.copy_reference:
@@ -301,8 +450,10 @@ def main():
                               gemm_accum=args.gemm_accum)
     stream = torch.cuda.current_stream()
     plan.prime(dinp)
+    n_updates = 1
     for _ in range(args.warmup):
         plan.step(dinp)
+    n_updates += args.warmup
     torch.cuda.synchronize()
 
     K = args.steps
@@ -322,6 +473,7 @@ def main():
         e[4].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    n_updates += K
 
     step_s = (t1 - t0) / K
     cast_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
@@ -351,7 +503,21 @@ def main():
         graph_pct = None
     else:
         step_s, graph_ms = graph_steps(plan, dinp, K)
+        n_updates += 3 + K
         graph_pct = pct(graph_ms)
+    # Clocks: the step repeated for about half a second (outside the timed region) while the
+    # sampler polls the device's metrics.
+    clocks = None
+    if not args.no_clocks:
+        sampler = ClockSampler()
+        reps = max(1, int(0.5 / max(step_s, 1e-4)))
+        with sampler:
+            for _ in range(reps):
+                plan.step(dinp)
+            torch.cuda.synchronize()
+        n_updates += reps
+        clocks = sampler.summary()
+        clocks["steps"] = reps
     cold_gbps, cold_ms = cold_cast_gbps(plan, dinp)
     other = "fast" if args.gemm_accum == "exact" else "exact"
     other_tflops = other_gemm_tflops(plan, other)
@@ -363,7 +529,9 @@ def main():
         if t.get("gemm_source") == source_digest():
             traffic = t.get("gemm_bytes_per_launch")
     fast = args.gemm_accum == "fast"
-    peak = PEAK_FP8_MFMA_TFLOPS if fast else PEAK_BF16_MFMA_TFLOPS
+    # The roofline is the FP8 dense MFMA peak in both modes. The exact mode runs the BF16 MFMA on
+    # exactly widened codes, whose own ceiling (half of it) is reported beside it.
+    peak = PEAK_FP8_MFMA_TFLOPS
 
     g = w.gemms[0]
 
@@ -399,7 +567,9 @@ def main():
                      "traffic": traffic,
                      "kernel": ("gemm_fp8_kernel (fp8 MFMA, fast accumulation)" if fast else
                                 "gemm_fp8_kernel (bf16 MFMA on widened FP8)"),
-                     "frac_of_fp8_mfma_peak": round(gemm_tflops / PEAK_FP8_MFMA_TFLOPS, 4)},
+                     "instruction_peak": PEAK_FP8_MFMA_TFLOPS if fast else PEAK_BF16_MFMA_TFLOPS,
+                     "frac_of_instruction_peak": round(gemm_tflops / (PEAK_FP8_MFMA_TFLOPS if fast else
+                                                                      PEAK_BF16_MFMA_TFLOPS), 4)},
         "components": {
             "gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(gemm_tflops, 2),
             "cast_ms": round(cast_ms, 4), "cast_bytes": cast_bytes, "cast_gbps": round(cast_gbps, 1),
@@ -414,15 +584,26 @@ def main():
         },
         "percentiles_ms": {"step": graph_pct or step_pct, "eager_step": step_pct, "gemm": gemm_pct, "cast": cast_pct},
         "device": info,
+        "clocks": clocks,
         "rocm": {"hip": torch.version.hip, "torch": torch.__version__},
     }
     if args.output_cast != "none":
         out["components"]["output_cast"] = args.output_cast
         out["components"]["output_cast_bytes"] = plan.output_cast_bytes()
         out["components"]["separate_output_cast_ms"] = round(ocast_ms, 4)
+    ok = True
+    if args.recipe == "delayed" and not args.layernorm and args.output_cast == "none":
+        out["parity"] = parity(w, inp, plan, n_updates, True, fast)
+        ok = out["parity"]["ok"]
+    else:
+        out["parity"] = {"skipped": "checked for the delayed recipe on plain operands; the other options "
+                                    "are covered by the GPU tests"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
+    if not ok:
+        print("parity check failed: " + "; ".join(out["parity"].get("failures", [])), file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -330,7 +330,21 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int nk = (int)((K + kBK - 1) / kBK);
   const uint32_t Ku = (uint32_t)K;
-  const float s = *sa * *sb;
+  // The output is (acc * s1) * s2. Normally s1 = sa_inv * sb_inv and s2 = 1 (one rounding of the
+  // scale, and multiplying by 1 is exact). When that product overflows or underflows binary32 while
+  // acc * sa_inv * sb_inv may still be representable, the two factors are applied one at a time:
+  // the smaller first when the product is too large (both exceed 1), the larger first when it is
+  // too small.
+  const float sa_v = *sa, sb_v = *sb, s_ab = sa_v * sb_v;
+  float s1 = s_ab, s2 = 1.0f;
+  if (!(__builtin_fabsf(s_ab) >= 1.17549435e-38f && __builtin_fabsf(s_ab) <= 3.40282347e38f) && s_ab == s_ab &&
+      sa_v != 0.0f && sb_v != 0.0f) {
+    const bool a_big = __builtin_fabsf(sa_v) >= __builtin_fabsf(sb_v);
+    const float big = a_big ? sa_v : sb_v, small = a_big ? sb_v : sa_v;
+    const bool too_large = __builtin_fabsf(s_ab) > 1.0f;
+    s1 = too_large ? small : big;
+    s2 = too_large ? big : small;
+  }
   const bool vec = ((reinterpret_cast<uintptr_t>(C) | (uintptr_t)(ldc * 2)) & 15) == 0;
   const bool do_c = YF == kNoY || C != nullptr;   // the fused call may skip the BF16 output
 
@@ -381,8 +395,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
         for (int q = 0; q < 4; ++q) {
           const int chunk = (wn * kWN + j * 32 + 8 * q) >> 3;
           const v16f& a = acc.v[i][j];
-          const uint2 v = {pack_bf16(a[4 * q] * s, a[4 * q + 1] * s),
-                           pack_bf16(a[4 * q + 2] * s, a[4 * q + 3] * s)};
+          const uint2 v = {pack_bf16((a[4 * q] * s1) * s2, (a[4 * q + 1] * s1) * s2),
+                           pack_bf16((a[4 * q + 2] * s1) * s2, (a[4 * q + 3] * s1) * s2)};
           *reinterpret_cast<uint2*>(rp + ((chunk ^ (row & 31)) << 4)) = v;
         }
     }

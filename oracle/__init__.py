@@ -46,7 +46,7 @@ test under tests/):
 from .codec import (FMT, FP8Format, decode, decode_table, encode, encode_scalar,
                     bf16_to_f32)
 from .recipe import (amax, cast, DelayedScaling, max_nan, primed_scale, update_scale, update_scale_fmax)
-from .gemm import gemm_ref, gemm_abs_ref, gemm_bound, gemm_check, gemm_entry
+from .gemm import gemm_ref, gemm_abs_ref, gemm_bound, gemm_check, gemm_entry, gemm_ratio
 from .layernorm import layer_norm_bound, layer_norm_check, layer_norm_ref
 from .allreduce import reduce_bound, reduce_check, reduce_ref, shared_scale
 from .adam import (adam_step_f64, adam_step_ref, adam_weight_codes_ref, f16_decode, f16_encode,
@@ -55,7 +55,7 @@ from .adam import (adam_step_f64, adam_step_ref, adam_weight_codes_ref, f16_deco
 __all__ = [
     "FMT", "FP8Format", "decode", "decode_table", "encode", "encode_scalar", "bf16_to_f32",
     "amax", "cast", "DelayedScaling", "max_nan", "primed_scale", "update_scale", "update_scale_fmax",
-    "gemm_ref", "gemm_abs_ref", "gemm_bound", "gemm_check", "gemm_entry",
+    "gemm_ref", "gemm_abs_ref", "gemm_bound", "gemm_check", "gemm_entry", "gemm_ratio",
     "layer_norm_ref", "layer_norm_bound", "layer_norm_check",
     "shared_scale", "reduce_ref", "reduce_bound", "reduce_check",
     "adam_step_ref", "adam_step_f64", "adam_weight_codes_ref", "f16_encode", "f16_decode", "update_fp16_scale",

@@ -75,29 +75,43 @@ def bf16_bits_to_f64(y_bits) -> np.ndarray:
     return y.view(np.float32).astype(np.float64)
 
 
-def gemm_check(y_bits, y_ref, abs_ref, sum_coef=SUM_COEF):
-    """Grade BF16 output bits against the reference.
+def gemm_ratio(y_bits, y_ref, abs_ref, sum_coef=SUM_COEF) -> np.ndarray:
+    """|y - y_ref| / bound for every entry (float64, the shape of y_ref).
 
-    Returns (ok, worst) where worst is the largest |y - y_ref| / bound over the
-    finite entries. Non-finite references (NaN or Inf codes among the operands)
-    must be matched exactly in kind. sum_coef is the coefficient of
-    sum_k |a_k b_k| in the bound: SUM_COEF for FP32 accumulation,
-    FAST_ACCUM_SUM_COEF for fast accumulation.
+    A finite reference with a zero bound gives 0 when y equals it and inf
+    otherwise. A non-finite reference (NaN or Inf codes among the operands)
+    gives 0 when y matches it in kind (NaN for NaN, the same infinity) and inf
+    otherwise. An entry is within the tolerance exactly when its ratio is <= 1.
     """
     y = bf16_bits_to_f64(y_bits)
     y_ref = np.asarray(y_ref, dtype=np.float64)
+    abs_ref = np.asarray(abs_ref, dtype=np.float64)
+    ratio = np.zeros(y_ref.shape, np.float64)
     fin = np.isfinite(y_ref)
-    ok = True
     if (~fin).any():
         yr, yy = y_ref[~fin], y[~fin]
         same = (np.isnan(yr) & np.isnan(yy)) | (yr == yy)
-        ok = bool(same.all())
-    bound = gemm_bound(y_ref[fin], np.asarray(abs_ref, dtype=np.float64)[fin], sum_coef)
-    err = np.abs(y[fin] - y_ref[fin])
-    if err.size == 0:
-        return ok, 0.0
-    if not np.isfinite(err).all():
-        return False, float("inf")
-    ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
-    worst = float(ratio.max())
-    return ok and worst <= 1.0, worst
+        ratio[~fin] = np.where(same, 0.0, np.inf)
+    bound = gemm_bound(y_ref[fin], abs_ref[fin], sum_coef)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(y[fin] - y_ref[fin])
+    err = np.where(np.isfinite(err), err, np.inf)
+    safe = np.where(bound > 0, bound, 1.0)
+    ratio[fin] = np.where(bound > 0, err / safe, np.where(err > 0, np.inf, 0.0))
+    return ratio
+
+
+def gemm_check(y_bits, y_ref, abs_ref, sum_coef=SUM_COEF):
+    """Grade BF16 output bits against the reference.
+
+    Returns (ok, worst): ok when every entry is within the tolerance (see
+    gemm_ratio), worst the largest |y - y_ref| / bound over the entries with a
+    finite reference (0.0 when there are none). sum_coef is the coefficient of
+    sum_k |a_k b_k| in the bound: SUM_COEF for FP32 accumulation,
+    FAST_ACCUM_SUM_COEF for fast accumulation.
+    """
+    ratio = gemm_ratio(y_bits, y_ref, abs_ref, sum_coef)
+    fin = np.isfinite(np.asarray(y_ref, dtype=np.float64))
+    ok = bool((ratio <= 1.0).all())
+    worst = float(ratio[fin].max()) if fin.any() else 0.0
+    return ok, worst

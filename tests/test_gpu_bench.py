@@ -32,7 +32,13 @@ def test_bench_line_contract(monkeypatch, capsys):
     roof = line["roofline"]
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
-    assert roof["peak"] == 2500.0 and line["components"]["gemm_fast_accum_tflops"] > 0
+    assert roof["peak"] == 5000.0 and roof["instruction_peak"] == 2500.0
+    assert line["components"]["gemm_fast_accum_tflops"] > 0
+    par = line["parity"]
+    assert par["ok"] and len(par["checked"]) == 3, par
+    assert par["checked"][-1]["fp32_bound_ok"]
+    clk = line["clocks"]
+    assert clk is not None and ("sclk_mhz" in clk or "error" in clk)
     assert line["config"]["step_launch"] == "hip_graph"
     assert 0 < line["ms_per_step"] and 0 < line["components"]["eager_ms_per_step"]
     (eager,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--no-graph")
@@ -42,6 +48,8 @@ def test_bench_line_contract(monkeypatch, capsys):
     assert 0 < pc["p10"] <= pc["p50"] <= pc["p90"] and line["rocm"]["hip"]
     (fast,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--gemm-accum", "fast")
     assert fast["config"]["gemm_accum"] == "fast" and fast["roofline"]["peak"] == 5000.0
+    assert fast["roofline"]["instruction_peak"] == 5000.0 and fast["parity"]["ok"]
+    assert fast["parity"]["checked"][-1]["fast_bound_ok"]
     assert fast["components"]["gemm_exact_accum_tflops"] > 0
 
 

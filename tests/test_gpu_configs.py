@@ -3,10 +3,11 @@
 Every workload runs the hot path as the benchmark does (LayerPlan: fused
 amax+cast(+transpose) of every operand, the GEMMs, the scale updates). The
 tiny workload is checked in full for all 16 delayed-scaling steps. The large
-ones are checked at full size on what the oracle can compute piece by piece:
-amax, scales and history exactly; sampled rows and columns of the codes
-exactly; q_t == q^T on the device for every element; and a sampled block of
-every GEMM's output against the oracle's FP64 result on the oracle's own codes.
+ones are checked in full at full size: amax, scales and history exactly; every
+code of every tensor exactly (q_t == q^T on the device); and every output of
+every GEMM against the oracle's FP64 result on the oracle's own codes, graded
+in row blocks. The fast-accumulation GEMM is run on the same codes and graded
+the same way.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,8 @@ import torch
 
 import oracle
 import workloads as wl
-from tests.gpu_util import banner, dev, host, require_gpu
+from oracle.gemm import FAST_ACCUM_SUM_COEF
+from tests.gpu_util import banner, dev, f32, first_diff, host, require_gpu
 
 import fp8_mixed_precision_cast_amd as fp8
 from fp8_mixed_precision_cast_amd.linear import plan_from_workload
@@ -32,6 +34,31 @@ def _state_equal(st, rec, tag):
     assert _bits(host(st.scale_inv))[0] == _bits(rec.scale_inv), f"{tag}: scale_inv"
 
 
+class _Grade:
+    """Running count of entries over the bound and the worst ratio, with the worst entry's values."""
+
+    def __init__(self):
+        self.n, self.bad, self.worst, self.at = 0, 0, 0.0, None
+
+    def add(self, ratio, r0, y_bits, ref, absr):
+        self.n += ratio.size
+        self.bad += int((ratio > 1.0).sum())
+        i, j = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        if ratio[i, j] > self.worst:
+            self.worst = float(ratio[i, j])
+            self.at = (int(r0 + i), int(j), float(oracle.gemm.bf16_bits_to_f64(y_bits[i, j])), float(ref[i, j]),
+                       float(absr[i, j]))
+
+    def text(self):
+        return f"{self.bad} of {self.n} over, worst {self.worst:.4g} at (i, j, y, y_ref, sum|ab|) = {self.at}"
+
+
+def _fast_call(a, af, b, bf, sa, sb, m, n):
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    fp8.fp8_scaled_gemm_fast_accum(a, af, b, bf, sa, sb, c)
+    return c
+
+
 def test_tiny_forward_sixteen_steps():
     require_gpu()
     w = wl.BY_NAME["tiny_fwd_256"]
@@ -41,6 +68,7 @@ def test_tiny_forward_sixteen_steps():
     recs = {n: oracle.DelayedScaling(w.formats[n], w.history_len, w.margin) for n in ("X", "W")}
     wd = dev(inp["W"])
     saturated_steps = []
+    fast_r11, fast_own = _Grade(), _Grade()
     for t, xt in enumerate(xs):
         banner("tiny step", t)
         plan.step({"X": dev(xt), "W": wd})
@@ -55,24 +83,51 @@ def test_tiny_forward_sixteen_steps():
         absr = oracle.gemm_abs_ref(qx, "e4m3", qw, "e4m3", sx_inv, sw_inv)
         ok, worst = oracle.gemm_check(host(plan.out["fwd"].view(torch.int16)), ref, absr)
         assert ok, f"step {t}: gemm worst {worst}"
+        # the fast-accumulation GEMM on the same codes and inverse scales
+        y_fast = _fast_call(dev(qx), "e4m3", dev(qw), "e4m3", f32(sx_inv), f32(sw_inv), 256, 256)
+        yf = host(y_fast.view(torch.int16))
+        fast_r11.add(oracle.gemm_ratio(yf, ref, absr), 0, yf, ref, absr)
+        fast_own.add(oracle.gemm_ratio(yf, ref, absr, FAST_ACCUM_SUM_COEF), 0, yf, ref, absr)
         for r in recs.values():
             r.update()
         _state_equal(plan.state["X"], recs["X"], f"step {t} X")
         _state_equal(plan.state["W"], recs["W"], f"step {t} W")
     # steps whose u_t exceeds every earlier factor overflow the delayed scale and saturate
     assert saturated_steps == [1, 4, 6]
-
-
-def _sample(n, k, rng):
-    idx = rng.choice(n, min(k, n), replace=False)
-    return np.unique(np.concatenate([[0, n - 1], idx]))
+    print(f"GRADE tiny_fwd_256/fwd (16 steps) fast under the FP32 bound: {fast_r11.text()}", flush=True)
+    print(f"GRADE tiny_fwd_256/fwd (16 steps) fast under its own bound: {fast_own.text()}", flush=True)
+    assert fast_own.bad == 0, fast_own.text()
 
 
 BIG = ["mlp7b_up_fwd", "mlp7b_bwd_hybrid", "proj13b_fwd", "slice70b_fwd"]
+ROW_BLOCK = 4096          # output rows graded per oracle block
+CAST_ROWS = 2048          # source rows per oracle cast chunk (chunks run in a thread pool)
 
 
+def _oracle_codes(x, scale, fmt):
+    """The oracle's cast of a whole BF16 tensor, computed in row chunks on a thread pool (the cast is
+    elementwise, so the chunks are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(x.shape, np.uint8)
+
+    def one(r0):
+        out[r0:r0 + CAST_ROWS] = oracle.cast(x[r0:r0 + CAST_ROWS], scale, fmt, "bf16")
+
+    with ThreadPoolExecutor(min(16, len(__import__("os").sched_getaffinity(0)))) as ex:
+        list(ex.map(one, range(0, x.shape[0], CAST_ROWS)))
+    return out
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", BIG)
 def test_full_size_workload(name):
+    """Every code and every GEMM output of the workload, at full size, in the benchmark's launch
+    configuration. The codes of every tensor must equal the oracle's cast of the whole tensor bit for
+    bit (q_t == q^T on the device). Every output of every GEMM is graded against the oracle's FP64
+    GEMM on the oracle's codes: the FP32-accumulation GEMM within |y - y_ref| <= 2**-7 |y_ref| +
+    1e-6 sum|ab| everywhere. The fast-accumulation GEMM (FP8 matrix instruction) runs on the same
+    codes and must stay within its own 2**-9 bound everywhere; how many of its outputs miss the
+    FP32-accumulation bound is counted and printed (a characterisation, not asserted)."""
     require_gpu()
     w = wl.BY_NAME[name]
     banner("generate", name)
@@ -83,9 +138,8 @@ def test_full_size_workload(name):
     plan.prime(dinp)
     plan.step(dinp)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(w.config_id)
 
-    used = {}
+    used, codes = {}, {}
     for t in w.tensors:
         fmt = w.formats[t.name]
         x = inp[t.name]
@@ -96,36 +150,44 @@ def test_full_size_workload(name):
         rec.record(a)
         rec.update()
         _state_equal(plan.state[t.name], rec, f"{name}/{t.name}")
-        rows = _sample(x.shape[0], 48, rng)
-        q = plan.q[t.name]
-        got = host(q[torch.from_numpy(rows).cuda()])
-        want = oracle.cast(x[rows], used[t.name][0], fmt, "bf16")
-        assert np.array_equal(got, want), f"{t.name} sampled rows"
+        want = _oracle_codes(x, used[t.name][0], fmt)
+        codes[t.name] = want
+        got = host(plan.q[t.name])
+        assert np.array_equal(got, want), f"{t.name}: codes ({first_diff(got, want)})"
+        del got
         if plan.qt[t.name] is not None:
-            qt = plan.qt[t.name]
-            assert torch.equal(qt, q.t()), f"{t.name}: q_t != q^T"
-            cols = _sample(x.shape[1], 16, rng)
-            got_t = host(qt[torch.from_numpy(cols).cuda()])
-            want_t = oracle.cast(np.ascontiguousarray(x[:, cols].T), used[t.name][0], fmt, "bf16")
-            assert np.array_equal(got_t, want_t), f"{t.name} sampled columns"
+            assert torch.equal(plan.qt[t.name], plan.q[t.name].t()), f"{t.name}: q_t != q^T"
 
+    summary = {}
     for g in w.gemms:
-        banner("gemm-check", name, g.name)
         y = plan.out[g.name]
         assert y.shape == (g.m, g.n)
-        ii = _sample(g.m, 62, rng)
-        jj = _sample(g.n, 62, rng)
-
-        def operand_rows(tname, transposed, idx):
-            x = inp[tname]
-            src = np.ascontiguousarray(x[:, idx].T) if transposed else x[idx]
-            return oracle.cast(src, used[tname][0], w.formats[tname], "bf16")
-
-        qa = operand_rows(g.a, g.a_transposed, ii)
-        qb = operand_rows(g.b, g.b_transposed, jj)
-        ref = oracle.gemm_ref(qa, g.a_fmt, qb, g.b_fmt, used[g.a][1], used[g.b][1])
-        absr = oracle.gemm_abs_ref(qa, g.a_fmt, qb, g.b_fmt, used[g.a][1], used[g.b][1])
-        yi = y.view(torch.int16)[torch.from_numpy(ii).cuda()][:, torch.from_numpy(jj).cuda()]
-        ok, worst = oracle.gemm_check(host(yi), ref, absr)
-        assert ok, f"{name}/{g.name}: worst |err|/bound {worst}"
+        a_dev, af, b_dev, bf, sa_dev, sb_dev, _ = plan.gemm_operands()[[x.name for x in w.gemms].index(g.name)]
+        banner("gemm-fast", name, g.name)
+        y_fast = _fast_call(a_dev, af, b_dev, bf, sa_dev, sb_dev, g.m, g.n)
+        ye = host(y.view(torch.int16))
+        yf = host(y_fast.view(torch.int16))
+        del y_fast
+        qa = codes[g.a].T if g.a_transposed else codes[g.a]
+        qb = np.ascontiguousarray(codes[g.b].T) if g.b_transposed else codes[g.b]
+        sa, sb = used[g.a][1], used[g.b][1]
+        exact, fast_r11, fast_own = _Grade(), _Grade(), _Grade()
+        for r0 in range(0, g.m, ROW_BLOCK):
+            banner("gemm-grade", name, g.name, "rows", r0)
+            qa_blk = np.ascontiguousarray(qa[r0:r0 + ROW_BLOCK])
+            ref = oracle.gemm_ref(qa_blk, g.a_fmt, qb, g.b_fmt, sa, sb)
+            absr = oracle.gemm_abs_ref(qa_blk, g.a_fmt, qb, g.b_fmt, sa, sb)
+            assert np.isfinite(ref).all()
+            blk_e, blk_f = ye[r0:r0 + ROW_BLOCK], yf[r0:r0 + ROW_BLOCK]
+            exact.add(oracle.gemm_ratio(blk_e, ref, absr), r0, blk_e, ref, absr)
+            fast_r11.add(oracle.gemm_ratio(blk_f, ref, absr), r0, blk_f, ref, absr)
+            fast_own.add(oracle.gemm_ratio(blk_f, ref, absr, FAST_ACCUM_SUM_COEF), r0, blk_f, ref, absr)
+            del ref, absr
+        summary[g.name] = {"exact_fp32_bound": exact.text(), "fast_fp32_bound": fast_r11.text(),
+                           "fast_own_bound": fast_own.text()}
+        print(f"GRADE {name}/{g.name} exact under the FP32 bound: {exact.text()}", flush=True)
+        print(f"GRADE {name}/{g.name} fast under the FP32 bound: {fast_r11.text()}", flush=True)
+        print(f"GRADE {name}/{g.name} fast under its own bound: {fast_own.text()}", flush=True)
+        assert exact.bad == 0, f"{name}/{g.name}: exact GEMM {exact.text()}"
+        assert fast_own.bad == 0, f"{name}/{g.name}: fast GEMM {fast_own.text()}"
         assert torch.isfinite(y.float()).all(), f"{name}/{g.name}: non-finite output"

@@ -159,3 +159,62 @@ def test_gemm_at_the_largest_leading_dimension():
     wide = torch.zeros(2, ld + 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(fp8.Fp8mpError):
         fp8.fp8_scaled_gemm(wide[:, :k], "e4m3", b_store[:2, :k], "e5m2", f32(sa), f32(sb), c[:2, :2])
+
+
+def test_gemm_structured_cancellation_at_the_largest_k():
+    """K = 11008 (the 7B dgrad's K), every output cancelling exactly: each row of A is a run of
+    positive codes followed by the same run again, each row of B a run of positive codes followed by
+    its negation. The exact sum is 0, so the FP32-accumulation bound reduces to 1e-6 * sum|ab| while
+    the FP32 partial sums climb to half of sum|ab| and come back down: the worst case for chained FP32
+    accumulation. Every output must stay within the first-order error bound of that chain, one
+    rounding (unit roundoff 2**-24) per 16-product instruction, ceil(K / 16) * 2**-24 * sum|ab|,
+    which a dropped or doubled K step exceeds by orders of magnitude. How the worst output compares
+    with the 1e-6 * sum|ab| term is printed: at this K that term is at the limit of any chained FP32
+    accumulation (a CPU model that rounds to nearest after every 16 products reaches 0.75 and 0.89 of
+    it on these inputs), so it is reported, not asserted."""
+    require_gpu()
+    m, n, k = 96, 80, 11008
+    h = k // 2
+    rng = np.random.default_rng(11008)
+    chain = -(-k // 16) * 2.0 ** -24
+    for lo in (0x40, 0x01):                     # codes in [2, 448], then the full positive range
+        ca = rng.integers(lo, 0x7F, (m, h)).astype(np.uint8)
+        cb = rng.integers(lo, 0x7F, (n, h)).astype(np.uint8)
+        a = np.concatenate([ca, ca], axis=1)
+        b = np.concatenate([cb, cb | np.uint8(0x80)], axis=1)
+        sa, sb = np.float32(1 / 7.0), np.float32(3.0)
+        banner("gemm cancellation K=11008", hex(lo))
+        y = _run(a, "e4m3", b, "e4m3", sa, sb)
+        ref = oracle.gemm_ref(a, "e4m3", b, "e4m3", sa, sb)
+        absr = oracle.gemm_abs_ref(a, "e4m3", b, "e4m3", sa, sb)
+        assert not ref.any()
+        _, worst = oracle.gemm_check(y, ref, absr)
+        err = np.abs(oracle.gemm.bf16_bits_to_f64(y))
+        worst_chain = float((err / (chain * absr)).max())
+        print(f"GRADE cancellation K=11008 codes from {lo:#x}: worst |err| / (1e-6 sum|ab|) {worst:.4f}, "
+              f"of the chained-FP32 bound {worst_chain:.4f}", flush=True)
+        assert worst_chain <= 1.0, f"worst |err| / chained bound = {worst_chain}"
+
+
+@pytest.mark.parametrize("call", ["exact", "fast"])
+def test_gemm_inverse_scale_pairs_whose_product_leaves_binary32(call):
+    """Inverse scales whose product overflows (2**70 * 2**70) or underflows (2**-100 * 2**-60)
+    binary32 while the scaled result itself is a normal BF16 value: the result must still be within
+    the bound. A pair with an ordinary product (2**100 * 2**-100) is graded alongside."""
+    require_gpu()
+    f = fp8.fp8_scaled_gemm if call == "exact" else fp8.fp8_scaled_gemm_fast_accum
+    cases = [("e4m3", 0x01, 2.0 ** 70, 2.0 ** 70),      # acc = 16 * 2**-18 -> y = 2**126
+             ("e5m2", 0x7B, 2.0 ** -100, 2.0 ** -60),   # acc = 16 * 57344**2 -> y ~ 2**-124.4
+             ("e4m3", 0x7E, 2.0 ** 100, 2.0 ** -100)]
+    for fmt, code, sa, sb in cases:
+        a = np.full((40, 16), code, np.uint8)
+        b = np.full((24, 16), code, np.uint8)
+        b[::2, 3] |= 0x80                              # one negative product in every other column
+        sa, sb = np.float32(sa), np.float32(sb)
+        banner("gemm extreme scales", call, fmt, float(sa), float(sb))
+        c = torch.zeros(40, 24, dtype=torch.int16, device="cuda")
+        f(dev(a), fmt, dev(b), fmt, f32(sa), f32(sb), c)
+        y = host(c)
+        ref = oracle.gemm_ref(a, fmt, b, fmt, sa, sb)
+        assert np.isfinite(ref).all() and (np.abs(ref) > 2.0 ** -126).all() and (np.abs(ref) < 2.0 ** 127).all()
+        _check(a, fmt, b, fmt, sa, sb, y, f"{call} {fmt} scales {float(sa)} {float(sb)}")

@@ -312,3 +312,37 @@ def test_layer_plan_fast_accum_tiny_recipe():
             st = plan.state[n]
             assert np.array_equal(host(st.history).view(np.uint32), r.history.view(np.uint32)), (t, n)
             assert host(st.scale)[0] == r.scale and host(st.scale_inv)[0] == r.scale_inv, (t, n)
+
+
+def test_fast_instruction_drops_products_far_below_the_largest():
+    """The FP8 matrix instruction's own reduction, pinned on the device: in every 64-wide K block the
+    row holds one dominant product (+448*448 in the first block, -448*448 in the second, so they
+    cancel) and 63 products of magnitude 1.5. The exact sum is the small products' sum. The FP32
+    accumulation GEMM meets the FP32 bound; the fast GEMM loses the small products (the alignment to
+    the dominant product leaves them below its last kept bit), so it misses the FP32 bound while
+    staying within its own 2**-9 bound. This is the evidence that the fast mode cannot be graded
+    under the FP32 bound on every input."""
+    require_gpu()
+    a = np.full((64, 128), 0x38, np.uint8)       # E4M3 1.0
+    b = np.full((32, 128), 0x3C, np.uint8)       # E4M3 1.5
+    a[:, ::64] = 0x7E                            # 448 at k = 0 and k = 64
+    b[:, 0] = 0x7E
+    b[:, 64] = 0xFE
+    rng = np.random.default_rng(64)
+    signs = rng.integers(0, 2, (31, 128)).astype(np.uint8) << 7
+    signs[:, [0, 64]] = 0
+    b[1:] |= signs                               # row 0 all positive; the others mixed
+    banner("gemm-fast dominant products")
+    y_fast = _gemm(fp8.fp8_scaled_gemm_fast_accum, a, "e4m3", b, "e4m3", 1.0, 1.0)
+    y_exact = _gemm(fp8.fp8_scaled_gemm, a, "e4m3", b, "e4m3", 1.0, 1.0)
+    ref = oracle.gemm_ref(a, "e4m3", b, "e4m3", 1.0, 1.0)
+    absr = oracle.gemm_abs_ref(a, "e4m3", b, "e4m3", 1.0, 1.0)
+    assert ref[0, 0] == 126 * 1.5
+    assert oracle.gemm_check(y_exact, ref, absr)[0]
+    ok_fast_fp32, worst_fp32 = oracle.gemm_check(y_fast, ref, absr)
+    ok_fast_own, worst_own = oracle.gemm_check(y_fast, ref, absr, FAST_ACCUM_SUM_COEF)
+    yf = oracle.gemm.bf16_bits_to_f64(y_fast)
+    print(f"GRADE dominant-product blocks: fast row 0 = {yf[0, 0]} (exact {ref[0, 0]}), worst under the FP32 "
+          f"bound {worst_fp32:.1f}, under its own bound {worst_own:.4f}", flush=True)
+    assert not ok_fast_fp32 and worst_fp32 > 10.0
+    assert ok_fast_own

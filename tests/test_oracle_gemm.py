@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from oracle.codec import FMT
-from oracle.gemm import (bf16_bits_to_f64, gemm_abs_ref, gemm_check, gemm_entry, gemm_ref)
+from oracle.gemm import (SUM_COEF, bf16_bits_to_f64, gemm_abs_ref, gemm_check, gemm_entry, gemm_ratio, gemm_ref)
 
 
 def _finite_codes(rng, shape, name):
@@ -76,6 +76,78 @@ def test_triple_loop_non_square():
             assert ref[i, j] == pytest.approx(s, rel=1e-15, abs=1e-300)
             r, b = gemm_entry(A, "e5m2", B, "e4m3", 2.0, 0.5, i, j)
             assert r == pytest.approx(ref[i, j], rel=1e-15, abs=1e-300)
+
+
+def test_abs_sum_and_entry_match_exact_rational_triple_loop():
+    """sum_k |a_k b_k| (gemm_abs_ref and gemm_entry's second value) against a triple loop in exact
+    rationals over the codes' integer values, with negative and non-power-of-two inverse scales, so
+    that a missing abs on either operand or on a scale, a dropped term or a transposed pairing fails."""
+    rng = np.random.default_rng(5)
+    for af, bf, (m, n, k) in [("e5m2", "e4m3", (4, 5, 23)), ("e4m3", "e4m3", (3, 6, 40)),
+                              ("e4m3", "e5m2", (5, 2, 17))]:
+        A = _finite_codes(rng, (m, k), af)
+        B = _finite_codes(rng, (n, k), bf)
+        sa, sb = np.float32(-0.3), np.float32(1.75)
+        absr = gemm_abs_ref(A, af, B, bf, sa, sb)
+        ref = gemm_ref(A, af, B, bf, sa, sb)
+        fa, fb = Fraction(float(sa)), Fraction(float(sb))
+        for i in range(m):
+            for j in range(n):
+                tot = Fraction(0)
+                val = Fraction(0)
+                for kk in range(k):
+                    p = (Fraction(_int_value(int(A[i, kk]), af)) * UNIT[af] *
+                         Fraction(_int_value(int(B[j, kk]), bf)) * UNIT[bf])
+                    tot += abs(p)
+                    val += p
+                want_abs = tot * abs(fa) * abs(fb)
+                want = val * fa * fb
+                assert abs(Fraction(absr[i, j]) - want_abs) <= want_abs * Fraction(1, 2 ** 50)
+                r, b = gemm_entry(A, af, B, bf, sa, sb, i, j)
+                assert abs(Fraction(b) - want_abs) <= want_abs * Fraction(1, 2 ** 50)
+                assert abs(Fraction(r) - want) <= tot * abs(fa * fb) * Fraction(1, 2 ** 50)
+                assert abs(Fraction(ref[i, j]) - want) <= tot * abs(fa * fb) * Fraction(1, 2 ** 50)
+        # the bound term is never smaller than |y| and is the plain sum when all products are >= 0
+        assert (absr >= np.abs(ref) * (1 - 2 ** -50)).all()
+    P = np.full((2, 8), 0x40, np.uint8)           # E4M3 2.0
+    Q = np.full((3, 8), 0x38, np.uint8)           # E4M3 1.0
+    assert np.array_equal(gemm_abs_ref(P, "e4m3", Q, "e4m3", 0.5, 3.0), np.full((2, 3), 24.0))
+    assert np.array_equal(gemm_abs_ref(P, "e4m3", Q, "e4m3", 0.5, 3.0),
+                          np.abs(gemm_ref(P, "e4m3", Q, "e4m3", 0.5, 3.0)))
+
+
+def test_ratio_hand_values_and_counts():
+    """gemm_ratio on hand-computed entries: the bound 2**-7 |y_ref| + c * sum|ab| evaluated by hand,
+    zero bounds, NaN and infinite references, and the count of planted violations."""
+    y_ref = np.array([[100.0, 100.0, 0.0, 0.0, np.nan, np.inf, -np.inf, 3.0]])
+    absr = np.array([[200.0, 200.0, 0.0, 0.0, 1.0, 1.0, 1.0, 1e7]])
+    # BF16 bits: 101.0, 100.0, 0.0, 1.0, NaN, +Inf, +Inf, 0.0
+    y = np.array([[0x42CA, 0x42C8, 0x0000, 0x3F80, 0x7FC0, 0x7F80, 0x7F80, 0x0000]], np.uint16)
+    r = gemm_ratio(y, y_ref, absr)
+    want0 = 1.0 / (2.0 ** -7 * 100.0 + SUM_COEF * 200.0)
+    assert r[0, 0] == pytest.approx(want0, rel=1e-15)
+    assert r[0, 1] == 0.0 and r[0, 2] == 0.0 and r[0, 3] == np.inf
+    assert r[0, 4] == 0.0 and r[0, 5] == 0.0 and r[0, 6] == np.inf
+    assert r[0, 7] == pytest.approx(3.0 / (2.0 ** -7 * 3.0 + 10.0), rel=1e-15)
+    assert int((r > 1).sum()) == 3
+    ok, worst = gemm_check(y, y_ref, absr)
+    assert not ok and worst == np.inf
+    # a larger sum coefficient only lowers the ratio of finite entries
+    r2 = gemm_ratio(y, y_ref, absr, 2.0 ** -9)
+    assert r2[0, 0] == pytest.approx(1.0 / (2.0 ** -7 * 100.0 + 2.0 ** -9 * 200.0), rel=1e-15)
+    rng = np.random.default_rng(6)
+    A = _finite_codes(rng, (20, 64), "e4m3")
+    B = _finite_codes(rng, (30, 64), "e4m3")
+    ref = gemm_ref(A, "e4m3", B, "e4m3", 0.5, 0.25)
+    ab = gemm_abs_ref(A, "e4m3", B, "e4m3", 0.5, 0.25)
+    bits = _to_bf16_bits(ref)
+    assert (gemm_ratio(bits, ref, ab) <= 1.0).all()
+    bad = bits.copy()
+    pos = [(0, 0), (7, 13), (19, 29)]
+    for i, j in pos:
+        bad[i, j] ^= 0x8000 if ref[i, j] != 0 else 0x3F80   # flip the sign (or plant 1.0 for a zero)
+    rr = gemm_ratio(bad, ref, ab)
+    assert sorted(map(tuple, np.argwhere(rr > 1.0).tolist())) == pos
 
 
 def _to_bf16_bits(y: np.ndarray) -> np.ndarray:
