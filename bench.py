@@ -269,12 +269,15 @@ def other_gemm_tflops(plan, accum: str, iters: int = 20) -> float:
 
 
 class ClockSampler:
-    """Samples the GPU's graphics (SCLK) and memory (MCLK) clocks and the socket power through the amdsmi
-    library while the step runs: a background thread polls the device's metrics table. Reports the
-    median, min and max of what it saw, or the reason it could not read them."""
+    """The GPU's graphics clock (SCLK, mean over the XCDs), memory clock (MCLK) and socket power while the
+    step runs, read through the amdsmi library from the device's metrics table. The table refreshes
+    about once a second, so a background thread polls it every 20 ms and keeps each refreshed reading
+    (a new system clock counter) taken after the window began; the mean power between the first and
+    last of them comes from the energy accumulator. Reports what it saw, or why it could not."""
 
     def __init__(self):
-        self.samples, self.error, self._stop, self._thread, self._h, self._smi = [], None, False, None, None, None
+        self.readings, self.error, self._stop, self._thread, self._h, self._smi = [], None, False, None, None, None
+        self._first = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -282,35 +285,34 @@ class ClockSampler:
             if not handles:
                 raise RuntimeError("no GPU handle")
             self._h = handles[0]
-            if len(handles) > 1:
-                import torch
-                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
-                for h in handles:
-                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
-                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
-                        self._h = h
             self._smi = amdsmi
+            self._res = float(amdsmi.amdsmi_get_energy_count(self._h).get("counter_resolution", 15.3))
+            self._first = self._read()
         except Exception as e:  # the numbers are context; their absence is reported, not fatal
             self.error = f"{type(e).__name__}: {str(e)[:100]}"
+            self._smi = None
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        g = m.get("current_gfxclks")
+        gfx = [v for v in g if isinstance(v, (int, float)) and 0 < v < 65535] if isinstance(g, (list, tuple)) else []
+        num = lambda v: v if isinstance(v, (int, float)) else None
+        return {"counter": m.get("system_clock_counter"), "sclk": sum(gfx) / len(gfx) if gfx else None,
+                "sclk_per_xcd": gfx, "mclk": num(m.get("current_uclk")),
+                "power": num(m.get("current_socket_power")), "energy": num(m.get("energy_accumulator"))}
 
     def _poll(self):
-        smi = self._smi
+        last = self._first["counter"]
         while not self._stop:
             try:
-                m = smi.amdsmi_get_gpu_metrics_info(self._h)
-                g = m.get("current_gfxclks")
-                gfx = [v for v in g if isinstance(v, (int, float))] if isinstance(g, (list, tuple)) else []
-                if not gfx and isinstance(m.get("current_gfxclk"), (int, float)):
-                    gfx = [m["current_gfxclk"]]
-                uclk = m.get("current_uclk")
-                pw = m.get("current_socket_power", m.get("average_socket_power"))
-                self.samples.append((sum(gfx) / len(gfx) if gfx else None,
-                                     uclk if isinstance(uclk, (int, float)) else None,
-                                     pw if isinstance(pw, (int, float)) else None))
+                r = self._read()
             except Exception as e:
                 self.error = f"{type(e).__name__}: {str(e)[:100]}"
                 return
-            time.sleep(0.002)
+            if r["counter"] != last:
+                self.readings.append(r)
+                last = r["counter"]
+            time.sleep(0.02)
 
     def __enter__(self):
         if self._smi is not None:
@@ -326,16 +328,23 @@ class ClockSampler:
         return False
 
     def summary(self):
-        def stats(vals):
-            v = sorted(x for x in vals if x is not None)
-            if not v:
-                return None
-            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1]}
-        if not self.samples:
-            return {"error": self.error or "no samples"}
-        return {"samples": len(self.samples), "sclk_mhz": stats(s[0] for s in self.samples),
-                "mclk_mhz": stats(s[1] for s in self.samples), "socket_power_w": stats(s[2] for s in self.samples),
-                "source": "amdsmi gpu metrics, polled every 2 ms during the clock window"}
+        # the first refreshed reading may still average time before the load began
+        rs = self.readings[1:] if len(self.readings) > 2 else self.readings
+        if not rs:
+            return {"error": self.error or "no refreshed reading of the metrics table in the window"}
+
+        def stats(key):
+            v = sorted(r[key] for r in rs if r[key] is not None)
+            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1]} if v else None
+        out = {"readings": len(rs), "sclk_mhz": stats("sclk"), "mclk_mhz": stats("mclk"),
+               "socket_power_w": stats("power"), "sclk_per_xcd_mhz_last": rs[-1]["sclk_per_xcd"],
+               "source": "amdsmi gpu metrics table (refreshed about once a second), polled during the window"}
+        a, b = rs[0], rs[-1]
+        if len(rs) > 1 and a["energy"] is not None and b["energy"] is not None and b["counter"] != a["counter"]:
+            # system_clock_counter counts nanoseconds
+            out["mean_power_w"] = round((b["energy"] - a["energy"]) * self._res * 1e-6 /
+                                        ((b["counter"] - a["counter"]) * 1e-9), 1)
+        return out
 
 
 def parity(w, inp, plan, n_updates: int, recorded_after: bool, fast: bool, seed: int = 7):
@@ -505,12 +514,12 @@ def main():
         step_s, graph_ms = graph_steps(plan, dinp, K)
         n_updates += 3 + K
         graph_pct = pct(graph_ms)
-    # Clocks: the step repeated for about half a second (outside the timed region) while the
-    # sampler polls the device's metrics.
+    # Clocks: the step repeated for about three seconds (outside the timed region) while the
+    # sampler polls the device's metrics table.
     clocks = None
     if not args.no_clocks:
         sampler = ClockSampler()
-        reps = max(1, int(0.5 / max(step_s, 1e-4)))
+        reps = max(1, int(3.0 / max(step_s, 1e-4)))
         with sampler:
             for _ in range(reps):
                 plan.step(dinp)

@@ -77,9 +77,10 @@ fp8mp_status check_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const
   if (lda < k || ldb < k || (c != nullptr && ldc < n)) return FP8MP_ERR_INVALID_ARG;
   if (!is_aligned(a_scale_inv, 4) || !is_aligned(b_scale_inv, 4)) return FP8MP_ERR_INVALID_ARG;
   if (k % 16 != 0) return FP8MP_ERR_UNSUPPORTED;
+  // 16-byte copies of the operands and 16-byte stores of the output rows
   if (k > 0 && (lda % 16 != 0 || ldb % 16 != 0 || !is_aligned(a, 16) || !is_aligned(b, 16)))
-    return FP8MP_ERR_UNSUPPORTED;
-  if (!is_aligned(c, 2)) return FP8MP_ERR_INVALID_ARG;
+    return FP8MP_ERR_INVALID_ARG;
+  if (c != nullptr && (!is_aligned(c, 16) || ldc % 8 != 0)) return FP8MP_ERR_INVALID_ARG;
   // tile copies address at most 256 rows with 32-bit offsets
   if (k > 0 && (lda > fp8mp::kGemmMaxLd || ldb > fp8mp::kGemmMaxLd)) return FP8MP_ERR_UNSUPPORTED;
   // every row index product must stay inside int64 (lda, ldb may be 0 when k == 0)
@@ -104,9 +105,16 @@ fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int
   if ((q || q_t) && scale == nullptr) return FP8MP_ERR_INVALID_ARG;
   if (q && ld_q < cols) return FP8MP_ERR_INVALID_ARG;
   if (q_t && ld_qt < rows) return FP8MP_ERR_INVALID_ARG;
-  if (!is_aligned(x, x_dtype == FP8MP_BF16 ? 2 : 4)) return FP8MP_ERR_INVALID_ARG;
   if (amax && !is_aligned(amax, 4)) return FP8MP_ERR_INVALID_ARG;
   if (scale && !is_aligned(scale, 4)) return FP8MP_ERR_INVALID_ARG;
+  // The kernels move 16-byte vectors: every data pointer is 16-byte aligned.
+  if (!is_aligned(x, 16) || (q && !is_aligned(q, 16)) || (q_t && !is_aligned(q_t, 16))) return FP8MP_ERR_INVALID_ARG;
+  // One contiguous run (flat kernels) or 16-byte aligned BF16 rows (tile kernel).
+  const bool flat = (rows == 1 || (ld_x == cols && (!q || ld_q == cols))) && !q_t;
+  if (!flat) {
+    if (x_dtype != FP8MP_BF16) return FP8MP_ERR_UNSUPPORTED;   // fp32 sources: contiguous, no transposed copy
+    if ((ld_x * 2) % 16 != 0 || (q && ld_q % 16 != 0) || (q_t && ld_qt % 16 != 0)) return FP8MP_ERR_INVALID_ARG;
+  }
   // every row/column index product must stay inside int64
   if (rows > (INT64_MAX / 8) / ld_x) return FP8MP_ERR_UNSUPPORTED;
   if (q_t && cols > (INT64_MAX / 8) / ld_qt) return FP8MP_ERR_UNSUPPORTED;
@@ -127,7 +135,7 @@ fp8mp_status fp8_amax_cast_batched(int32_t n_items, const fp8mp_cast_item* items
     if (!valid_dtype(it.x_dtype) || !valid_format(it.fmt) || it.numel < 0) return FP8MP_ERR_INVALID_ARG;
     if (it.numel == 0) continue;
     if (it.x == nullptr || (it.q && it.scale == nullptr)) return FP8MP_ERR_INVALID_ARG;
-    if (!is_aligned(it.x, it.x_dtype == FP8MP_BF16 ? 2 : 4)) return FP8MP_ERR_INVALID_ARG;
+    if (!is_aligned(it.x, 16) || (it.q && !is_aligned(it.q, 16))) return FP8MP_ERR_INVALID_ARG;
     if ((it.amax && !is_aligned(it.amax, 4)) || (it.scale && !is_aligned(it.scale, 4))) return FP8MP_ERR_INVALID_ARG;
   }
   int cus = 0;
@@ -143,8 +151,7 @@ fp8mp_status fp8_amax_cast_batched(int32_t n_items, const fp8mp_cast_item* items
   for (int32_t i = 0; i < n_items; ++i) {
     const fp8mp_cast_item& it = items[i];
     if (it.numel == 0 || (!it.q && !it.amax)) continue;
-    const bool batchable = it.x_dtype == FP8MP_BF16 && is_aligned(it.x, 16) && (!it.q || is_aligned(it.q, 16));
-    if (!batchable) {
+    if (it.x_dtype != FP8MP_BF16) {   // fp32 sources: their own flat kernel
       st = from_hip(fp8mp::launch_amax_cast(it.x, it.x_dtype, 1, it.numel, it.numel, it.fmt, it.scale, it.q,
                                             it.numel, nullptr, 0, it.amax, cus, stream));
       if (st != FP8MP_OK) return st;
@@ -234,6 +241,7 @@ fp8mp_status scaled_gemm_amax_cast(const uint8_t* a, fp8mp_format a_fmt, int64_t
   if (st != FP8MP_OK) return st;
   if (!valid_format(y_fmt)) return FP8MP_ERR_INVALID_ARG;
   if (y_q && (y_scale == nullptr || ld_yq < n)) return FP8MP_ERR_INVALID_ARG;
+  if (y_q && (!is_aligned(y_q, 16) || ld_yq % 16 != 0)) return FP8MP_ERR_INVALID_ARG;
   if (y_scale && !is_aligned(y_scale, 4)) return FP8MP_ERR_INVALID_ARG;
   if (y_amax && !is_aligned(y_amax, 4)) return FP8MP_ERR_INVALID_ARG;
   if (y_q && m > (INT64_MAX / 8) / ld_yq) return FP8MP_ERR_UNSUPPORTED;

@@ -27,6 +27,21 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // for the non
 constexpr int kTileRows = 128;   // 32 row groups of 4
 constexpr int kTileCols = 128;   // 8 column groups of 16
 
+// The last numel % 16 elements of a flat cast, one per thread of block 0
+// (at most 15; the 16-byte chunks before them go through the vector body).
+template <int FMT, int DT, bool HAS_Q>
+__device__ __forceinline__ uint32_t flat_tail(const void* __restrict__ x, uint8_t* __restrict__ q, int64_t numel,
+                                              float s, uint32_t m) {
+  const int64_t e = (numel & ~int64_t(15)) + threadIdx.x;
+  if (e < numel) {
+    const float v = DT == FP8MP_BF16 ? __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[e] << 16)
+                                     : static_cast<const float*>(x)[e];
+    m = amax_f32(m, v);
+    if constexpr (HAS_Q) q[e] = enc1<FMT>(v, s);
+  }
+  return m;
+}
+
 // ---------------------------------------------------------------------------
 // Contiguous BF16 source: each thread converts kFlatUnroll chunks of 16
 // elements per iteration (two 16-byte loads -> one 16-byte store per chunk);
@@ -80,11 +95,12 @@ __device__ __forceinline__ uint32_t flat_bf16_body(const uint4* __restrict__ x, 
 
 template <int FMT, bool HAS_Q>
 __global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16(const uint4* __restrict__ x,
-                                                             uint4* __restrict__ q, int64_t nchunk,
+                                                             uint4* __restrict__ q, int64_t numel,
                                                              const float* __restrict__ scale,
                                                              float* __restrict__ amax) {
   const float s = HAS_Q ? *scale : 1.0f;
-  const uint32_t m = flat_bf16_body<FMT, HAS_Q>(x, q, nchunk, s, blockIdx.x, gridDim.x);
+  uint32_t m = flat_bf16_body<FMT, HAS_Q>(x, q, numel / 16, s, blockIdx.x, gridDim.x);
+  if (blockIdx.x == 0) m = flat_tail<FMT, FP8MP_BF16, HAS_Q>(x, reinterpret_cast<uint8_t*>(q), numel, s, m);
   if (amax) block_amax_commit<kFlatBlock>(m, amax);
 }
 
@@ -110,15 +126,13 @@ __global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16_batched(CastBatch b
     m = has_q ? flat_bf16_body<FP8MP_E5M2, true>(x, q, nchunk, s, block, nblocks)
               : flat_bf16_body<FP8MP_E5M2, false>(x, q, nchunk, s, block, nblocks);
   if (block == 0) {
-    const int64_t e = nchunk * 16 + threadIdx.x;
-    if (e < batch.numel[t]) {
-      const float v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(batch.x[t])[e] << 16);
-      m = amax_f32(m, v);
-      if (has_q) {
-        uint8_t* qb = static_cast<uint8_t*>(batch.q[t]);
-        qb[e] = batch.fmt[t] == FP8MP_E4M3 ? enc1<FP8MP_E4M3>(v, s) : enc1<FP8MP_E5M2>(v, s);
-      }
-    }
+    uint8_t* qb = static_cast<uint8_t*>(batch.q[t]);
+    if (batch.fmt[t] == FP8MP_E4M3)
+      m = has_q ? flat_tail<FP8MP_E4M3, FP8MP_BF16, true>(batch.x[t], qb, batch.numel[t], s, m)
+                : flat_tail<FP8MP_E4M3, FP8MP_BF16, false>(batch.x[t], qb, batch.numel[t], s, m);
+    else
+      m = has_q ? flat_tail<FP8MP_E5M2, FP8MP_BF16, true>(batch.x[t], qb, batch.numel[t], s, m)
+                : flat_tail<FP8MP_E5M2, FP8MP_BF16, false>(batch.x[t], qb, batch.numel[t], s, m);
   }
   if (batch.amax[t] != nullptr) block_amax_commit<kFlatBlock>(canonical_nan(m), batch.amax[t]);
 }
@@ -126,10 +140,11 @@ __global__ __launch_bounds__(kFlatBlock) void cast_flat_bf16_batched(CastBatch b
 // Contiguous fp32 source, 16 elements (four 16-byte loads) -> one 16-byte store.
 template <int FMT, bool HAS_Q>
 __global__ __launch_bounds__(kFlatBlock) void cast_flat_f32(const float4* __restrict__ x,
-                                                            uint4* __restrict__ q, int64_t nchunk,
+                                                            uint4* __restrict__ q, int64_t numel,
                                                             const float* __restrict__ scale,
                                                             float* __restrict__ amax) {
   const float s = HAS_Q ? *scale : 1.0f;
+  const int64_t nchunk = numel / 16;
   uint32_t acc = 0;
   const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
   for (int64_t i = (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; i < nchunk; i += stride) {
@@ -150,39 +165,8 @@ __global__ __launch_bounds__(kFlatBlock) void cast_flat_f32(const float4* __rest
       q[i] = o;
     }
   }
+  if (blockIdx.x == 0) acc = flat_tail<FMT, FP8MP_F32, HAS_Q>(x, reinterpret_cast<uint8_t*>(q), numel, s, acc);
   if (amax) block_amax_commit<kFlatBlock>(acc, amax);
-}
-
-// ---------------------------------------------------------------------------
-// Any layout, one element per iteration over the row-major index range
-// [start, end). Serves strided views, fp32 with a transposed copy, unaligned
-// pointers and the tails of the flat kernels.
-template <int FMT, int DT>
-__global__ __launch_bounds__(kFlatBlock) void cast_generic(const void* __restrict__ xv, int64_t cols,
-                                                           int64_t ld_x, int64_t start, int64_t end,
-                                                           const float* __restrict__ scale,
-                                                           uint8_t* __restrict__ q, int64_t ld_q,
-                                                           uint8_t* __restrict__ q_t, int64_t ld_qt,
-                                                           float* __restrict__ amax) {
-  const float s = (q || q_t) ? *scale : 1.0f;
-  uint32_t acc = 0;
-  const int64_t stride = (int64_t)gridDim.x * kFlatBlock;
-  for (int64_t e = start + (int64_t)blockIdx.x * kFlatBlock + threadIdx.x; e < end; e += stride) {
-    const int64_t r = e / cols, c = e - r * cols;
-    float v;
-    if constexpr (DT == FP8MP_BF16) {
-      v = __uint_as_float((uint32_t)static_cast<const uint16_t*>(xv)[r * ld_x + c] << 16);
-    } else {
-      v = static_cast<const float*>(xv)[r * ld_x + c];
-    }
-    acc = amax_f32(acc, v);
-    if (q || q_t) {
-      const uint8_t code = enc1<FMT>(v, s);
-      if (q) q[r * ld_q + c] = code;
-      if (q_t) q_t[c * ld_qt + r] = code;
-    }
-  }
-  if (amax) block_amax_commit<kFlatBlock>(canonical_nan(acc), amax);
 }
 
 // ---------------------------------------------------------------------------
@@ -221,7 +205,7 @@ __global__ __launch_bounds__(kTileBlock) void cast_tile_bf16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ld_q,
     uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ amax, int64_t tiles_c,
-    int64_t ntiles, int vec_ok) {
+    int64_t ntiles) {
   __shared__ __attribute__((aligned(16))) uint8_t T[kTileCols * kTileRows];
   const float s = (HAS_Q || HAS_QT) ? *scale : 1.0f;
   const int tid = threadIdx.x, cg = tid & 7, rg = tid >> 3;
@@ -230,7 +214,7 @@ __global__ __launch_bounds__(kTileBlock) void cast_tile_bf16(
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
     const int64_t R0 = tr * kTileRows, C0 = tc * kTileCols;
-    const bool full = vec_ok && (R0 + kTileRows <= rows) && (C0 + kTileCols <= cols);
+    const bool full = (R0 + kTileRows <= rows) && (C0 + kTileCols <= cols);
     if (full) {
       const int64_t r0 = R0 + rg * 4, c0 = C0 + cg * 16;
       u32x4 v[4][2];
@@ -305,75 +289,50 @@ __global__ __launch_bounds__(kTileBlock) void cast_tile_bf16(
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-template <int FMT, int DT>
-hipError_t launch_generic(const void* x, int64_t cols, int64_t ld_x, int64_t start, int64_t end,
-                          const float* scale, uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
-                          float* amax, int num_cus, hipStream_t stream) {
-  const int64_t n = end - start;
-  if (n <= 0) return hipSuccess;
-  const int grid = (int)std::min<int64_t>(cdiv(n, kFlatBlock), (int64_t)num_cus * 2);
-  hipLaunchKernelGGL((cast_generic<FMT, DT>), dim3(grid), dim3(kFlatBlock), 0, stream, x, cols, ld_x,
-                     start, end, scale, q, ld_q, q_t, ld_qt, amax);
-  return hipGetLastError();
-}
-
+// Argument rules (validated by the C-ABI before this is called): x, q and q_t
+// 16-byte aligned. A call is flat when the source and the codes are one
+// contiguous run (one row, or ld_x == cols and ld_q == cols) and there is no
+// transposed copy: BF16 and fp32 sources then take the flat kernels. Every
+// other call has a BF16 source with 16-byte aligned rows (ld_x * 2, ld_q and
+// ld_qt multiples of 16) and takes the 2-D tile kernel.
 template <int FMT>
 hipError_t launch_fmt(const void* x, fp8mp_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
                       const float* scale, uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
                       float* amax, int num_cus, hipStream_t stream) {
   const int64_t numel = rows * cols;
-  const int esize = dt == FP8MP_BF16 ? 2 : 4;
-  const bool contiguous = ld_x == cols && (q == nullptr || ld_q == cols) && q_t == nullptr;
-
-  if (contiguous && aligned(x, 16) && (q == nullptr || aligned(q, 16))) {
+  const bool flat = (rows == 1 || (ld_x == cols && (q == nullptr || ld_q == cols))) && q_t == nullptr;
+  if (flat) {
     const int64_t nchunk = numel / 16;
-    if (nchunk > 0) {
-      const int per_block = dt == FP8MP_BF16 ? kFlatBlock * kFlatUnroll : kFlatBlock;
-      const int grid = (int)std::min<int64_t>(cdiv(nchunk, per_block), (int64_t)num_cus * 2);
-      if (dt == FP8MP_BF16) {
-        if (q) hipLaunchKernelGGL((cast_flat_bf16<FMT, true>), dim3(grid), dim3(kFlatBlock), 0, stream,
-                                  (const uint4*)x, (uint4*)q, nchunk, scale, amax);
-        else hipLaunchKernelGGL((cast_flat_bf16<FMT, false>), dim3(grid), dim3(kFlatBlock), 0, stream,
-                                (const uint4*)x, (uint4*)nullptr, nchunk, scale, amax);
-      } else {
-        if (q) hipLaunchKernelGGL((cast_flat_f32<FMT, true>), dim3(grid), dim3(kFlatBlock), 0, stream,
-                                  (const float4*)x, (uint4*)q, nchunk, scale, amax);
-        else hipLaunchKernelGGL((cast_flat_f32<FMT, false>), dim3(grid), dim3(kFlatBlock), 0, stream,
-                                (const float4*)x, (uint4*)nullptr, nchunk, scale, amax);
-      }
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+    const int per_block = dt == FP8MP_BF16 ? kFlatBlock * kFlatUnroll : kFlatBlock;
+    // at least one block: block 0 also converts the numel % 16 tail
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(nchunk, per_block), (int64_t)num_cus * 2));
+    if (dt == FP8MP_BF16) {
+      if (q) hipLaunchKernelGGL((cast_flat_bf16<FMT, true>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                                (const uint4*)x, (uint4*)q, numel, scale, amax);
+      else hipLaunchKernelGGL((cast_flat_bf16<FMT, false>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                              (const uint4*)x, (uint4*)nullptr, numel, scale, amax);
+    } else {
+      if (q) hipLaunchKernelGGL((cast_flat_f32<FMT, true>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                                (const float4*)x, (uint4*)q, numel, scale, amax);
+      else hipLaunchKernelGGL((cast_flat_f32<FMT, false>), dim3(grid), dim3(kFlatBlock), 0, stream,
+                              (const float4*)x, (uint4*)nullptr, numel, scale, amax);
     }
-    // the last numel % 16 elements
-    if (dt == FP8MP_BF16)
-      return launch_generic<FMT, FP8MP_BF16>(x, cols, ld_x, nchunk * 16, numel, scale, q, ld_q, q_t,
-                                             ld_qt, amax, num_cus, stream);
-    return launch_generic<FMT, FP8MP_F32>(x, cols, ld_x, nchunk * 16, numel, scale, q, ld_q, q_t, ld_qt,
-                                          amax, num_cus, stream);
-  }
-
-  if (dt == FP8MP_BF16) {
-    const bool vec_ok = aligned(x, 16) && (ld_x * esize) % 16 == 0 &&
-                        (q == nullptr || (aligned(q, 16) && ld_q % 16 == 0)) &&
-                        (q_t == nullptr || (aligned(q_t, 16) && ld_qt % 16 == 0));
-    const int64_t tiles_r = cdiv(rows, kTileRows), tiles_c = cdiv(cols, kTileCols);
-    const int64_t ntiles = tiles_r * tiles_c;
-    const int grid = (int)std::min<int64_t>(ntiles, (int64_t)num_cus * 4);   // 4 per CU: measured best of 2-16
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
-#define FP8MP_TILE(HQ, HQT)                                                                       \
-  hipLaunchKernelGGL((cast_tile_bf16<FMT, HQ, HQT>), dim3(grid), dim3(kTileBlock), 0, stream, xb, \
-                     rows, cols, ld_x, scale, q, ld_q, q_t, ld_qt, amax, tiles_c, ntiles, (int)vec_ok)
-    if (q && q_t) FP8MP_TILE(true, true);
-    else if (q) FP8MP_TILE(true, false);
-    else if (q_t) FP8MP_TILE(false, true);
-    else FP8MP_TILE(false, false);
-#undef FP8MP_TILE
     return hipGetLastError();
   }
-  return launch_generic<FMT, FP8MP_F32>(x, cols, ld_x, 0, numel, scale, q, ld_q, q_t, ld_qt, amax,
-                                        num_cus, stream);
+  if (dt != FP8MP_BF16) return hipErrorInvalidValue;   // refused by the C-ABI's validation
+  const int64_t tiles_r = cdiv(rows, kTileRows), tiles_c = cdiv(cols, kTileCols);
+  const int64_t ntiles = tiles_r * tiles_c;
+  const int grid = (int)std::min<int64_t>(ntiles, (int64_t)num_cus * 4);   // 4 per CU: measured best of 2-16
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+#define FP8MP_TILE(HQ, HQT)                                                                       \
+  hipLaunchKernelGGL((cast_tile_bf16<FMT, HQ, HQT>), dim3(grid), dim3(kTileBlock), 0, stream, xb, \
+                     rows, cols, ld_x, scale, q, ld_q, q_t, ld_qt, amax, tiles_c, ntiles)
+  if (q && q_t) FP8MP_TILE(true, true);
+  else if (q) FP8MP_TILE(true, false);
+  else if (q_t) FP8MP_TILE(false, true);
+  else FP8MP_TILE(false, false);
+#undef FP8MP_TILE
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -345,7 +345,6 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     s1 = too_large ? small : big;
     s2 = too_large ? big : small;
   }
-  const bool vec = ((reinterpret_cast<uintptr_t>(C) | (uintptr_t)(ldc * 2)) & 15) == 0;
   const bool do_c = YF == kNoY || C != nullptr;   // the fused call may skip the BF16 output
 
   int bm, bn;
@@ -409,9 +408,9 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   const int64_t gn = n0 + 8 * c;
   const bool do_q = YF != kNoY && y_q != nullptr, do_amax = YF != kNoY && y_amax != nullptr;
   const float ys = do_q ? *y_scale : 0.f;
-  const bool vq = ((reinterpret_cast<uintptr_t>(y_q) | (uintptr_t)ld_yq) & 7) == 0;
   uint32_t am = 0;   // packed BF16 magnitudes of the in-range outputs
-  const bool full = m0 + kBM <= M && n0 + kBN <= N && vec && (!do_q || vq);
+  // C and y_q are 16-byte aligned with 16-byte row pitches (checked by the C-ABI).
+  const bool full = m0 + kBM <= M && n0 + kBN <= N;
   if (full) {
     // Interior tile: the chunks of up to 16 passes are read first (the
     // accumulators are dead, so the registers are free), then stored with
@@ -459,8 +458,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
       }
     }
   } else {
-    // Edge tiles and unaligned outputs: row and column checks, element stores
-    // where a chunk straddles N or the layout forbids wide stores.
+    // Edge tiles: row and column checks, element stores where a chunk
+    // straddles N.
     for (int p = 0; p < kBM / kRowsPerPass; ++p) {
       const int row = p * kRowsPerPass + (tid >> 5);
       const int64_t gm = m0 + row;
@@ -469,24 +468,12 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       uint16_t* dst = C + gm * ldc + gn;
       if (gn + 8 <= N) {
-        if (!do_c) {
-        } else if (vec) {
-          *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-        }
+        if (do_c) *reinterpret_cast<uint4*>(dst) = v;
         if constexpr (YF != kNoY) {
           if (do_amax) am = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(am, w[0]), w[1]), w[2]), w[3]);
           if (do_q) {
             const uint32_t q0 = enc4_bf16_sel<YF>(w[0], w[1], ys), q1 = enc4_bf16_sel<YF>(w[2], w[3], ys);
-            uint8_t* qd = y_q + gm * ld_yq + gn;
-            if (vq) {
-              *reinterpret_cast<uint2*>(qd) = uint2{q0, q1};
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) qd[e] = (uint8_t)((e < 4 ? q0 : q1) >> (8 * (e & 3)));
-            }
+            *reinterpret_cast<uint2*>(y_q + gm * ld_yq + gn) = uint2{q0, q1};
           }
         }
       } else {

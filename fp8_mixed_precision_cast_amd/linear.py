@@ -28,8 +28,9 @@ only.
 "fast" uses the FP8 matrix instruction's reduced-precision accumulation
 (fp8_scaled_gemm_fast_accum, within 2**-9 of sum|a*b|) for every GEMM.
 
-The plan owns its device buffers (allocated once, through torch); a step
-allocates nothing and never synchronises.
+The plan owns its device buffers (allocated once, through torch, with rows
+starting 16 bytes apart multiples as the C-ABI requires of strided buffers); a
+step allocates nothing and never synchronises.
 """
 from __future__ import annotations
 
@@ -41,6 +42,14 @@ import torch
 from . import (CastBatch, CurrentScalingState, DelayedScalingState, ScaleUpdateBatch, fp8_amax_cast,
                fp8_amax_cast_batched, fp8_layernorm_amax_cast, fp8_scale_update_batched, fp8_scaled_gemm,
                fp8_scaled_gemm_amax_cast, fp8_scaled_gemm_amax_cast_fast_accum, fp8_scaled_gemm_fast_accum)
+
+
+def _pitched(rows: int, cols: int, dtype, device) -> torch.Tensor:
+    """A rows x cols buffer whose rows start 16 bytes apart multiples (the C-ABI's rule for strided
+    buffers); contiguous when a row is already a multiple of 16 bytes."""
+    esz = torch.empty(0, dtype=dtype).element_size()
+    ld = -(-cols * esz // 16) * 16 // esz
+    return torch.empty(rows, max(ld, 1), dtype=dtype, device=device)[:, :cols]
 
 
 @dataclass(frozen=True)
@@ -106,8 +115,8 @@ class LayerPlan:
             r, c = o.shape
             self.state[o.name] = (DelayedScalingState(o.fmt, history_len, margin, device) if recipe == "delayed"
                                   else CurrentScalingState(o.fmt, margin, device))
-            self.q[o.name] = torch.empty(r, c, dtype=torch.uint8, device=device) if o.plain else None
-            self.qt[o.name] = torch.empty(c, r, dtype=torch.uint8, device=device) if o.transposed else None
+            self.q[o.name] = _pitched(r, c, torch.uint8, device) if o.plain else None
+            self.qt[o.name] = _pitched(c, r, torch.uint8, device) if o.transposed else None
         self._batch = None
         self._cast_batch = None
         self._gemm_args = []
@@ -118,11 +127,11 @@ class LayerPlan:
                 raise ValueError(f"gemm {g.name}: operand layout not produced")
             if a.shape[1] != b.shape[1]:
                 raise ValueError(f"gemm {g.name}: K mismatch {tuple(a.shape)} vs {tuple(b.shape)}")
-            c = torch.empty(a.shape[0], b.shape[0], dtype=torch.bfloat16, device=device)
+            c = _pitched(a.shape[0], b.shape[0], torch.bfloat16, device)
             self.out[g.name] = c
             if output_cast:
                 self.ystate[g.name] = DelayedScalingState("e4m3", history_len, margin, device)
-                self.yq[g.name] = torch.empty(a.shape[0], b.shape[0], dtype=torch.uint8, device=device)
+                self.yq[g.name] = _pitched(a.shape[0], b.shape[0], torch.uint8, device)
             sa, sb = self.state[g.a], self.state[g.b]
             self._gemm_args.append((a, sa.fmt, b, sb.fmt, sa.scale_inv, sb.scale_inv, c))
 
@@ -161,7 +170,8 @@ class LayerPlan:
         batched = set()
         if self.recipe == "delayed":
             names = [n for n, o in self.operands.items()
-                     if n not in self.ln and not o.transposed and inputs[n].is_contiguous()]
+                     if n not in self.ln and not o.transposed and inputs[n].is_contiguous()
+                     and self.q[n] is not None and self.q[n].is_contiguous()]
             key = tuple((n, inputs[n].data_ptr(), inputs[n].dtype, inputs[n].numel()) for n in names)
             if names and (self._cast_batch is None or self._cast_batch[0] != key):
                 items = [(inputs[n], self.state[n].fmt, self.state[n].scale, self.q[n], self.state[n].amax_slot)

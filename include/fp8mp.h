@@ -81,7 +81,15 @@ typedef enum {
  *
  * q, q_t and amax may each be NULL; scale may be NULL only when q and q_t are
  * both NULL (an amax-only pass). rows or cols == 0 is a no-op returning OK.
- * Any alignment is accepted; 16-byte aligned rows take the vector path.
+ *
+ * Layout rules (the kernels move 16-byte vectors; there is no scalar path):
+ *   - x, q and q_t start on 16-byte boundaries, else FP8MP_ERR_INVALID_ARG.
+ *   - A flat call, one contiguous run (rows == 1, or ld_x == cols and
+ *     ld_q == cols) with q_t NULL, takes any cols, BF16 or fp32.
+ *   - Any other call needs a BF16 source and 16-byte row pitches: ld_x * 2,
+ *     ld_q and ld_qt multiples of 16, else FP8MP_ERR_INVALID_ARG. Ragged
+ *     rows and cols are fine. An fp32 source that is strided or needs q_t is
+ *     FP8MP_ERR_UNSUPPORTED.
  */
 fp8mp_status fp8_amax_cast(const void* x, fp8mp_dtype x_dtype, int64_t rows, int64_t cols,
                            int64_t ld_x, fp8mp_format fmt, const float* scale,
@@ -102,12 +110,12 @@ typedef struct {
 /*
  * fp8_amax_cast_batched: fp8_amax_cast for n_items contiguous tensors, with
  * the same results as n_items separate calls. A layer casts all its operands
- * at the start of a step ([TE] §動的スケーリングとFP8レシピの設定); contiguous BF16
- * sources with 16-byte aligned x and q share one launch per 8 tensors, the
- * workgroups split among them by size; other items take fp8_amax_cast's
- * kernels one by one. items is a host array; each item is validated as
- * fp8_amax_cast validates a rows = 1, cols = numel call. Items must not
- * overlap one another's outputs.
+ * at the start of a step ([TE] §動的スケーリングとFP8レシピの設定); BF16 sources
+ * share one launch per 8 tensors, the workgroups split among them by size;
+ * fp32 sources take fp8_amax_cast's flat kernel one by one. items is a host
+ * array; each item is validated as fp8_amax_cast validates a rows = 1,
+ * cols = numel call (x and q on 16-byte boundaries), all before anything is
+ * launched. Items must not overlap one another's outputs.
  */
 fp8mp_status fp8_amax_cast_batched(int32_t n_items, const fp8mp_cast_item* items, hipStream_t stream);
 
@@ -166,11 +174,16 @@ fp8mp_status fp8_scale_update_batched(int32_t n_tensors, float* const* amax_hist
  *
  * Format pairs: (E4M3, E4M3) for the forward pass; (E5M2, E4M3) for dgrad and
  * wgrad of the HYBRID recipe ([TE] §動的スケーリングとFP8レシピの設定); (E4M3, E5M2)
- * and (E5M2, E5M2) are also accepted. k must be a multiple of 16, a and b
- * 16-byte aligned and lda, ldb multiples of 16 (else FP8MP_ERR_UNSUPPORTED);
- * c needs only its natural 2-byte alignment and any ldc >= n.
+ * and (E5M2, E5M2) are also accepted. k must be a multiple of 16 (the
+ * kernel's K granule; else FP8MP_ERR_UNSUPPORTED). a, b and c start on
+ * 16-byte boundaries, lda and ldb are multiples of 16 and ldc a multiple of
+ * 8 (16-byte row pitches), else FP8MP_ERR_INVALID_ARG. lda, ldb at most
+ * 4 MiB (else FP8MP_ERR_UNSUPPORTED).
  * m, n arbitrary; m == 0 or n == 0 is a no-op; k == 0 writes zeros (times the
- * inverse scales). NaN codes propagate to NaN outputs.
+ * inverse scales). NaN codes propagate to NaN outputs. The output is
+ * (acc * (sa_inv * sb_inv)) rounded to BF16, or, when that product of the
+ * inverse scales overflows or underflows binary32, the two factors applied
+ * one after the other.
  */
 fp8mp_status fp8_scaled_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda,
                              const uint8_t* b, fp8mp_format b_fmt, int64_t ldb,
@@ -217,7 +230,8 @@ fp8mp_status fp8_scaled_gemm_fast_accum(const uint8_t* a, fp8mp_format a_fmt, in
  *            y_amax is given: the BF16 output is then computed but not stored.
  *   y_fmt    the format of y_q (validated even when y_q is NULL).
  *   y_scale  one fp32 on the device; required when y_q is given.
- *   y_q      m x n codes, leading dimension ld_yq (>= n), or NULL.
+ *   y_q      m x n codes, leading dimension ld_yq (>= n, a multiple of 16),
+ *            starting on a 16-byte boundary, or NULL.
  *   y_amax   one fp32 on the device, max-accumulated, or NULL.
  * With y_q and y_amax both NULL the call equals fp8_scaled_gemm. y_q and
  * y_amax must not overlap c, a or b.

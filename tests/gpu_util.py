@@ -47,3 +47,16 @@ def first_diff(a: np.ndarray, b: np.ndarray) -> str:
         return "equal"
     i = tuple(idx[0])
     return f"{idx.shape[0]} mismatches, first at {i}: got {a[i]!r} want {b[i]!r}"
+
+
+def pitched(rows: int, cols: int, dtype, fill=None, pad_bytes: int = 0):
+    """A rows x cols device view whose rows start 16 bytes apart multiples (row pitch rounded up to 16
+    bytes, plus pad_bytes, a multiple of 16) in a 16-byte aligned allocation, as the C-ABI requires of
+    every strided buffer. Returns (view, storage); the storage shows writes past the view's columns."""
+    assert pad_bytes % 16 == 0
+    esz = torch.empty(0, dtype=dtype).element_size()
+    ld = (-(-cols * esz // 16) * 16 + pad_bytes) // esz
+    store = torch.empty(rows, max(ld, 1), dtype=dtype, device="cuda")
+    if fill is not None:
+        store.fill_(fill)
+    return store[:, :cols], store

@@ -51,6 +51,19 @@ def test_cast_argument_validation(lib):
     assert f(A16, 1, 4, 4, 4, 0, A16, A16, 3, None, 0, None, None) == INVALID    # ld_q < cols
     assert f(A16, 1, 4, 8, 8, 0, A16, None, 0, A16, 3, None, None) == INVALID    # ld_qt < rows
     assert f(P(4097), 1, 4, 4, 4, 0, A16, A16, 4, None, 0, None, None) == INVALID  # misaligned bf16
+    # every data pointer starts on a 16-byte boundary
+    assert f(P(4096 + 8), 1, 4, 4, 4, 0, A16, A16, 4, None, 0, None, None) == INVALID
+    assert f(A16, 1, 4, 4, 4, 0, A16, P(4096 + 4), 4, None, 0, None, None) == INVALID
+    assert f(A16, 1, 4, 16, 16, 0, A16, None, 0, P(4096 + 2), 16, None, None) == INVALID
+    # a strided (or transposed) BF16 call needs 16-byte row pitches
+    assert f(A16, 1, 4, 4, 12, 0, A16, A16, 16, None, 0, None, None) == INVALID  # ld_x of 24 bytes
+    assert f(A16, 1, 4, 4, 16, 0, A16, A16, 8, None, 0, None, None) == INVALID   # ld_q of 8 bytes
+    assert f(A16, 1, 4, 16, 16, 0, A16, None, 0, A16, 8, None, None) == INVALID  # ld_qt of 8 bytes
+    # fp32 sources: contiguous codes only
+    assert f(A16, 0, 4, 4, 8, 0, A16, A16, 16, None, 0, None, None) == UNSUPPORTED  # strided fp32
+    assert f(A16, 0, 4, 4, 4, 0, A16, None, 0, A16, 16, None, None) == UNSUPPORTED  # fp32 with q_t
+    # one row is a contiguous run whatever its leading dimensions
+    assert f(A16, 1, 1, 4, 4, 0, None, None, 0, None, 0, None, None) == OK
     assert f(A16, 1, 0, 4, 4, 0, None, None, 0, None, 0, None, None) == OK       # empty
     assert f(A16, 1, 4, 4, 4, 0, None, None, 0, None, 0, None, None) == OK       # nothing requested
 
@@ -79,6 +92,9 @@ def test_batched_cast_validation(lib):
     assert f(2, arr(item(), item(x=None)), None) == INVALID       # every item is checked
     assert f(1, arr(item(scale=None)), None) == INVALID           # codes need a scale
     assert f(1, arr(item(x=4097)), None) == INVALID               # misaligned BF16 source
+    assert f(1, arr(item(x=4096 + 8)), None) == INVALID           # source not on a 16-byte boundary
+    assert f(1, arr(item(q=12288 + 4)), None) == INVALID          # codes not on a 16-byte boundary
+    assert f(1, arr(item(x_dtype=0, x=4096 + 4)), None) == INVALID
     assert f(1, arr(item(amax=4098)), None) == INVALID
 
 
@@ -114,9 +130,13 @@ def test_gemm_argument_validation(lib, name):
     assert f(*args(c=None)) == INVALID
     assert f(*args(sa=None)) == INVALID
     assert f(*args(k=24, lda=32, ldb=32)) == UNSUPPORTED       # k % 16
-    assert f(*args(lda=40)) == UNSUPPORTED                      # lda % 16
-    assert f(*args(a=P(4096 + 8))) == UNSUPPORTED               # a not 16-byte aligned
+    assert f(*args(lda=40)) == INVALID                          # lda not a multiple of 16 bytes
+    assert f(*args(ldb=40)) == INVALID
+    assert f(*args(a=P(4096 + 8))) == INVALID                   # a not 16-byte aligned
+    assert f(*args(b=P(4096 + 1))) == INVALID
     assert f(*args(c=P(4097))) == INVALID                       # c not 2-byte aligned
+    assert f(*args(c=P(4096 + 2))) == INVALID                   # c not 16-byte aligned
+    assert f(*args(ldc=12)) == INVALID                          # ldc not a multiple of 8 elements
     assert f(*args(m=0)) == OK
     assert f(*args(lda=2**22 + 16)) == UNSUPPORTED              # a tile's rows would pass 32-bit offsets
     assert f(*args(ldb=2**22 + 16)) == UNSUPPORTED
@@ -128,11 +148,14 @@ def test_fused_gemm_argument_validation(lib, name):
     args = lambda **kw: [kw.get("a", A16), kw.get("af", 0), kw.get("lda", 32), kw.get("b", A16), kw.get("bf", 0),
                          kw.get("ldb", 32), kw.get("m", 4), kw.get("n", 8), kw.get("k", 32),
                          kw.get("sa", A16), kw.get("sb", A16), kw.get("c", A16), kw.get("ldc", 8),
-                         kw.get("yf", 0), kw.get("ys", A16), kw.get("yq", A16), kw.get("ldq", 8),
+                         kw.get("yf", 0), kw.get("ys", A16), kw.get("yq", A16), kw.get("ldq", 16),
                          kw.get("ya", A16), None]
     assert f(*args(af=3)) == INVALID                            # the GEMM's own rules apply
     assert f(*args(c=None, yq=None, ya=None)) == INVALID         # c may be NULL only with another output
-    assert f(*args(lda=40)) == UNSUPPORTED
+    assert f(*args(lda=40)) == INVALID
+    assert f(*args(k=24, lda=32, ldb=32)) == UNSUPPORTED
+    assert f(*args(yq=P(4096 + 8))) == INVALID                 # y_q not 16-byte aligned
+    assert f(*args(ldq=24)) == INVALID                          # ld_yq not a multiple of 16
     assert f(*args(yf=2)) == INVALID
     assert f(*args(yf=2, yq=None, ya=None)) == INVALID          # y_fmt checked even without y outputs
     assert f(*args(ys=None)) == INVALID                         # y_q needs a scale
@@ -239,11 +262,11 @@ def test_valid_calls_without_device_report_no_device(lib):
     assert lib.fp8_scale_update(A16, 4, 0, 0, A16, A16, None) == NO_DEVICE
     assert lib.fp8_amax_cast(A16, 1, 4, 4, 4, 0, A16, A16, 4, None, 0, A16, None) == NO_DEVICE
     assert lib.fp8_scaled_gemm(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE
-    assert lib.fp8_scaled_gemm_amax_cast(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, 0, A16, A16, 8, A16,
+    assert lib.fp8_scaled_gemm_amax_cast(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, 0, A16, A16, 16, A16,
                                          None) == NO_DEVICE
     assert lib.fp8_scaled_gemm_fast_accum(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, None) == NO_DEVICE
     assert lib.fp8_scaled_gemm_amax_cast_fast_accum(A16, 0, 32, A16, 0, 32, 4, 8, 32, A16, A16, A16, 8, 0, A16, A16,
-                                                    8, A16, None) == NO_DEVICE
+                                                    16, A16, None) == NO_DEVICE
     assert lib.fp8_layernorm_amax_cast(A16, 1, 4, 8, 8, A16, None, 1e-5, A16, 8, 0, A16, A16, 8, A16, None, None,
                                        None) == NO_DEVICE
     assert lib.fp8_reduce_shared_scale(A16, 1, 4, 64, 64, A16, A16, 1, None) == NO_DEVICE

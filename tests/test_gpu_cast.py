@@ -2,8 +2,9 @@
 
 Exhaustive over all 65536 BF16 inputs at a set of scales, structured fp32
 sweeps around every rounding boundary, special values, and every layout path
-(flat with a ragged tail, 2-D tiles with ragged edges, strided, unaligned,
-transposed copy, amax only, empty).
+(flat with a ragged tail, 2-D tiles with ragged edges, strided views,
+transposed copy, amax only, empty), and the refusal of layouts the kernels do
+not take (misaligned starts or row pitches, strided or transposed fp32).
 """
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ import torch
 import oracle
 import workloads as wl
 from oracle.codec import FMT, decode_table
-from tests.gpu_util import banner, dev, f32, f32_bits, first_diff, host, require_gpu
+from tests.gpu_util import banner, dev, f32, f32_bits, first_diff, host, pitched, require_gpu
 
 import fp8_mixed_precision_cast_amd as fp8
 
@@ -26,10 +27,18 @@ def _amax_bits(a) -> int:
 
 
 def _run_cast(x_np, dtype, fmt, scale, with_q=True, with_qt=False, amax0=0.0):
-    xd = dev(x_np)
+    """Contiguous source and codes (the flat kernels); with the transposed copy, a BF16 source and code
+    buffers with 16-byte row pitches (the tile kernel)."""
     rows, cols = x_np.shape
-    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda") if with_q else None
-    qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda") if with_qt else None
+    if with_qt:
+        xd, _ = pitched(rows, cols, torch.int16)
+        xd.copy_(dev(x_np))
+        q = pitched(rows, cols, torch.uint8)[0] if with_q else None
+        qt = pitched(cols, rows, torch.uint8)[0]
+    else:
+        xd = dev(x_np)
+        q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda") if with_q else None
+        qt = None
     am = f32(amax0)
     fp8.fp8_amax_cast(xd, fmt, f32(scale), q, qt, am)
     return (host(q) if with_q else None), (host(qt) if with_qt else None), f32_bits(am)[0]
@@ -134,25 +143,23 @@ def test_layouts_with_transpose(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_strided_and_unaligned_views(fmt):
+def test_strided_views(fmt):
     require_gpu()
     base = _bf16_matrix(130, 320, 5)
     xd_full = dev(base)
     s = 3.5
-    # (rows, cols of the source view, left pad of the q buffer)
+    # (rows, cols of the source view): every view starts on a 16-byte boundary, rows 640 bytes apart
     cases = {
-        "col-slice-unaligned": (slice(0, 130), slice(3, 203), 1),    # odd start, ld 320
-        "row-slice": (slice(1, 129), slice(0, 320), 0),              # contiguous rows, offset start
-        "strided-vector": (slice(0, 128), slice(0, 256), 0),         # ld 320 (640 B rows), tile vector path
-        "strided-ragged": (slice(2, 130), slice(64, 300), 0),        # ld 320, ragged right edge
+        "row-slice": (slice(1, 129), slice(0, 320)),                 # contiguous rows, offset start
+        "strided-vector": (slice(0, 128), slice(0, 256)),            # ld 320, full tiles
+        "strided-ragged": (slice(2, 130), slice(64, 300)),           # ld 320, ragged right and bottom edges
     }
-    for name, (rs, cs, pad) in cases.items():
+    for name, (rs, cs) in cases.items():
         banner("strided", fmt, name)
         xv = xd_full[rs, cs]
         rows, cols = xv.shape
-        q_store = torch.zeros(rows, cols + 2 * pad, dtype=torch.uint8, device="cuda")
-        q = q_store[:, pad:cols + pad]
-        qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+        q, q_store = pitched(rows, cols, torch.uint8, fill=0x5A, pad_bytes=16)
+        qt, _ = pitched(cols, rows, torch.uint8)
         am = f32(0.0)
         fp8.fp8_amax_cast(xv, fmt, f32(s), q, qt, am)
         xh = base[rs, cs]
@@ -160,12 +167,43 @@ def test_strided_and_unaligned_views(fmt):
         assert np.array_equal(host(q), want), first_diff(host(q), want)
         assert np.array_equal(host(qt), want.T)
         assert f32_bits(am)[0] == _amax_bits(oracle.amax(xh, "bf16"))
-        if pad:
-            assert not host(q_store)[:, :pad].any() and not host(q_store)[:, cols + pad:].any()
+        assert (host(q_store)[:, cols:] == 0x5A).all(), "wrote past cols"
         # the same view cast without the transposed copy (tile path, q only)
-        q2 = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+        q2, _ = pitched(rows, cols, torch.uint8)
         fp8.fp8_amax_cast(xv, fmt, f32(s), q2, None, None)
         assert np.array_equal(host(q2), want)
+
+
+def test_layouts_the_kernels_do_not_take_are_refused():
+    """Starts or row pitches that are not multiples of 16 bytes are invalid arguments; fp32 sources
+    that are strided or need the transposed copy are unsupported. Nothing is written."""
+    require_gpu()
+    base = dev(_bf16_matrix(130, 320, 5))
+    q, _ = pitched(130, 200, torch.uint8, fill=0x5A)
+    qt, _ = pitched(200, 130, torch.uint8, fill=0x5A)
+    f32src = torch.zeros(64, 64, dtype=torch.float32, device="cuda")
+    cases = {
+        "source start not 16-byte aligned": (base[:, 3:203], q, qt, 1),
+        "source rows 2 elements apart from 16-byte": (torch.zeros(130, 204, dtype=torch.int16, device="cuda")[:, :200],
+                                                      q, qt, 1),
+        "codes start not 16-byte aligned": (base[:, :200], torch.zeros(130, 216, dtype=torch.uint8,
+                                                                       device="cuda")[:, 8:208], None, 1),
+        "codes pitch not a multiple of 16": (base[:, :200], torch.zeros(130, 200, dtype=torch.uint8, device="cuda"),
+                                             None, 1),
+        "transposed codes pitch not a multiple of 16": (base[:, :200], None,
+                                                        torch.zeros(200, 130, dtype=torch.uint8, device="cuda"), 1),
+        "fp32 with a transposed copy": (f32src, None, torch.zeros(64, 64, dtype=torch.uint8, device="cuda"), 2),
+        "strided fp32": (torch.zeros(64, 128, dtype=torch.float32, device="cuda")[:, :64],
+                         torch.zeros(64, 64, dtype=torch.uint8, device="cuda"), None, 2),
+    }
+    for name, (x, qq, qqt, status) in cases.items():
+        banner("refused", name)
+        am = f32(0.0)
+        with pytest.raises(fp8.Fp8mpError) as ei:
+            fp8.fp8_amax_cast(x, "e4m3", f32(1.0), qq, qqt, am)
+        assert ei.value.status == status, name
+        assert f32_bits(am)[0] == 0, name
+    assert (host(q) == 0x5A).all() and (host(qt) == 0x5A).all()
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -219,9 +257,10 @@ def test_invalid_arguments_raise():
 
 
 def test_batched_cast_equals_separate_calls():
-    """fp8_amax_cast_batched over 11 items (two batched launches plus fallbacks): BF16 with ragged tails, an
-    unaligned view and an fp32 source (both take the single-tensor kernels), amax-only and codes-only items,
-    an empty one; codes and amax bit-identical to separate fp8_amax_cast calls and to the oracle."""
+    """fp8_amax_cast_batched over 11 items (two batched launches plus the fp32 source's own kernel): BF16
+    with ragged tails, amax-only and codes-only items, an empty one; codes and amax bit-identical to the
+    oracle. An item whose source or codes do not start on a 16-byte boundary makes the whole call an
+    invalid argument, refused before anything runs."""
     require_gpu()
     import workloads as wl
     rng = np.random.default_rng(77)
@@ -231,12 +270,8 @@ def test_batched_cast_equals_separate_calls():
         fmt = "e4m3" if k % 2 == 0 else "e5m2"
         x = wl.small_normal(500 + k, (1, max(n, 1)), std=float(np.exp2(rng.uniform(-4, 4))), outlier_factor=20.0)
         x = x[:, :n]
-        if k == 6:
-            src = torch.zeros(n + 1, dtype=torch.int16, device="cuda")
-            src[1:] = dev(x[0])
-            xt = src[1:]                                  # 2-byte aligned only: fallback kernels
-        elif k == 8:
-            xt = dev(oracle.bf16_to_f32(x[0]))            # fp32 source: fallback kernels
+        if k == 8:
+            xt = dev(oracle.bf16_to_f32(x[0]))            # fp32 source: its own flat kernel
         else:
             xt = dev(x[0]) if n else torch.zeros(0, dtype=torch.int16, device="cuda")
         s = np.float32(np.exp2(rng.uniform(-6, 6)))
@@ -254,6 +289,14 @@ def test_batched_cast_equals_separate_calls():
             assert np.array_equal(host(q), want), (k, first_diff(host(q), want))
         if am is not None:
             assert f32_bits(am)[0] == np.float32(oracle.amax(src, dtype)).view(np.uint32), k
+    banner("batched-cast misaligned item")
+    src = torch.zeros(4097, dtype=torch.int16, device="cuda")
+    q = torch.full((4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    am = f32(0.0)
+    with pytest.raises(fp8.Fp8mpError) as ei:
+        fp8.fp8_amax_cast_batched([(dev(np.ones(64, np.uint16)), "e4m3", f32(1.0), None, am),
+                                   (src[1:], "e4m3", f32(1.0), q, None)])
+    assert ei.value.status == 1 and f32_bits(am)[0] == 0 and (host(q) == 0x5A).all()
 
 
 def test_beyond_two_to_the_31_elements():
@@ -297,12 +340,16 @@ def test_beyond_two_to_the_31_elements():
         del q
         torch.cuda.empty_cache()
     banner("cast-transpose >2^31")
-    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
-    qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+    xp, xp_store = pitched(rows, cols, torch.int16)   # 16-byte row pitch for the tile kernel
+    xp.copy_(x2)
+    del x, x2
+    torch.cuda.empty_cache()
+    q, _ = pitched(rows, cols, torch.uint8)
+    qt, _ = pitched(cols, rows, torch.uint8)
     am = f32(0.0)
-    fp8.fp8_amax_cast(x2, "e4m3", f32(s), q, qt, am)
+    fp8.fp8_amax_cast(xp, "e4m3", f32(s), q, qt, am)
     r, c = idx // cols, idx % cols
-    got_q = host(q.view(-1)[ti])
+    got_q = host(q[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()])
     got_qt = host(qt[torch.from_numpy(c).cuda(), torch.from_numpy(r).cuda()])
     want = oracle.cast(xs, np.float32(s), "e4m3", "bf16")
     assert np.array_equal(got_q, want), first_diff(got_q, want)

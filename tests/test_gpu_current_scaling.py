@@ -10,7 +10,7 @@ import torch
 import oracle
 import workloads as wl
 from oracle.recipe import update_scale
-from tests.gpu_util import banner, dev, host, require_gpu
+from tests.gpu_util import banner, dev, host, pitched, require_gpu
 
 import fp8_mixed_precision_cast_amd as fp8
 from fp8_mixed_precision_cast_amd.linear import plan_from_workload
@@ -36,8 +36,8 @@ def test_current_scaling_codes_and_scales(fmt, margin):
         x = wl.small_normal(shape[0] + margin, shape, std=std, outlier_factor=20.0)
         banner("current", fmt, margin, shape)
         st = fp8.CurrentScalingState(fmt, margin)
-        q = torch.empty(*shape, dtype=torch.uint8, device="cuda")
-        qt = torch.empty(shape[1], shape[0], dtype=torch.uint8, device="cuda")
+        q, _ = pitched(shape[0], shape[1], torch.uint8)
+        qt, _ = pitched(shape[1], shape[0], torch.uint8)
         st.cast(dev(x), q, qt)
         s, si = _jit_scale(x, "bf16", fmt, margin)
         assert _bits(host(st.scale))[0] == _bits(s) and _bits(host(st.scale_inv))[0] == _bits(si)

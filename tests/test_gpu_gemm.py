@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle.codec import FMT
-from tests.gpu_util import banner, dev, f32, host, require_gpu
+from tests.gpu_util import banner, dev, f32, host, pitched, require_gpu
 
 import fp8_mixed_precision_cast_amd as fp8
 
@@ -38,12 +38,10 @@ def _check(a, af, b, bf, sa, sb, y_bits, tag):
 
 def _run(a, af, b, bf, sa, sb, ldc_pad=0):
     m, n = a.shape[0], b.shape[0]
-    c_store = torch.zeros(m, n + ldc_pad, dtype=torch.int16, device="cuda")
-    c = c_store[:, :n]
+    c, c_store = pitched(m, n, torch.int16, fill=0, pad_bytes=2 * ldc_pad)
     fp8.fp8_scaled_gemm(dev(a), af, dev(b), bf, f32(sa), f32(sb), c)
     out = host(c_store)
-    if ldc_pad:
-        assert not out[:, n:].any(), "wrote past n"
+    assert not out[:, n:].any(), "wrote past n"
     return out[:, :n]
 
 
@@ -72,7 +70,7 @@ def test_gemm_all_codes_and_strided_operands():
     a_full = _codes(rng, (m, k + 64), "e5m2")
     b_full = _codes(rng, (n, k + 32), "e4m3")
     ad, bd = dev(a_full)[:, 16:16 + k], dev(b_full)[:, 32:32 + k]
-    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    c, _ = pitched(m, n, torch.int16, fill=0)
     banner("gemm-strided")
     fp8.fp8_scaled_gemm(ad, "e5m2", bd, "e4m3", f32(2.0 ** -10), f32(3.0), c)
     _check(a_full[:, 16:16 + k], "e5m2", b_full[:, 32:32 + k], "e4m3", 2.0 ** -10, 3.0, host(c), "strided")
@@ -103,13 +101,29 @@ def test_gemm_nan_inputs_and_degenerate_sizes():
                         torch.zeros(0, 8, dtype=torch.int16, device="cuda"))
 
 
-def test_gemm_rejects_unsupported_k():
+def test_gemm_rejects_unsupported_k_and_misaligned_buffers():
+    """K not a multiple of 16 is a shape the kernel does not tile (unsupported); operands or outputs
+    whose start or row pitch is not a multiple of 16 bytes are invalid arguments, refused before
+    anything runs (the output keeps its contents)."""
     require_gpu()
     a = torch.zeros(16, 24, dtype=torch.uint8, device="cuda")
-    c = torch.zeros(16, 16, dtype=torch.int16, device="cuda")
+    c = torch.full((16, 16), 7, dtype=torch.int16, device="cuda")
     with pytest.raises(fp8.Fp8mpError) as ei:
         fp8.fp8_scaled_gemm(a, "e4m3", a, "e4m3", f32(1.0), f32(1.0), c)
     assert ei.value.status == 2
+    a = torch.zeros(16, 64, dtype=torch.uint8, device="cuda")
+    store = torch.zeros(16, 80, dtype=torch.uint8, device="cuda")
+    cases = {"a offset by 8 bytes": (store[:, 8:72], a, c),
+             "lda of 40 bytes": (torch.zeros(16, 40, dtype=torch.uint8, device="cuda")[:, :32],
+                                 torch.zeros(16, 32, dtype=torch.uint8, device="cuda"), c),
+             "c offset by 2 bytes": (a, a, torch.zeros(16, 24, dtype=torch.int16, device="cuda")[:, 1:17]),
+             "ldc of 20 elements": (a, a, torch.zeros(16, 20, dtype=torch.int16, device="cuda")[:, :16])}
+    for name, (aa, bb, cc) in cases.items():
+        before = host(cc).copy()
+        with pytest.raises(fp8.Fp8mpError) as ei:
+            fp8.fp8_scaled_gemm(aa, "e4m3", bb, "e4m3", f32(1.0), f32(1.0), cc)
+        assert ei.value.status == 1, name
+        assert np.array_equal(host(cc), before), name
 
 
 def test_gemm_output_beyond_two_to_the_31_elements():
@@ -152,7 +166,7 @@ def test_gemm_at_the_largest_leading_dimension():
     b_store = torch.zeros(n, ld, dtype=torch.uint8, device="cuda")
     a_store[:, :k] = dev(a)
     b_store[:, :k] = dev(b)
-    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    c, _ = pitched(m, n, torch.int16, fill=0)
     banner("gemm max ld")
     fp8.fp8_scaled_gemm(a_store[:, :k], "e4m3", b_store[:, :k], "e5m2", f32(sa), f32(sb), c)
     _check(a, "e4m3", b, "e5m2", sa, sb, host(c), "max ld")

@@ -14,7 +14,7 @@ import torch
 import oracle
 from oracle.codec import FMT
 from oracle.gemm import FAST_ACCUM_SUM_COEF
-from tests.gpu_util import banner, dev, f32, first_diff, host, require_gpu
+from tests.gpu_util import banner, dev, f32, first_diff, host, pitched, require_gpu
 
 import fp8_mixed_precision_cast_amd as fp8
 
@@ -44,8 +44,8 @@ def _pow2_rows(rng, shape, fmt):
 
 def _gemm(call, a, af, b, bf, sa, sb):
     m, n = a.shape[0], b.shape[0]
-    c_store = torch.zeros(m, n + 8, dtype=torch.int16, device="cuda")
-    call(dev(a), af, dev(b), bf, f32(sa), f32(sb), c_store[:, :n])
+    c, c_store = pitched(m, n, torch.int16, fill=0, pad_bytes=16)
+    call(dev(a), af, dev(b), bf, f32(sa), f32(sb), c)
     out = host(c_store)
     assert not out[:, n:].any(), "wrote past n"
     return out[:, :n]
@@ -124,7 +124,7 @@ def test_fast_gemm_fused_output_cast_matches_its_own_output(y_fmt):
     banner("gemm-fast-fused", y_fmt)
     c_plain = _gemm(fp8.fp8_scaled_gemm_fast_accum, a, "e4m3", b, "e4m3", sa, sb)
     c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
-    yq = torch.zeros(m, n, dtype=torch.uint8, device="cuda")
+    yq, _ = pitched(m, n, torch.uint8, fill=0)
     yamax = torch.zeros(1, dtype=torch.float32, device="cuda")
     ys = np.float32(0.37)
     fp8.fp8_scaled_gemm_amax_cast_fast_accum(dev(a), "e4m3", dev(b), "e4m3", f32(sa), f32(sb), c, y_fmt,
@@ -271,7 +271,7 @@ def test_fast_gemm_at_the_largest_leading_dimension():
     b_store = torch.zeros(n, ld, dtype=torch.uint8, device="cuda")
     a_store[:, :k] = dev(a)
     b_store[:, :k] = dev(b)
-    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    c, _ = pitched(m, n, torch.int16, fill=0)
     banner("gemm-fast max ld")
     fp8.fp8_scaled_gemm_fast_accum(a_store[:, :k], "e4m3", b_store[:, :k], "e5m2", f32(sa), f32(sb), c)
     ref = oracle.gemm_ref(a, "e4m3", b, "e5m2", sa, sb)

@@ -3,8 +3,9 @@
 Its BF16 output must be the plain GEMM's, bit for bit, and within the GEMM
 bound of the oracle's FP64 product; its amax and FP8 copy must equal, bit for
 bit, the oracle's amax and cast applied to that BF16 output (the definition of
-the fused call), across ragged shapes, both output formats, strided and
-unaligned code outputs, saturating and underflowing scales and NaN outputs.
+the fused call), across ragged shapes, both output formats, code outputs with
+wider row pitches, saturating and underflowing scales and NaN outputs. A code
+output whose start or row pitch is not a multiple of 16 bytes is refused.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ import torch
 
 import oracle
 from oracle.codec import FMT
-from tests.gpu_util import banner, dev, f32, first_diff, host, require_gpu
+from tests.gpu_util import banner, dev, f32, first_diff, host, pitched, require_gpu
 
 import fp8_mixed_precision_cast_amd as fp8
 
@@ -31,13 +32,14 @@ def _bits(v):
 
 
 def _fused(a, af, b, bf, sa, sb, yf, ys, amax0=0.0, ldq_pad=0, want_q=True, want_amax=True):
+    """ldq_pad: extra bytes (a multiple of 16) in the row pitch of y_q beyond n rounded up to 16."""
     m, n = a.shape[0], b.shape[0]
     da, db = dev(a), dev(b)
-    c_plain = torch.zeros(m, n, dtype=torch.int16, device="cuda")
+    c_plain, _ = pitched(m, n, torch.int16, fill=0)
     fp8.fp8_scaled_gemm(da, af, db, bf, f32(sa), f32(sb), c_plain)
-    c = torch.zeros(m, n, dtype=torch.int16, device="cuda")
-    q_store = torch.full((m, n + ldq_pad), 0x5A, dtype=torch.uint8, device="cuda")
-    q = q_store[:, :n] if want_q else None
+    c, _ = pitched(m, n, torch.int16, fill=0)
+    q, q_store = pitched(m, n, torch.uint8, fill=0x5A, pad_bytes=ldq_pad)
+    q = q if want_q else None
     am = f32(amax0) if want_amax else None
     fp8.fp8_scaled_gemm_amax_cast(da, af, db, bf, f32(sa), f32(sb), c, yf, f32(ys) if want_q else None, q, am)
     cb = host(c)
@@ -46,8 +48,7 @@ def _fused(a, af, b, bf, sa, sb, yf, ys, amax0=0.0, ldq_pad=0, want_q=True, want
         qs = host(q_store)
         want = oracle.cast(cb, np.float32(ys), yf, "bf16")
         assert np.array_equal(qs[:, :n], want), first_diff(qs[:, :n], want)
-        if ldq_pad:
-            assert (qs[:, n:] == 0x5A).all(), "wrote past n in y_q"
+        assert (qs[:, n:] == 0x5A).all(), "wrote past n in y_q"
     if want_amax:
         want_a = oracle.max_nan([np.float32(amax0), oracle.amax(cb, "bf16")])
         assert _bits(host(am)[0]) == _bits(want_a), (host(am)[0], want_a)
@@ -67,7 +68,7 @@ def test_fused_amax_cast_shapes(yf, shape):
         a, b = _codes(rng, (m, k), af), _codes(rng, (n, k), bf)
         sa, sb = np.float32(0.75), np.float32(3.0)
         c = None
-        for ys, pad in ((1.0, 0), (37.5, 5), (1e6, 8), (1e-30, 3)):    # plain, unaligned, saturating, underflow
+        for ys, pad in ((1.0, 0), (37.5, 16), (1e6, 32), (1e-30, 16)):  # plain, wider pitch, saturating, underflow
             banner("fused", af, bf, yf, shape, ys, pad)
             c = _fused(a, af, b, bf, sa, sb, yf, ys, amax0=0.0, ldq_pad=pad)
         ref = oracle.gemm_ref(a, af, b, bf, sa, sb)
@@ -182,9 +183,21 @@ def test_fused_without_bf16_output():
         a, b = _codes(rng, (m, k), "e4m3"), _codes(rng, (n, k), "e5m2")
         banner("fused-no-c", m, n, k)
         cb = _fused(a, "e4m3", b, "e5m2", 0.5, 2.0, "e4m3", 3.0)      # reference run with c
-        q = torch.empty(m, n, dtype=torch.uint8, device="cuda")
+        q, _ = pitched(m, n, torch.uint8)
         am = f32(0.0)
         fp8.fp8_scaled_gemm_amax_cast(dev(a), "e4m3", dev(b), "e5m2", f32(0.5), f32(2.0), None, "e4m3", f32(3.0), q, am)
         want = oracle.cast(cb, np.float32(3.0), "e4m3", "bf16")
         assert np.array_equal(host(q), want), first_diff(host(q), want)
         assert _bits(host(am)[0]) == _bits(oracle.amax(cb, "bf16"))
+
+
+def test_fused_refuses_misaligned_code_outputs():
+    require_gpu()
+    a = torch.zeros(32, 64, dtype=torch.uint8, device="cuda")
+    c = torch.zeros(32, 32, dtype=torch.int16, device="cuda")
+    store = torch.full((32, 64), 0x5A, dtype=torch.uint8, device="cuda")
+    for name, yq in (("offset by 8 bytes", store[:, 8:40]), ("pitch of 40 bytes", store[:, :40].contiguous()[:, :32])):
+        with pytest.raises(fp8.Fp8mpError) as ei:
+            fp8.fp8_scaled_gemm_amax_cast(a, "e4m3", a, "e4m3", f32(1.0), f32(1.0), c, "e4m3", f32(1.0), yq, None)
+        assert ei.value.status == 1, name
+    assert (host(store) == 0x5A).all()
