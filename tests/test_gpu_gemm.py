@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle.codec import FMT
-from tests.gpu_util import banner, dev, f32, host, pitched, require_gpu
+from tests.gpu_util import banner, dev, f32, first_diff, host, pitched, require_gpu
 
 import fp8_mixed_precision_cast_amd as fp8
 
@@ -232,3 +232,55 @@ def test_gemm_inverse_scale_pairs_whose_product_leaves_binary32(call):
         ref = oracle.gemm_ref(a, fmt, b, fmt, sa, sb)
         assert np.isfinite(ref).all() and (np.abs(ref) > 2.0 ** -126).all() and (np.abs(ref) < 2.0 ** 127).all()
         _check(a, fmt, b, fmt, sa, sb, y, f"{call} {fmt} scales {float(sa)} {float(sb)}")
+
+
+# Shapes whose tile count leaves a partly filled last round on 256 CUs, so the FP32-accumulation GEMM cuts
+# the remaining columns (or rows) into one round of narrow tiles: 256 x 192, 256 x 128, 192 x 256 and
+# 128 x 256, each with ragged edges in both directions. The fast GEMM runs the same shapes on whole tiles.
+NARROW_SHAPES = [(4000, 6900, 64), (4000, 4452, 48), (6900, 4000, 64), (4452, 4000, 32)]
+
+
+@pytest.mark.parametrize("shape", NARROW_SHAPES)
+@pytest.mark.parametrize("call", ["exact", "fast"])
+def test_gemm_launches_with_narrow_last_round(shape, call):
+    """Every output of launches whose last round runs narrow tiles, against the oracle (the FP32 bound
+    for the exact GEMM, the fast bound for the FP8 instruction), for two format pairs; on rows of
+    +-2**e codes (exact sums in both modes) the two GEMMs must give the same bits."""
+    require_gpu()
+    from oracle.gemm import FAST_ACCUM_SUM_COEF
+    m, n, k = shape
+    f = fp8.fp8_scaled_gemm if call == "exact" else fp8.fp8_scaled_gemm_fast_accum
+    coef = oracle.gemm.SUM_COEF if call == "exact" else FAST_ACCUM_SUM_COEF
+    rng = np.random.default_rng(m + 3 * n + 7 * k)
+    for af, bf in (("e4m3", "e4m3"), ("e5m2", "e4m3")):
+        a = _codes(rng, (m, k), af, spread=40)
+        b = _codes(rng, (n, k), bf, spread=40)
+        sa, sb = np.float32(0.5), np.float32(1 / 3.0)
+        banner("gemm narrow plan", call, af, bf, shape)
+        c, store = pitched(m, n, torch.int16, fill=0x7FC1, pad_bytes=16)
+        f(dev(a), af, dev(b), bf, f32(sa), f32(sb), c)
+        out = host(store)
+        assert (out[:, n:] == 0x7FC1).all(), "wrote past n"
+        ref = oracle.gemm_ref(a, af, b, bf, sa, sb)
+        absr = oracle.gemm_abs_ref(a, af, b, bf, sa, sb)
+        ok, worst = oracle.gemm_check(out[:, :n], ref, absr, coef)
+        assert ok, f"{call} {af}x{bf} {shape}: worst |err|/bound {worst}"
+    # exact sums: one magnitude per row of A and of B, so both GEMMs must agree bit for bit
+    e_a = rng.integers(4, 12, m)
+    e_b = rng.integers(4, 12, n)
+    a = ((e_a[:, None] << 3) | (rng.integers(0, 2, (m, k)) << 7)).astype(np.uint8)
+    b = ((e_b[:, None] << 3) | (rng.integers(0, 2, (n, k)) << 7)).astype(np.uint8)
+    c1, _ = pitched(m, n, torch.int16, fill=0)
+    c2, _ = pitched(m, n, torch.int16, fill=0)
+    fp8.fp8_scaled_gemm(dev(a), "e4m3", dev(b), "e4m3", f32(1.0), f32(1.0), c1)
+    f(dev(a), "e4m3", dev(b), "e4m3", f32(1.0), f32(1.0), c2)
+    assert np.array_equal(host(c1), host(c2)), first_diff(host(c1), host(c2))
+    assert np.array_equal(host(c1), host(torch.from_numpy(_exact_bits(a, b)).cuda()))
+
+
+def _exact_bits(a, b):
+    """BF16 bits of the exact product of E4M3 code rows (the oracle's FP64 sum, rounded to BF16)."""
+    ref = oracle.gemm_ref(a, "e4m3", b, "e4m3", 1.0, 1.0)
+    u = ref.astype(np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16).view(
+        np.int16)
