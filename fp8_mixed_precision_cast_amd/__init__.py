@@ -81,10 +81,10 @@ def load_library() -> ctypes.CDLL:
     lib.fp8_reduce_shared_scale.restype = ctypes.c_int
     fl = ctypes.c_float
     lib.fp8_adam_step.argtypes = [i64, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                  fl, fl, fl, fl, fl, fl, fl, vp]
+                                  fl, fl, fl, fl, fl, i64, vp]
     lib.fp8_adam_step.restype = ctypes.c_int
     lib.fp8_adam_step_weight_cast.argtypes = [i64, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                              vp, fl, fl, fl, fl, fl, fl, fl, ctypes.c_int, vp, vp, vp, vp]
+                                              vp, fl, fl, fl, fl, fl, i64, ctypes.c_int, vp, vp, vp, vp]
     lib.fp8_adam_step_weight_cast.restype = ctypes.c_int
     lib.fp8mp_status_string.argtypes = [ctypes.c_int]
     lib.fp8mp_status_string.restype = ctypes.c_char_p
@@ -316,9 +316,10 @@ def fp8_reduce_shared_scale(q, fmt, scale_inv, out, stream=None) -> None:
 
 
 def fp8_adam_step(grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w, w_dq_in, w_dq_out, w_scale,
-                  w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2, stream=None,
+                  w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay, step, stream=None,
                   wq=None, wq_fmt="e4m3", wq_scale=None, wq_amax=None) -> None:
-    """One Adam step over FP8 m (codes), FP16 v and tensor-scaled FP16 w (all updated in place).
+    """Adam step number `step` (1, 2, ...) over FP8 m (codes), FP16 v and tensor-scaled FP16 w (all
+    updated in place); the library forms the bias corrections from beta1, beta2 and step.
 
     With wq and/or wq_amax (fp8_adam_step_weight_cast): also wq = enc(W * wq_scale) and
     wq_amax = max(wq_amax, max |W|) for the stored master weights W = fp16 w * w_scale_inv."""
@@ -331,7 +332,7 @@ def fp8_adam_step(grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v,
     args = (n, _ptr(grad), _src_dtype(grad), _ptr(m_q), _ptr(m_dq_in), _ptr(m_dq_out), _ptr(m_scale),
             _ptr(m_scale_inv), _ptr(m_amax), _ptr(v), _ptr(w), _ptr(w_dq_in), _ptr(w_dq_out), _ptr(w_scale),
             _ptr(w_scale_inv), _ptr(w_amax), float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
-            float(bias_c1), float(bias_c2))
+            int(step))
     if wq is None and wq_amax is None:
         _check(load_library().fp8_adam_step(*args, _stream(stream)), "fp8_adam_step")
     else:
@@ -374,13 +375,12 @@ class AdamFP8State:
     def step(self, grad, stream=None) -> None:
         self.t += 1
         b1, b2 = self.hp["beta1"], self.hp["beta2"]
-        c1, c2 = 1.0 / (1.0 - b1 ** self.t), 1.0 / (1.0 - b2 ** self.t)
         i, o = self.cur, 1 - self.cur
         ms, ws = self.m_state, self.w_state
         qs = self.wq_state
         fp8_adam_step(grad.reshape(-1), self.m_q, self.m_dq[i:i + 1], self.m_dq[o:o + 1], ms.scale, ms.scale_inv,
                       ms.amax_slot, self.v, self.w, self.w_dq[i:i + 1], self.w_dq[o:o + 1], ws.scale, ws.scale_inv,
-                      ws.amax_slot, self.hp["lr"], b1, b2, self.hp["eps"], self.hp["weight_decay"], c1, c2, stream,
+                      ws.amax_slot, self.hp["lr"], b1, b2, self.hp["eps"], self.hp["weight_decay"], self.t, stream,
                       wq=self.wq, wq_fmt=qs.fmt if qs else "e4m3", wq_scale=qs.scale if qs else None,
                       wq_amax=qs.amax_slot if qs else None)
         ms.update(stream)

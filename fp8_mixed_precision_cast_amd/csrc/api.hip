@@ -21,8 +21,20 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];
 std::atomic<int> g_num_cus[kMaxDevices];
 
-bool valid_format(int f) { return f == FP8MP_E4M3 || f == FP8MP_E5M2; }
-bool valid_dtype(int d) { return d == FP8MP_F32 || d == FP8MP_BF16; }
+// A C caller may pass any int where the header names an enum, and in C++ reading
+// an out-of-range value as the enum type is undefined: the enum arguments are
+// read through their object representation, as int, and checked as such.
+template <class E>
+int raw(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+template <class E>
+bool valid_format(const E& f) { return raw(f) == FP8MP_E4M3 || raw(f) == FP8MP_E5M2; }
+template <class E>
+bool valid_dtype(const E& d) { return raw(d) == FP8MP_F32 || raw(d) == FP8MP_BF16; }
 
 fp8mp_status query_device(int* dev_out, hipDeviceProp_t* props_out) {
   int count = 0;
@@ -87,7 +99,9 @@ fp8mp_status check_gemm(const uint8_t* a, fp8mp_format a_fmt, int64_t lda, const
   if ((lda > 0 && m > (INT64_MAX / 8) / lda) || (ldb > 0 && n > (INT64_MAX / 8) / ldb) ||
       (c != nullptr && m > (INT64_MAX / 8) / ldc))
     return FP8MP_ERR_UNSUPPORTED;
-  if (((m + 127) / 128) * ((n + 127) / 128) > 0x7FFFFFFF) return FP8MP_ERR_UNSUPPORTED;
+  // the launch's tile count must fit an int (each factor is checked first, so the product cannot overflow)
+  const int64_t tiles_m = m / 128 + (m % 128 != 0), tiles_n = n / 128 + (n % 128 != 0);
+  if (tiles_m > 0x7FFFFFFF || tiles_n > 0x7FFFFFFF || tiles_m * tiles_n > 0x7FFFFFFF) return FP8MP_ERR_UNSUPPORTED;
   return FP8MP_OK;
 }
 
@@ -170,7 +184,7 @@ fp8mp_status fp8_amax_cast_batched(int32_t n_items, const fp8mp_cast_item* items
 
 fp8mp_status fp8_scale_update(float* amax_history, int32_t history_len, fp8mp_format fmt, int32_t margin,
                               float* scale, float* scale_inv, hipStream_t stream) {
-  if (!valid_format(fmt) && fmt != FP8MP_FP16) return FP8MP_ERR_INVALID_ARG;
+  if (!valid_format(fmt) && raw(fmt) != FP8MP_FP16) return FP8MP_ERR_INVALID_ARG;
   if (amax_history == nullptr || scale == nullptr || scale_inv == nullptr) return FP8MP_ERR_INVALID_ARG;
   if (history_len < 1 || margin < 0) return FP8MP_ERR_INVALID_ARG;
   if (!is_aligned(amax_history, 4) || !is_aligned(scale, 4) || !is_aligned(scale_inv, 4))
@@ -189,7 +203,7 @@ fp8mp_status fp8_scale_update_batched(int32_t n_tensors, float* const* amax_hist
   if (n_tensors == 0) return FP8MP_OK;
   if (!amax_histories || !history_lens || !fmts || !margins || !scales || !scale_invs) return FP8MP_ERR_INVALID_ARG;
   for (int32_t t = 0; t < n_tensors; ++t) {
-    if (!valid_format(fmts[t]) && fmts[t] != FP8MP_FP16) return FP8MP_ERR_INVALID_ARG;
+    if (!valid_format(fmts[t]) && raw(fmts[t]) != FP8MP_FP16) return FP8MP_ERR_INVALID_ARG;
     if (!amax_histories[t] || !scales[t] || !scale_invs[t]) return FP8MP_ERR_INVALID_ARG;
     if (history_lens[t] < 1 || margins[t] < 0) return FP8MP_ERR_INVALID_ARG;
     if (!is_aligned(amax_histories[t], 4) || !is_aligned(scales[t], 4) || !is_aligned(scale_invs[t], 4))
@@ -340,8 +354,9 @@ fp8mp_status check_adam(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uin
                         float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax, uint16_t* v,
                         uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
                         const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
-                        float weight_decay, float bias_c1, float bias_c2) {
+                        float weight_decay, int64_t step) {
   if (!valid_dtype(grad_dtype) || n < 0) return FP8MP_ERR_INVALID_ARG;
+  if (step < 1 || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f)) return FP8MP_ERR_INVALID_ARG;
   const void* required[] = {grad, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, v, w, w_dq_in, w_dq_out,
                             w_scale, w_scale_inv};
   for (const void* p : required)
@@ -353,10 +368,16 @@ fp8mp_status check_adam(int64_t n, const void* grad, fp8mp_dtype grad_dtype, uin
     if (p != nullptr && !is_aligned(p, 4)) return FP8MP_ERR_INVALID_ARG;
   if (!is_aligned(grad, grad_dtype == FP8MP_BF16 ? 2 : 4) || !is_aligned(v, 2) || !is_aligned(w, 2))
     return FP8MP_ERR_INVALID_ARG;
-  const float hp[] = {lr, beta1, beta2, eps, weight_decay, bias_c1, bias_c2};
+  const float hp[] = {lr, beta1, beta2, eps, weight_decay};
   for (float x : hp)
     if (!std::isfinite(x)) return FP8MP_ERR_INVALID_ARG;
   return FP8MP_OK;
+}
+
+// Adam's bias correction 1 / (1 - beta^t), formed in binary64 from the binary32
+// beta and rounded once to binary32 (finite for 0 <= beta < 1 and t >= 1).
+float bias_correction(float beta, int64_t step) {
+  return (float)(1.0 / (1.0 - std::pow((double)beta, (double)step)));
 }
 
 }  // namespace
@@ -365,17 +386,18 @@ fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype, 
                            float* m_dq_out, const float* m_scale, const float* m_scale_inv, float* m_amax,
                            uint16_t* v, uint16_t* w, const float* w_dq_in, float* w_dq_out, const float* w_scale,
                            const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2, float eps,
-                           float weight_decay, float bias_c1, float bias_c2, hipStream_t stream) {
+                           float weight_decay, int64_t step, hipStream_t stream) {
   fp8mp_status st = check_adam(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w,
                                w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay,
-                               bias_c1, bias_c2);
+                               step);
   if (st != FP8MP_OK || n == 0) return st;
   int cus = 0;
   st = check_device(&cus);
   if (st != FP8MP_OK) return st;
   return from_hip(fp8mp::launch_adam_step(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax,
                                           v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2,
-                                          eps, weight_decay, bias_c1, bias_c2, -1, nullptr, nullptr, nullptr, cus,
+                                          eps, weight_decay, bias_correction(beta1, step),
+                                          bias_correction(beta2, step), -1, nullptr, nullptr, nullptr, cus,
                                           stream));
 }
 
@@ -384,12 +406,11 @@ fp8mp_status fp8_adam_step_weight_cast(int64_t n, const void* grad, fp8mp_dtype 
                                        const float* m_scale_inv, float* m_amax, uint16_t* v, uint16_t* w,
                                        const float* w_dq_in, float* w_dq_out, const float* w_scale,
                                        const float* w_scale_inv, float* w_amax, float lr, float beta1, float beta2,
-                                       float eps, float weight_decay, float bias_c1, float bias_c2,
-                                       fp8mp_format wq_fmt, const float* wq_scale, uint8_t* wq, float* wq_amax,
+                                       float eps, float weight_decay, int64_t step, fp8mp_format wq_fmt, const float* wq_scale, uint8_t* wq, float* wq_amax,
                                        hipStream_t stream) {
   fp8mp_status st = check_adam(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax, v, w,
                                w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2, eps, weight_decay,
-                               bias_c1, bias_c2);
+                               step);
   if (st != FP8MP_OK) return st;
   if (!valid_format(wq_fmt) || (wq == nullptr && wq_amax == nullptr) || (wq != nullptr && wq_scale == nullptr))
     return FP8MP_ERR_INVALID_ARG;
@@ -401,12 +422,13 @@ fp8mp_status fp8_adam_step_weight_cast(int64_t n, const void* grad, fp8mp_dtype 
   if (st != FP8MP_OK) return st;
   return from_hip(fp8mp::launch_adam_step(n, grad, grad_dtype, m_q, m_dq_in, m_dq_out, m_scale, m_scale_inv, m_amax,
                                           v, w, w_dq_in, w_dq_out, w_scale, w_scale_inv, w_amax, lr, beta1, beta2,
-                                          eps, weight_decay, bias_c1, bias_c2, wq_fmt, wq_scale, wq, wq_amax, cus,
+                                          eps, weight_decay, bias_correction(beta1, step),
+                                          bias_correction(beta2, step), wq_fmt, wq_scale, wq, wq_amax, cus,
                                           stream));
 }
 
 const char* fp8mp_status_string(fp8mp_status status) {
-  switch (status) {
+  switch (raw(status)) {
     case FP8MP_OK: return "ok";
     case FP8MP_ERR_INVALID_ARG: return "invalid argument";
     case FP8MP_ERR_UNSUPPORTED: return "unsupported shape, layout or alignment";

@@ -331,7 +331,7 @@ fp8mp_status fp8_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t
  *   g = grad; m = dec_e4m3(m_q) * m_dq_in; v = fp16 v; w = fp16 w * w_dq_in
  *   m = beta1 * m + (1 - beta1) * g
  *   v = beta2 * v + (1 - beta2) * (g * g)
- *   u = (m * bias_c1) / (sqrt(v * bias_c2) + eps)
+ *   u = (m * c1) / (sqrt(v * c2) + eps)
  *   w = w - lr * (u + weight_decay * w)
  *   m_q = enc_e4m3(m * m_scale); v = fp16(v); w = fp16(w * w_scale)
  * (FP16 stores: round to nearest even, saturating at +-65504; the FP8 store is
@@ -349,7 +349,11 @@ fp8mp_status fp8_reduce_shared_scale(const uint8_t* q, fp8mp_format fmt, int32_t
  *                     one fp32 each on the device (read).
  *   m_dq_out, w_dq_out  one fp32 each (written).
  *   m_amax, w_amax    one fp32 each (max-accumulated) or NULL.
- *   bias_c1, bias_c2  1 / (1 - beta1^t) and 1 / (1 - beta2^t) for step t.
+ *   step              t >= 1, the number of this step. The bias corrections are
+ *                     formed on the host in binary64 and rounded once to binary32:
+ *                     c1 = fp32(1 / (1 - beta1^t)), c2 = fp32(1 / (1 - beta2^t)),
+ *                     with beta1, beta2 the binary32 arguments widened
+ *                     (0 <= beta1, beta2 < 1, else FP8MP_ERR_INVALID_ARG).
  */
 fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype,
                            uint8_t* m_q, const float* m_dq_in, float* m_dq_out,
@@ -358,7 +362,7 @@ fp8mp_status fp8_adam_step(int64_t n, const void* grad, fp8mp_dtype grad_dtype,
                            uint16_t* w, const float* w_dq_in, float* w_dq_out,
                            const float* w_scale, const float* w_scale_inv, float* w_amax,
                            float lr, float beta1, float beta2, float eps, float weight_decay,
-                           float bias_c1, float bias_c2, hipStream_t stream);
+                           int64_t step, hipStream_t stream);
 
 /*
  * fp8_adam_step_weight_cast: fp8_adam_step, and in the same pass the FP8
@@ -389,7 +393,7 @@ fp8mp_status fp8_adam_step_weight_cast(int64_t n, const void* grad, fp8mp_dtype 
                                        uint16_t* w, const float* w_dq_in, float* w_dq_out,
                                        const float* w_scale, const float* w_scale_inv, float* w_amax,
                                        float lr, float beta1, float beta2, float eps, float weight_decay,
-                                       float bias_c1, float bias_c2,
+                                       int64_t step,
                                        fp8mp_format wq_fmt, const float* wq_scale, uint8_t* wq, float* wq_amax,
                                        hipStream_t stream);
 

@@ -49,7 +49,7 @@ from .recipe import (amax, cast, DelayedScaling, max_nan, primed_scale, update_s
 from .gemm import gemm_ref, gemm_abs_ref, gemm_bound, gemm_check, gemm_entry, gemm_ratio
 from .layernorm import layer_norm_bound, layer_norm_check, layer_norm_ref
 from .allreduce import reduce_bound, reduce_check, reduce_ref, shared_scale
-from .adam import (adam_step_f64, adam_step_ref, adam_weight_codes_ref, f16_decode, f16_encode,
+from .adam import (adam_step_f64, adam_step_ref, adam_weight_codes_ref, bias_corrections, f16_decode, f16_encode,
                    update_fp16_scale)
 
 __all__ = [
@@ -58,5 +58,5 @@ __all__ = [
     "gemm_ref", "gemm_abs_ref", "gemm_bound", "gemm_check", "gemm_entry", "gemm_ratio",
     "layer_norm_ref", "layer_norm_bound", "layer_norm_check",
     "shared_scale", "reduce_ref", "reduce_bound", "reduce_check",
-    "adam_step_ref", "adam_step_f64", "adam_weight_codes_ref", "f16_encode", "f16_decode", "update_fp16_scale",
+    "adam_step_ref", "adam_step_f64", "adam_weight_codes_ref", "bias_corrections", "f16_encode", "f16_decode", "update_fp16_scale",
 ]

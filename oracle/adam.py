@@ -10,8 +10,10 @@ moment in FP16 and the master weights in FP16 with tensor scaling, 6 bytes per
 parameter instead of 16. FP16 tops out at 65504 ([MPT] §定義, precision table).
 
 The pages name the storage precisions only. Readings taken:
-  * Adam with decoupled weight decay (wd = 0 is plain Adam), bias corrections
-    supplied by the caller as c1 = 1 / (1 - beta1**t), c2 = 1 / (1 - beta2**t);
+  * Adam with decoupled weight decay (wd = 0 is plain Adam); the bias
+    corrections of step t are c1 = 1 / (1 - beta1**t), c2 = 1 / (1 - beta2**t),
+    formed in float64 from the binary32 betas and rounded once to binary32
+    (`bias_corrections`);
   * the first moment is E4M3 codes with one scale per tensor; the master
     weights are FP16 values of w * s_w with one scale per tensor; both scales
     follow the delayed recipe (the step writes with the current scale and
@@ -42,6 +44,15 @@ from .codec import bf16_to_f32, decode_table
 from .recipe import cast, max_nan, update_scale_fmax
 
 FP16_MAX = 65504.0
+
+
+def bias_corrections(beta1, beta2, t: int):
+    """Adam's bias corrections of step t >= 1: fp32(1 / (1 - beta**t)) for each beta, with beta the
+    binary32 value widened to float64 and the power, difference and quotient taken in float64."""
+    if t < 1:
+        raise ValueError("step numbers start at 1")
+    b1, b2 = float(np.float32(beta1)), float(np.float32(beta2))
+    return np.float32(1.0 / (1.0 - b1 ** t)), np.float32(1.0 / (1.0 - b2 ** t))
 
 
 def f16_encode(x) -> np.ndarray:

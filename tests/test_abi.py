@@ -214,17 +214,20 @@ def test_adam_argument_validation(lib):
     def args(**kw):
         a = dict(n=64, g=B[0], gd=1, mq=B[1], mdi=B[2], mdo=B[3], ms=B[4], msi=B[5], ma=None, v=B[6], w=B[7],
                  wdi=B[8], wdo=B[9], ws=B[10], wsi=B[11], wa=None, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0,
-                 c1=10.0, c2=1000.0)
+                 t=7)
         a.update(kw)
         return [a[k] for k in ("n", "g", "gd", "mq", "mdi", "mdo", "ms", "msi", "ma", "v", "w", "wdi", "wdo", "ws",
-                               "wsi", "wa", "lr", "b1", "b2", "eps", "wd", "c1", "c2")] + [None]
+                               "wsi", "wa", "lr", "b1", "b2", "eps", "wd", "t")] + [None]
     assert f(*args(gd=4)) == INVALID
     assert f(*args(n=-1)) == INVALID
     assert f(*args(g=None)) == INVALID
     assert f(*args(mdo=B[2])) == INVALID                      # dequantisation factor read and written in place
     assert f(*args(wdo=B[8])) == INVALID
     assert f(*args(lr=float("nan"))) == INVALID
-    assert f(*args(c2=float("inf"))) == INVALID
+    assert f(*args(t=0)) == INVALID                           # step numbers start at 1
+    assert f(*args(b1=1.0)) == INVALID                        # 1 - beta^t must not vanish
+    assert f(*args(b2=-0.5)) == INVALID
+    assert f(*args(b1=float("nan"))) == INVALID
     assert f(*args(v=P(4097))) == INVALID
     assert f(*args(n=0)) == OK
     assert lib.fp8_amax_cast(A16, 1, 4, 4, 4, 2, A16, A16, 4, None, 0, None, None) == INVALID   # not for casts
@@ -233,10 +236,10 @@ def test_adam_argument_validation(lib):
 def _adam_wq_args(B, **kw):
     a = dict(n=64, g=B[0], gd=1, mq=B[1], mdi=B[2], mdo=B[3], ms=B[4], msi=B[5], ma=None, v=B[6], w=B[7],
              wdi=B[8], wdo=B[9], ws=B[10], wsi=B[11], wa=None, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0,
-             c1=10.0, c2=1000.0, qf=0, qs=B[12], q=B[13], qa=B[14])
+             t=7, qf=0, qs=B[12], q=B[13], qa=B[14])
     a.update(kw)
     return [a[k] for k in ("n", "g", "gd", "mq", "mdi", "mdo", "ms", "msi", "ma", "v", "w", "wdi", "wdo", "ws",
-                           "wsi", "wa", "lr", "b1", "b2", "eps", "wd", "c1", "c2", "qf", "qs", "q", "qa")] + [None]
+                           "wsi", "wa", "lr", "b1", "b2", "eps", "wd", "t", "qf", "qs", "q", "qa")] + [None]
 
 
 def test_adam_weight_cast_argument_validation(lib):

@@ -31,7 +31,13 @@ def _state(rng, n, g_dtype):
     return g, m_q, v, w
 
 
-HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01, c1=1 / (1 - 0.9 ** 7), c2=1 / (1 - 0.999 ** 7))
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01, step=7)
+
+
+def _ref_hp(hp):
+    """The oracle takes the bias corrections of the step; the library forms them from the step number."""
+    c1, c2 = oracle.bias_corrections(hp["beta1"], hp["beta2"], hp["step"])
+    return {**{k: v for k, v in hp.items() if k != "step"}, "c1": c1, "c2": c2}
 
 
 def _gpu_step(g, g_dtype, m_q, v, w, m_dq, m_scale, w_dq, w_scale, hp, offset=0):
@@ -47,7 +53,7 @@ def _gpu_step(g, g_dtype, m_q, v, w, m_dq, m_scale, w_dq, w_scale, hp, offset=0)
                                        ws=w_scale, wsi=np.float32(1) / np.float32(w_scale)).items()}
     mdo, wdo, ma, wa = f32(-1.0), f32(-1.0), f32(0.0), f32(0.0)
     fp8.fp8_adam_step(dg, dm, scal["mdi"], mdo, scal["ms"], scal["msi"], ma, dv, dw, scal["wdi"], wdo, scal["ws"],
-                      scal["wsi"], wa, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"], hp["c1"], hp["c2"])
+                      scal["wsi"], wa, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"], hp["step"])
     return (host(dm), host(dv), host(dw), host(ma)[0], host(wa)[0], host(mdo)[0], host(wdo)[0],
             host(scal["msi"])[0], host(scal["wsi"])[0])
 
@@ -71,7 +77,7 @@ def test_adam_step_bit_exact(g_dtype, n):
     for offset, (m_scale, w_scale) in ((0, (2.0 ** 14, 1024.0)), (1, (3000.0, 777.0)), (0, (1e6, 5e6))):
         m_dq, w_dq = np.float32(2.0 ** -14), np.float32(1 / 1024)
         banner("adam", g_dtype, n, offset, m_scale, w_scale)
-        ref = oracle.adam_step_ref(g, g_dtype, m_q, m_dq, m_scale, v, w, w_dq, w_scale, **HP)
+        ref = oracle.adam_step_ref(g, g_dtype, m_q, m_dq, m_scale, v, w, w_dq, w_scale, **_ref_hp(HP))
         got = _gpu_step(g, g_dtype, m_q, v, w, m_dq, m_scale, w_dq, w_scale, HP, offset)
         _compare(ref, got)
 
@@ -85,7 +91,7 @@ def test_adam_special_values():
     g[3], g[4], g[5] = np.nan, np.inf, -np.inf
     m_q[10:14] = 0
     v[10:14] = 0
-    ref = oracle.adam_step_ref(g, "f32", m_q, 2.0 ** -14, 2.0 ** 14, v, w, 1 / 1024, 1e9, **HP)
+    ref = oracle.adam_step_ref(g, "f32", m_q, 2.0 ** -14, 2.0 ** 14, v, w, 1 / 1024, 1e9, **_ref_hp(HP))
     banner("adam-special")
     got = _gpu_step(g, "f32", m_q, v, w, np.float32(2.0 ** -14), 2.0 ** 14, np.float32(1 / 1024), 1e9, HP)
     gm, gv, gw = got[0], got[1], got[2]
@@ -111,7 +117,7 @@ def _gpu_step_wq(g, g_dtype, m_q, v, w, m_dq, m_scale, w_dq, w_scale, hp, fmt, w
         buf = torch.full((n + offset + 1,), 0x5A, dtype=torch.uint8, device="cuda")
         wq = buf[offset:offset + n]
     fp8.fp8_adam_step(dg, dm, scal["mdi"], mdo, scal["ms"], scal["msi"], ma, dv, dw, scal["wdi"], wdo, scal["ws"],
-                      scal["wsi"], wa, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"], hp["c1"], hp["c2"],
+                      scal["wsi"], wa, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["wd"], hp["step"],
                       wq=wq, wq_fmt=fmt, wq_scale=scal["qs"], wq_amax=qa)
     if codes:
         hb = host(buf)
@@ -132,14 +138,14 @@ def test_adam_weight_codes_bit_exact(fmt, n):
     m_dq, w_dq = np.float32(2.0 ** -14), np.float32(1 / 1024)
     for offset, w_scale, q_scale in ((0, 1024.0, 448.0 / 0.08), (3, 777.0, 60.0), (0, 1024.0, 1e9)):
         banner("adam-wq", fmt, n, offset, w_scale, q_scale)
-        ref = oracle.adam_step_ref(g, "bf16", m_q, m_dq, 2.0 ** 14, v, w, w_dq, w_scale, **HP)
+        ref = oracle.adam_step_ref(g, "bf16", m_q, m_dq, 2.0 ** 14, v, w, w_dq, w_scale, **_ref_hp(HP))
         got, wq, qa = _gpu_step_wq(g, "bf16", m_q, v, w, m_dq, 2.0 ** 14, w_dq, w_scale, HP, fmt, q_scale, offset)
         _compare(ref, got)
         want_q, want_a = oracle.adam_weight_codes_ref(got[2], got[8], q_scale, fmt)
         assert np.array_equal(wq, want_q), "weight codes: " + first_diff(wq, want_q)
         assert _bits(qa) == _bits(oracle.max_nan([np.float32(0), want_a]))
     got, wq, qa = _gpu_step_wq(g, "bf16", m_q, v, w, m_dq, 2.0 ** 14, w_dq, 1024.0, HP, fmt, 1.0, codes=False)
-    _compare(oracle.adam_step_ref(g, "bf16", m_q, m_dq, 2.0 ** 14, v, w, w_dq, 1024.0, **HP), got)
+    _compare(oracle.adam_step_ref(g, "bf16", m_q, m_dq, 2.0 ** 14, v, w, w_dq, 1024.0, **_ref_hp(HP)), got)
     assert _bits(qa) == _bits(oracle.max_nan([np.float32(0), oracle.adam_weight_codes_ref(got[2], got[8], 1.0,
                                                                                           fmt)[1]]))
 
@@ -165,7 +171,7 @@ def test_adam_fp8_state_recipe_over_steps():
     m_h, w_h = np.zeros(L, np.float32), np.zeros(L, np.float32)
     for t in range(1, 13):
         g = f32_to_bf16_bits((rng.standard_normal(n) * 1e-2 * t).astype(np.float32))
-        c1, c2 = 1 / (1 - hp["beta1"] ** t), 1 / (1 - hp["beta2"] ** t)
+        c1, c2 = oracle.bias_corrections(hp["beta1"], hp["beta2"], t)
         m_q, v, w, ma, wa = oracle.adam_step_ref(g, "bf16", m_q, m_dq, m_s, v, w, w_dq, w_s, hp["lr"], hp["beta1"],
                                                  hp["beta2"], hp["eps"], hp["weight_decay"], c1, c2)
         m_dq, w_dq = m_si, w_si
@@ -208,10 +214,9 @@ def test_adam_full_size_weight():
     banner("adam-full", n)
     fp8.fp8_adam_step(grad, m_q, scal[0], mdo, scal[1], scal[2], ma, v.view(torch.int16), w.view(torch.int16),
                       scal[3], wdo, scal[4], scal[5], wa, **{k: v_ for k, v_ in zip(
-                          ("lr", "beta1", "beta2", "eps", "weight_decay", "bias_c1", "bias_c2"),
-                          (1e-4, 0.9, 0.95, 1e-8, 0.1, 1 / (1 - 0.9 ** 3), 1 / (1 - 0.95 ** 3)))})
+                          ("lr", "beta1", "beta2", "eps", "weight_decay", "step"), (1e-4, 0.9, 0.95, 1e-8, 0.1, 3))})
     ref = oracle.adam_step_ref(before[0], "bf16", before[1], 2.0 ** -20, 2.0 ** 20, before[2], before[3], 1 / 4096,
-                               4096.0, 1e-4, 0.9, 0.95, 1e-8, 0.1, 1 / (1 - 0.9 ** 3), 1 / (1 - 0.95 ** 3))
+                               4096.0, 1e-4, 0.9, 0.95, 1e-8, 0.1, *oracle.bias_corrections(0.9, 0.95, 3))
     assert np.array_equal(host(m_q[ti]), ref[0])
     assert np.array_equal(host(v.view(torch.int16)[ti]), ref[1])
     assert np.array_equal(host(w.view(torch.int16)[ti]), ref[2])

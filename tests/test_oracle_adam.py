@@ -115,3 +115,28 @@ def test_weight_codes_follow_the_stored_value_not_the_fp32_one():
     q, am = oracle.adam_weight_codes_ref(w, 1.0, 1.0, "e4m3")
     assert int(q[0]) == 0x38 and am == np.float32(1.0)
 
+
+
+def test_bias_corrections_exact_rationals():
+    """fp32(1 / (1 - beta**t)) from the binary32 beta: against exact rational arithmetic rounded to binary32
+    where the exact value is not within 2**-40 (relative) of a binary32 rounding boundary, for the usual
+    betas over many steps; t = 1 gives 1 / (1 - beta); the corrections fall towards 1 as t grows."""
+    from fractions import Fraction
+    for beta in (0.9, 0.95, 0.99, 0.999, 0.9999, 0.5, 0.0):
+        b = Fraction(float(np.float32(beta)))
+        prev = None
+        for t in (1, 2, 3, 7, 10, 100, 1000, 10000, 123457):
+            c1, _ = oracle.bias_corrections(beta, 0.5, t)
+            exact = 1 / (1 - b ** t)
+            lo = np.float32(float(exact))            # nearest binary32 (ties aside)
+            nb = np.nextafter(lo, np.float32(np.inf)) if Fraction(float(lo)) < exact else np.nextafter(lo, np.float32(0))
+            mid = (Fraction(float(lo)) + Fraction(float(nb))) / 2
+            if abs(exact - mid) > exact * Fraction(1, 2 ** 40):
+                assert c1 == lo, (beta, t, c1, lo)
+            if prev is not None:
+                assert c1 <= prev
+            prev = c1
+        assert oracle.bias_corrections(beta, beta, 1)[0] == np.float32(1 / (1 - float(np.float32(beta))))
+    assert oracle.bias_corrections(0.0, 0.0, 5) == (np.float32(1), np.float32(1))
+    with pytest.raises(ValueError):
+        oracle.bias_corrections(0.9, 0.999, 0)
