@@ -520,13 +520,18 @@ def main():
     if not args.no_clocks:
         sampler = ClockSampler()
         reps = max(1, int(3.0 / max(step_s, 1e-4)))
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
         with sampler:
             for _ in range(reps):
                 plan.step(dinp)
             torch.cuda.synchronize()
+        w1 = time.perf_counter()
         n_updates += reps
         clocks = sampler.summary()
         clocks["steps"] = reps
+        # eager steps back to back for seconds: the rate once power management has settled
+        clocks["window_ms_per_step"] = round((w1 - w0) / reps * 1e3, 4)
     cold_gbps, cold_ms = cold_cast_gbps(plan, dinp)
     other = "fast" if args.gemm_accum == "exact" else "exact"
     other_tflops = other_gemm_tflops(plan, other)
