@@ -10,14 +10,15 @@ K=4096; amax history 1024, margin 0).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp7b_up_fwd]
 
-Prints one JSON line. After W warm-up steps, K eager steps are timed with HIP
-events around every phase on the launch stream; they give `roofline` (the
-dominant kernel, the GEMM, per launch) and the per-phase `components`. Then the
-step is captured once as a HIP graph and K replays are timed, synchronized on
-both sides: `value` is the step's GEMM FLOPs divided by that step time (TFLOP/s,
-higher is better; `--no-graph` takes the eager steps instead, and the eager
-figure is reported either way). `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+Prints one JSON line. After W warm-up steps the step is captured once as a HIP
+graph and replayed untimed for --settle-seconds (the GPU's power management
+dips a few milliseconds into a burst and settles within a second or two); then
+K replays are timed, synchronized on both sides: `value` is the step's GEMM
+FLOPs divided by that step time (TFLOP/s, higher is better; `--no-graph` times
+eager steps instead). K eager steps follow directly, with HIP events around
+every phase on the launch stream: they give `roofline` (the dominant kernel,
+the GEMM, per launch) and the per-phase `components`. `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -40,6 +41,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-seconds", type=float, default=2.0,
+                    help="before the warm-up steps, repeat the step untimed for this long so the GPU's clock and "
+                         "power management have settled (reported in config.settle_s)")
     ap.add_argument("--workload", default="mlp7b_up_fwd")
     ap.add_argument("--recipe", default="delayed", choices=["delayed", "current"],
                     help="delayed scaling (the pages' default recipe) or just-in-time scaling")
@@ -226,15 +230,28 @@ def cold_cast_gbps(plan, dinp, reps: int = 5):
     return plan.cast_bytes(dinp) / (ms * 1e-3) / 1e9, ms
 
 
-def graph_steps(plan, dinp, steps: int):
-    """The step captured once as a HIP graph and replayed `steps` times, synchronized on both sides.
-    Returns (wall seconds per replay, per-replay milliseconds from HIP events recorded between the
-    replays on the launch stream)."""
+def settle(run_ten, seconds: float) -> int:
+    """Repeats the step (ten at a time) untimed for `seconds`; returns the number of steps run. A few
+    milliseconds into a burst of work the power controller lowers the clock below where it ends up
+    after a second or two (per-dispatch traces show it), so the timed steps follow this directly."""
     import torch
-    g = plan.capture(dinp)
+    n = 0
+    torch.cuda.synchronize()
+    s0 = time.perf_counter()
+    while True:   # at least ten, so a captured graph has been replayed before it is timed
+        run_ten()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - s0 >= seconds:
+            return n
+
+
+def graph_steps(g, steps: int):
+    """Replays the captured step `steps` times, synchronized on both sides. Returns (wall seconds per
+    replay, per-replay milliseconds from HIP events recorded between the replays on the launch
+    stream)."""
+    import torch
     stream = torch.cuda.current_stream()
-    for _ in range(3):
-        g.replay()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -466,6 +483,17 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # The timed steps: K replays of the step captured as a HIP graph (value, ms_per_step), right after
+    # the settle replays; with --no-graph, K eager steps after eager settle steps. The K eager steps
+    # with HIP events around every phase (roofline, components) follow directly.
+    if args.no_graph:
+        graph = None
+        settle_steps = settle(lambda: [plan.step(dinp) for _ in range(10)], args.settle_seconds)
+    else:
+        graph = plan.capture(dinp)
+        settle_steps = settle(lambda: [graph.replay() for _ in range(10)], args.settle_seconds)
+        graph_step_s, graph_ms = graph_steps(graph, K)
+    n_updates += settle_steps + (0 if args.no_graph else K)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -511,8 +539,7 @@ def main():
     if args.no_graph:
         graph_pct = None
     else:
-        step_s, graph_ms = graph_steps(plan, dinp, K)
-        n_updates += 3 + K
+        step_s = graph_step_s
         graph_pct = pct(graph_ms)
     # Clocks: the step repeated for about three seconds (outside the timed region) while the
     # sampler polls the device's metrics table.
@@ -575,6 +602,7 @@ def main():
                    "recipe": args.recipe, "output_cast": args.output_cast, "layernorm_x": bool(args.layernorm),
                    "gemm_accum": args.gemm_accum,
                    "step_launch": "eager" if args.no_graph else "hip_graph",
+                   "settle_s": args.settle_seconds, "settle_steps": settle_steps,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),

@@ -24,6 +24,7 @@ def _run(monkeypatch, capsys, *args):
 def test_bench_line_contract(monkeypatch, capsys):
     require_gpu()
     (line,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
+    assert line["config"]["settle_steps"] >= 10 and line["config"]["settle_s"] == 2.0
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
                 "vs_baseline", "dtype", "data", "config", "roofline", "components"):
         assert key in line, key
