@@ -1,0 +1,52 @@
+"""Every binary32 input through the cast, both formats: fp8_amax_cast at scale 1 on all 2**32 bit patterns
+(in chunks), compared code for code with the oracle's encoder. At scale 1 the product fp32(x) * s is x
+itself, so this covers every input the encoder can see; the binary32 multiply in front of it is checked
+by the scaled sweeps in test_gpu_cast.py. The amax of each chunk is checked too (NaN chunks give the
+canonical NaN)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import banner, f32, f32_bits, require_gpu
+
+import fp8_mixed_precision_cast_amd as fp8
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 1 << 27            # bit patterns per GPU launch
+PIECE = 1 << 22            # patterns per oracle task
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_every_binary32_input(fmt):
+    require_gpu()
+    workers = min(16, len(os.sched_getaffinity(0)))
+    x = torch.empty(CHUNK, dtype=torch.int32, device="cuda")
+    q = torch.empty(CHUNK, dtype=torch.uint8, device="cuda")
+    one = f32(1.0)
+    base = torch.arange(CHUNK, dtype=torch.int64, device="cuda")
+    mismatches = 0
+    with ThreadPoolExecutor(workers) as ex:
+        for c0 in range(0, 1 << 32, CHUNK):
+            banner("exhaustive", fmt, hex(c0))
+            x.copy_(((base + c0) & 0xFFFFFFFF).to(torch.int64).sub_(
+                torch.where(base + c0 >= (1 << 31), 1 << 32, 0)).to(torch.int32))
+            am = f32(0.0)
+            fp8.fp8_amax_cast(x.view(torch.float32), fmt, one, q, None, am)
+            got = q.cpu().numpy()
+            bits = np.arange(c0, c0 + CHUNK, dtype=np.uint64).astype(np.uint32)
+            vals = bits.view(np.float32)
+
+            def check(p0):
+                want = oracle.cast(vals[p0:p0 + PIECE], np.float32(1.0), fmt, "f32")
+                return int(np.count_nonzero(want != got[p0:p0 + PIECE]))
+            mismatches += sum(ex.map(check, range(0, CHUNK, PIECE)))
+            assert mismatches == 0, f"{fmt}: {mismatches} codes differ in chunk {hex(c0)}"
+            mags = bits & np.uint32(0x7FFFFFFF)
+            want_amax = 0x7FC00000 if (mags > 0x7F800000).any() else int(mags.max())
+            assert f32_bits(am)[0] == want_amax, (fmt, hex(c0))
