@@ -37,7 +37,7 @@ def test_every_binary32_input(fmt):
             x.copy_(((base + c0) & 0xFFFFFFFF).to(torch.int64).sub_(
                 torch.where(base + c0 >= (1 << 31), 1 << 32, 0)).to(torch.int32))
             am = f32(0.0)
-            fp8.fp8_amax_cast(x.view(torch.float32), fmt, one, q, None, am)
+            fp8.fp8_amax_cast(x.view(torch.float32).view(1, CHUNK), fmt, one, q.view(1, CHUNK), None, am)
             got = q.cpu().numpy()
             bits = np.arange(c0, c0 + CHUNK, dtype=np.uint64).astype(np.uint32)
             vals = bits.view(np.float32)
