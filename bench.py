@@ -448,8 +448,8 @@ def main():
         gemm_data(args.gemm_data)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); every box has one MI355X and this "
-              "path does not shard across GPUs.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this path measures one MI355X "
+              "and does not shard across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -28,11 +28,14 @@
 // whole rounds of 256 x 256 tiles and re-tiles the remaining columns (or rows)
 // into exactly one round of narrower tiles (256 x 192 or 256 x 128 as 4 x 2
 // waves, or 192 x 256 or 128 x 256 as 2 x 4 waves): at 4096 x 11008 every CU
-// then does 2.75 tiles' work instead of 3 rounds of whole tiles. Tiles of A and B are copied global -> LDS directly
-// (global_load_lds_dwordx4, no VGPR staging) into a double buffer, so the
-// next K step streams in while this one is multiplied. The 16-byte chunk c
-// of tile row r sits in LDS at chunk slot c ^ (r & 7): a wave's copy stays
-// coalesced and the fragment reads of eight consecutive rows hit eight
+// then does 2.75 tiles' work instead of 3 rounds of whole tiles. Tiles of A
+// and B are copied global -> LDS directly (buffer_load_dwordx4 ... lds, no
+// VGPR staging) into a double buffer, so the next K step streams in while
+// this one is multiplied; in the FP32-accumulation loop each step's barrier
+// sits at the top of its last chunk, so the first fragments of the next step
+// are read while that chunk's MFMAs run. The 16-byte chunk c of tile row r
+// sits in LDS at chunk slot c ^ (r & 7) ^ ((r >> 3) & 1): a wave's copy stays
+// coalesced and the fragment reads of sixteen consecutive rows hit sixteen
 // distinct bank groups. Tiles are numbered so that each XCD (workgroups are
 // dealt to the eight XCDs round-robin) owns a contiguous run of tile ids, and
 // runs are walked in groups of kGroupM tile rows so concurrently resident
@@ -186,11 +189,13 @@ __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int6
 }
 
 // Copies K step [k0, k0 + 128) of one operand into an LDS tile. Chunks of
-// missing rows or past K are read out of range, which stores zeros. A lane
-// none of whose rows exists (all of a wave's rows lie beyond a narrow tile's
-// height) issues nothing: those LDS rows are never read.
+// missing rows or past K are read out of range, which stores zeros. With
+// SKIP_EMPTY, a lane none of whose rows exists (all of a wave's rows lie
+// beyond a narrow tile's height) issues nothing: those LDS rows are never
+// read. Without it the copy has no branch (such lanes store zeros).
+template <bool SKIP_EMPTY = true>
 __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32_t K, uint8_t* lds, int wave) {
-  if (t.row_ok == 0) return;
+  if (SKIP_EMPTY && t.row_ok == 0) return;
   // all-ones where the chunk exists: a branch-free choice between its offset and out of range
   const uint32_t km0 = 0u - (uint32_t)(k0 + t.kc0 < K), km1 = 0u - (uint32_t)(k0 + t.kc1 < K);
 #pragma unroll
@@ -203,87 +208,18 @@ __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32
 }
 
 // Accumulators of one wave's 128 x 64 tile: 4 x 2 blocks of 32 x 32, each
-// held transposed (see mma_step), 128 floats per lane.
+// held transposed (see exact_chunk), 128 floats per lane.
 template <class G> struct Acc { v16f v[G::PM][G::PN]; };
-
-// One K step (32 x 32 x 16 BF16 MFMAs). Lane group G = lane / 32 owns
-// chunks 4G .. 4G+3 (k bytes 64G .. 64G+63) of its row; sub-step s (0..7)
-// feeds bytes 64G + 8s .. +7, widened to BF16, as the lane's 8 k values.
-// A and B walk k in the same order, so products pair up and the 128-byte step
-// is covered once. Each 16-byte chunk read serves two sub-steps.
-//
-// Block (i, j) is accumulated as B_j . A_i^T: lane l, register r then holds
-// C[32 i + l % 32][32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of the wave's tile.
-//
-// Software pipeline: the fragments of chunk c+1 are read from LDS while chunk
-// c is multiplied, and the operands of each sub-step are widened while the
-// MFMAs of the sub-step before it run. The copies of the next K step are
-// issued after the first two sub-steps' MFMAs (`issue_copies`): their LDS
-// writes then no longer compete with the first fragment reads of the step
-// (measured 2-5% faster than issuing them at the top).
-template <class GM, int FA, int FB, typename Issue>
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, Acc<GM>& acc, int wm, int wn, int lane,
-                                         Issue&& issue_copies) {
-  constexpr int kPM = GM::PM, kPN = GM::PN;
-  const int G = lane >> 5;
-  const int ra = wm * GM::WM + (lane & 31), rb = wn * GM::WN + (lane & 31);
-  uint4 aq[2][kPM], bq[2][kPN];
-  auto read_chunk = [&](int c, uint4 (&a)[kPM], uint4 (&b)[kPN]) {
-#pragma unroll
-    for (int j = 0; j < kPN; ++j) b[j] = *reinterpret_cast<const uint4*>(Bs + swz(rb + j * 32, 4 * G + c));
-#pragma unroll
-    for (int i = 0; i < kPM; ++i) a[i] = *reinterpret_cast<const uint4*>(As + swz(ra + i * 32, 4 * G + c));
-  };
-  read_chunk(0, aq[0], bq[0]);
-  v8bf aw[kPM], bw[kPN];
-#pragma unroll
-  for (int i = 0; i < kPM; ++i) aw[i] = widen8<FA>(aq[0][i].x, aq[0][i].y);
-#pragma unroll
-  for (int j = 0; j < kPN; ++j) bw[j] = widen8<FB>(bq[0][j].x, bq[0][j].y);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int cur = c & 1, nxt = cur ^ 1;
-    if (c + 1 < 4) read_chunk(c + 1, aq[nxt], bq[nxt]);
-    // keep the prefetch at the top of the chunk (the scheduler would otherwise sink it to its use)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const bool last = c == 3 && half == 1;
-      v8bf an[kPM], bn[kPN];
-      if (!last) {
-        const int sc = half == 0 ? cur : nxt;
-#pragma unroll
-        for (int i = 0; i < kPM; ++i)
-          an[i] = half == 0 ? widen8<FA>(aq[sc][i].z, aq[sc][i].w) : widen8<FA>(aq[sc][i].x, aq[sc][i].y);
-#pragma unroll
-        for (int j = 0; j < kPN; ++j)
-          bn[j] = half == 0 ? widen8<FB>(bq[sc][j].z, bq[sc][j].w) : widen8<FB>(bq[sc][j].x, bq[sc][j].y);
-      }
-#pragma unroll
-      for (int i = 0; i < kPM; ++i)
-#pragma unroll
-        for (int j = 0; j < kPN; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[j], aw[i], acc.v[i][j], 0, 0, 0);
-      if (c == 0 && half == 1) issue_copies();
-      if (!last) {
-#pragma unroll
-        for (int i = 0; i < kPM; ++i) aw[i] = an[i];
-#pragma unroll
-        for (int j = 0; j < kPN; ++j) bw[j] = bn[j];
-      }
-    }
-  }
-}
 
 // Operand format code of the f8f6f4 MFMAs: 0 = E4M3 (fp8), 1 = E5M2 (bf8).
 template <int FMT>
 constexpr int mfma_fmt() { return FMT == FP8MP_E4M3 ? 0 : 1; }
 
 // One K step on the FP8 MFMA (fast accumulation). Lane group G = lane / 32
-// owns chunks 4G .. 4G+3 of its row as in mma_step; sub-step h (0, 1) hands
+// owns chunks 4G .. 4G+3 of its row as in read_frags; sub-step h (0, 1) hands
 // chunks 4G+2h and 4G+2h+1 (32 codes) to one 32 x 32 x 64 MFMA. A and B
 // fragments are laid out alike, so products pair up; blocks are accumulated
-// transposed (B first), giving the same accumulator layout as mma_step.
+// transposed (B first), giving the same accumulator layout as exact_chunk.
 // Both sub-steps' fragments are read up front; the next K step's copies are
 // issued after the first sub-step's MFMAs.
 template <class GM, int FA, int FB, typename Issue>
@@ -320,24 +256,174 @@ __device__ __forceinline__ void mma_step_fast(const uint8_t* As, const uint8_t* 
   }
 }
 
-// Multiplies the step in `cur` and, from inside it, issues the copy of the
-// next K step into `nxt`. The two stages never overlap; saying so (restrict)
-// lets the compiler keep the copy in flight while the fragments of `cur` are
-// read.
-template <class GM, int FA, int FB, int ACC>
-__device__ __forceinline__ void pipelined_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bool more,
-                                               const TileCopy& ca, const TileCopy& cb, uint32_t k_next, uint32_t K,
-                                               Acc<GM>& acc, int wm, int wn, int wave, int lane) {
+// Multiplies the step in `cur` on the FP8 MFMA and, from inside it, issues
+// the copy of the next K step into `nxt`. The two stages never overlap;
+// saying so (restrict) lets the compiler keep the copy in flight while the
+// fragments of `cur` are read.
+template <class GM, int FA, int FB>
+__device__ __forceinline__ void pipelined_step_fast(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
+                                                    bool more, const TileCopy& ca, const TileCopy& cb,
+                                                    uint32_t k_next, uint32_t K, Acc<GM>& acc, int wm, int wn,
+                                                    int wave, int lane) {
   auto issue = [&]() {
     if (more) {
       load_tile(ca, k_next, K, nxt, wave);
       load_tile(cb, k_next, K, nxt + kTileBytes, wave);
     }
   };
-  if constexpr (ACC == kAccFast)
-    mma_step_fast<GM, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
-  else
-    mma_step<GM, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
+  mma_step_fast<GM, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
+}
+
+// Register state of the FP32-accumulation K loop: the raw fragments of two
+// chunks (slot = chunk & 1) and the widened operands of the next sub-step.
+template <class GM> struct ExactRegs {
+  uint4 aq[2][GM::PM], bq[2][GM::PN];
+  v8bf aw[GM::PM], bw[GM::PN];
+};
+
+// Reads chunk c (0..3) of this lane's fragments from the stage at st. The K
+// step (128 codes of each row) is cut into 8 chunks of 16 codes; lane group
+// G = lane / 32 owns chunks 4G .. 4G+3 of its row (rows ra + 32 i of A and
+// rb + 32 j of B), so one 16-byte read per fragment per chunk. A and B walk
+// k in the same order, so products pair up and the step is covered once.
+template <class GM>
+__device__ __forceinline__ void read_frags(const uint8_t* st, int ra, int rb, int G, int c, uint4 (&a)[GM::PM],
+                                           uint4 (&b)[GM::PN]) {
+#pragma unroll
+  for (int j = 0; j < GM::PN; ++j) b[j] = *reinterpret_cast<const uint4*>(st + kTileBytes + swz(rb + j * 32, 4 * G + c));
+#pragma unroll
+  for (int i = 0; i < GM::PM; ++i) a[i] = *reinterpret_cast<const uint4*>(st + swz(ra + i * 32, 4 * G + c));
+}
+
+// One chunk's two sub-steps of 32 x 32 x 16 BF16 MFMAs: sub-step h feeds
+// bytes 8h .. 8h+7 of each fragment, widened exactly to BF16, as the lane's
+// 8 k values. Half 0 widens the second half of chunk c (slot c & 1) and
+// half 1 the first half of chunk c + 1 (the other slot), each while the
+// MFMAs of the operands widened before run. mid() runs between the two
+// halves; with kLast the chunk after c does not exist and is not widened.
+//
+// Block (i, j) is accumulated as B_j . A_i^T: lane l, register r then holds
+// C[32 i + l % 32][32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of the wave's tile.
+template <class GM, int FA, int FB, bool kLast, typename Mid>
+__device__ __forceinline__ void exact_chunk(ExactRegs<GM>& r, Acc<GM>& acc, int c, Mid&& mid) {
+  constexpr int kPM = GM::PM, kPN = GM::PN;
+  const int sc = c & 1, sn = sc ^ 1;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const bool widen = half == 0 || !kLast;
+    v8bf an[kPM], bn[kPN];
+    if (widen) {
+#pragma unroll
+      for (int i = 0; i < kPM; ++i)
+        an[i] = half == 0 ? widen8<FA>(r.aq[sc][i].z, r.aq[sc][i].w) : widen8<FA>(r.aq[sn][i].x, r.aq[sn][i].y);
+#pragma unroll
+      for (int j = 0; j < kPN; ++j)
+        bn[j] = half == 0 ? widen8<FB>(r.bq[sc][j].z, r.bq[sc][j].w) : widen8<FB>(r.bq[sn][j].x, r.bq[sn][j].y);
+    }
+#pragma unroll
+    for (int i = 0; i < kPM; ++i)
+#pragma unroll
+      for (int j = 0; j < kPN; ++j)
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.bw[j], r.aw[i], acc.v[i][j], 0, 0, 0);
+    if (half == 0) {
+      // the halves stay apart: otherwise the scheduler hoists the widening of the
+      // next chunk, whose fragments are still being read, above these MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (widen) {
+#pragma unroll
+      for (int i = 0; i < kPM; ++i) r.aw[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < kPN; ++j) r.bw[j] = bn[j];
+    }
+  }
+}
+
+// Chunks 0..2 of a K step from stage rd, each reading the fragments of the
+// chunk after it first.
+template <class GM, int FA, int FB>
+__device__ __forceinline__ void exact_chunks012(const uint8_t* rd, ExactRegs<GM>& r, Acc<GM>& acc, int ra, int rb,
+                                                int G) {
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    read_frags<GM>(rd, ra, rb, G, c + 1, r.aq[(c + 1) & 1], r.bq[(c + 1) & 1]);
+    // keep the reads at the top of the chunk (the scheduler would otherwise sink them to their use)
+    __builtin_amdgcn_sched_barrier(0);
+    exact_chunk<GM, FA, FB, false>(r, acc, c, [] {});
+  }
+}
+
+// The steady-state body for step k >= 1: the last chunk of step k - 1, whose
+// stage `wr` then receives the copy of step k + 1, and the first three
+// chunks of step k from stage `rd`. Its barrier (at the top) publishes step
+// k, which each thread has waited for, and retires every read of `wr`: the
+// last chunk's fragments were read during the chunk before. The first chunk
+// of step k is read before the MFMAs of that last chunk are issued, so no
+// wave waits on LDS after the barrier with no MFMA work queued.
+//
+// rd and wr never overlap; saying so (restrict) lets the compiler keep the
+// copy into wr in flight while rd is read, here and in the next body (whose
+// reads are of this body's wr, after its own wait and barrier).
+template <class GM, int FA, int FB>
+__device__ __forceinline__ void exact_body(const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int k,
+                                           const TileCopy& ca, const TileCopy& cb, uint32_t K, ExactRegs<GM>& r,
+                                           Acc<GM>& acc, int ra, int rb, int G, int wave) {
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  read_frags<GM>(rd, ra, rb, G, 0, r.aq[0], r.bq[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  exact_chunk<GM, FA, FB, false>(r, acc, 3, [&] {
+    // copy of step k + 1; for k + 1 = nk every chunk lies past K and only zeros are stored
+    load_tile<false>(ca, (uint32_t)(k + 1) * kBK, K, wr, wave);
+    load_tile<false>(cb, (uint32_t)(k + 1) * kBK, K, wr + kTileBytes, wave);
+  });
+  exact_chunks012<GM, FA, FB>(rd, r, acc, ra, rb, G);
+}
+
+// Whole K loop of the FP32-accumulation GEMM (BF16 MFMA on widened codes),
+// software-pipelined across K steps: even steps in stage s0, odd ones in s1.
+// Within a step, the fragments of chunk c + 1 are read while chunk c is
+// multiplied, and each sub-step's operands are widened while the MFMAs of
+// the sub-step before run; each step's barrier sits at the top of its last
+// chunk (exact_body), and the copy of step k + 1 is issued during the last
+// chunk of step k - 1, so it has a whole step to land. The waits for the
+// copies are written out (buffer-to-LDS loads count in vmcnt).
+template <class GM, int FA, int FB>
+__device__ __forceinline__ void exact_k_loop(uint8_t* s0, uint8_t* s1, int nk, const TileCopy& ca,
+                                             const TileCopy& cb, uint32_t K, Acc<GM>& acc, int wm, int wn, int wave,
+                                             int lane) {
+  constexpr int kPM = GM::PM, kPN = GM::PN;
+  const int G = lane >> 5;
+  const int ra = wm * GM::WM + (lane & 31), rb = wn * GM::WN + (lane & 31);
+  if (nk <= 0) return;
+  ExactRegs<GM> r;
+  load_tile<false>(ca, 0, K, s0, wave);
+  load_tile<false>(cb, 0, K, s0 + kTileBytes, wave);
+  if (nk > 1) {
+    load_tile<false>(ca, kBK, K, s1, wave);
+    load_tile<false>(cb, kBK, K, s1 + kTileBytes, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  read_frags<GM>(s0, ra, rb, G, 0, r.aq[0], r.bq[0]);
+#pragma unroll
+  for (int i = 0; i < kPM; ++i) r.aw[i] = widen8<FA>(r.aq[0][i].x, r.aq[0][i].y);
+#pragma unroll
+  for (int j = 0; j < kPN; ++j) r.bw[j] = widen8<FB>(r.bq[0][j].x, r.bq[0][j].y);
+  exact_chunks012<GM, FA, FB>(s0, r, acc, ra, rb, G);
+  uint8_t* rd = s1;
+  uint8_t* wr = s0;
+  for (int k = 1; k < nk; ++k) {
+    exact_body<GM, FA, FB>(rd, wr, k, ca, cb, K, r, acc, ra, rb, G, wave);
+    uint8_t* t = rd;
+    rd = wr;
+    wr = t;
+  }
+  exact_chunk<GM, FA, FB, true>(r, acc, 3, [] {});
+  // the copy issued by the last body (of a step past K) may still be landing
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 }
 
 // No FP8 copy of the output (YF of the plain GEMM).
@@ -379,23 +465,27 @@ __device__ __forceinline__ void tile_body(
 
   const TileCopy ca = make_copy(A, lda, m0, M, K, GM::BM, wave, lane);
   const TileCopy cb = make_copy(B, ldb, n0, N, K, GM::BN, wave, lane);
-  if (nk > 0) {
-    load_tile(ca, 0, Ku, smem, wave);
-    load_tile(cb, 0, Ku, smem + kTileBytes, wave);
-  }
-  // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
-  // step kt + 1. At the top of a step each thread waits for its own copies
-  // into the stage to be read (buffer-to-LDS loads count in vmcnt; the wait
-  // is written out because the compiler does not insert it in every
-  // instantiation of such a loop), and the barrier then both publishes the
-  // stage and retires every read of the stage about to be overwritten.
-  for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
-    uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    pipelined_step<GM, FA, FB, ACC>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn, wave,
-                                    lane);
+  if constexpr (ACC == kAccExact) {
+    exact_k_loop<GM, FA, FB>(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
+  } else {
+    if (nk > 0) {
+      load_tile(ca, 0, Ku, smem, wave);
+      load_tile(cb, 0, Ku, smem + kTileBytes, wave);
+    }
+    // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
+    // step kt + 1. At the top of a step each thread waits for its own copies
+    // into the stage to be read (buffer-to-LDS loads count in vmcnt; the wait
+    // is written out because the compiler does not insert it in every
+    // instantiation of such a loop), and the barrier then both publishes the
+    // stage and retires every read of the stage about to be overwritten.
+    for (int kt = 0; kt < nk; ++kt) {
+      uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
+      uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      pipelined_step_fast<GM, FA, FB>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn,
+                                      wave, lane);
+    }
   }
 
   // Epilogue. Every wave must be done reading the last stage before the
@@ -614,7 +704,7 @@ hipError_t launch_plan(const GemmArgs& g, const TilePlan& p, hipStream_t stream)
   return hipGetLastError();
 }
 
-// The plain FP32-accumulation GEMM takes the tile plan. Measured on one box
+// The plain FP32-accumulation GEMM takes the tile plan. Measured on one MI355X
 // (4096 x 11008 x 4096, 7B backward, 13B projections): 1-3% faster with the
 // exact GEMM; the fast-accumulation GEMM was up to 6% slower (the chip runs at
 // its power limit there, and a full last round lowers the clock), so it and
