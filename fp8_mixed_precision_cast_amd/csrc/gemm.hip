@@ -370,7 +370,9 @@ template <class GM, int FA, int FB>
 __device__ __forceinline__ void exact_body(const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int k,
                                            const TileCopy& ca, const TileCopy& cb, uint32_t K, ExactRegs<GM>& r,
                                            Acc<GM>& acc, int ra, int rb, int G, int wave) {
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // Step 1 was copied with step 0 and waited for before the loop started;
+  // later steps' copies were issued by the body before.
+  if (k > 1) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   read_frags<GM>(rd, ra, rb, G, 0, r.aq[0], r.bq[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -382,31 +384,38 @@ __device__ __forceinline__ void exact_body(const uint8_t* __restrict__ rd, uint8
   exact_chunks012<GM, FA, FB>(rd, r, acc, ra, rb, G);
 }
 
-// Whole K loop of the FP32-accumulation GEMM (BF16 MFMA on widened codes),
-// software-pipelined across K steps: even steps in stage s0, odd ones in s1.
-// Within a step, the fragments of chunk c + 1 are read while chunk c is
-// multiplied, and each sub-step's operands are widened while the MFMAs of
-// the sub-step before run; each step's barrier sits at the top of its last
-// chunk (exact_body), and the copy of step k + 1 is issued during the last
-// chunk of step k - 1, so it has a whole step to land. The waits for the
-// copies are written out (buffer-to-LDS loads count in vmcnt).
-template <class GM, int FA, int FB>
-__device__ __forceinline__ void exact_k_loop(uint8_t* s0, uint8_t* s1, int nk, const TileCopy& ca,
-                                             const TileCopy& cb, uint32_t K, Acc<GM>& acc, int wm, int wn, int wave,
-                                             int lane) {
-  constexpr int kPM = GM::PM, kPN = GM::PN;
-  const int G = lane >> 5;
-  const int ra = wm * GM::WM + (lane & 31), rb = wn * GM::WN + (lane & 31);
-  if (nk <= 0) return;
-  ExactRegs<GM> r;
+// Copies K steps 0 and 1 of a tile into stages s0 and s1 (only step 0 when
+// nk = 1). The caller waits for them (vmcnt) and passes a barrier before the
+// K loop reads them.
+__device__ __forceinline__ void exact_first_copies(uint8_t* s0, uint8_t* s1, int nk, const TileCopy& ca,
+                                                   const TileCopy& cb, uint32_t K, int wave) {
   load_tile<false>(ca, 0, K, s0, wave);
   load_tile<false>(cb, 0, K, s0 + kTileBytes, wave);
   if (nk > 1) {
     load_tile<false>(ca, kBK, K, s1, wave);
     load_tile<false>(cb, kBK, K, s1 + kTileBytes, wave);
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
+}
+
+// Whole K loop of the FP32-accumulation GEMM (BF16 MFMA on widened codes),
+// software-pipelined across K steps: even steps in stage s0, odd ones in s1.
+// Steps 0 and 1 are already in the stages (exact_first_copies, waited for,
+// then a barrier). Within a step, the fragments of chunk c + 1 are read
+// while chunk c is multiplied, and each sub-step's operands are widened
+// while the MFMAs of the sub-step before run; each step's barrier sits at
+// the top of its last chunk (exact_body), and the copy of step k + 1 is
+// issued during the last chunk of step k - 1, so it has a whole step to
+// land. The waits for the copies are written out (buffer-to-LDS loads count
+// in vmcnt). On return every copy has landed.
+template <class GM, int FA, int FB>
+__device__ __forceinline__ void exact_k_steps(uint8_t* s0, uint8_t* s1, int nk, const TileCopy& ca,
+                                              const TileCopy& cb, uint32_t K, Acc<GM>& acc, int wm, int wn, int wave,
+                                              int lane) {
+  constexpr int kPM = GM::PM, kPN = GM::PN;
+  const int G = lane >> 5;
+  const int ra = wm * GM::WM + (lane & 31), rb = wn * GM::WN + (lane & 31);
+  if (nk <= 0) return;
+  ExactRegs<GM> r;
   read_frags<GM>(s0, ra, rb, G, 0, r.aq[0], r.bq[0]);
 #pragma unroll
   for (int i = 0; i < kPM; ++i) r.aw[i] = widen8<FA>(r.aq[0][i].x, r.aq[0][i].y);
@@ -426,6 +435,26 @@ __device__ __forceinline__ void exact_k_loop(uint8_t* s0, uint8_t* s1, int nk, c
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 }
 
+// The output is (acc * s1) * s2. Normally s1 = sa_inv * sb_inv and s2 = 1
+// (one rounding of the scale, and multiplying by 1 is exact). When that
+// product overflows or underflows binary32 while acc * sa_inv * sb_inv may
+// still be representable, the two factors are applied one at a time: the
+// smaller first when the product is too large (both exceed 1), the larger
+// first when it is too small.
+__device__ __forceinline__ void epilogue_scales(float sa_v, float sb_v, float& s1, float& s2) {
+  const float s_ab = sa_v * sb_v;
+  s1 = s_ab;
+  s2 = 1.0f;
+  if (!(__builtin_fabsf(s_ab) >= 1.17549435e-38f && __builtin_fabsf(s_ab) <= 3.40282347e38f) && s_ab == s_ab &&
+      sa_v != 0.0f && sb_v != 0.0f) {
+    const bool a_big = __builtin_fabsf(sa_v) >= __builtin_fabsf(sb_v);
+    const float big = a_big ? sa_v : sb_v, small = a_big ? sb_v : sa_v;
+    const bool too_large = __builtin_fabsf(s_ab) > 1.0f;
+    s1 = too_large ? small : big;
+    s2 = too_large ? big : small;
+  }
+}
+
 // No FP8 copy of the output (YF of the plain GEMM).
 constexpr int kNoY = -1;
 
@@ -441,21 +470,8 @@ __device__ __forceinline__ void tile_body(
   const int wm = wave / GM::WavesN, wn = wave % GM::WavesN;
   const int nk = (int)((K + kBK - 1) / kBK);
   const uint32_t Ku = (uint32_t)K;
-  // The output is (acc * s1) * s2. Normally s1 = sa_inv * sb_inv and s2 = 1 (one rounding of the
-  // scale, and multiplying by 1 is exact). When that product overflows or underflows binary32 while
-  // acc * sa_inv * sb_inv may still be representable, the two factors are applied one at a time:
-  // the smaller first when the product is too large (both exceed 1), the larger first when it is
-  // too small.
-  const float sa_v = *sa, sb_v = *sb, s_ab = sa_v * sb_v;
-  float s1 = s_ab, s2 = 1.0f;
-  if (!(__builtin_fabsf(s_ab) >= 1.17549435e-38f && __builtin_fabsf(s_ab) <= 3.40282347e38f) && s_ab == s_ab &&
-      sa_v != 0.0f && sb_v != 0.0f) {
-    const bool a_big = __builtin_fabsf(sa_v) >= __builtin_fabsf(sb_v);
-    const float big = a_big ? sa_v : sb_v, small = a_big ? sb_v : sa_v;
-    const bool too_large = __builtin_fabsf(s_ab) > 1.0f;
-    s1 = too_large ? small : big;
-    s2 = too_large ? big : small;
-  }
+  float s1, s2;
+  epilogue_scales(*sa, *sb, s1, s2);
   const bool do_c = YF == kNoY || C != nullptr;   // the fused call may skip the BF16 output
 
   Acc<GM> acc;
@@ -466,7 +482,12 @@ __device__ __forceinline__ void tile_body(
   const TileCopy ca = make_copy(A, lda, m0, M, K, GM::BM, wave, lane);
   const TileCopy cb = make_copy(B, ldb, n0, N, K, GM::BN, wave, lane);
   if constexpr (ACC == kAccExact) {
-    exact_k_loop<GM, FA, FB>(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
+    if (nk > 0) {
+      exact_first_copies(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, wave);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
+    exact_k_steps<GM, FA, FB>(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
   } else {
     if (nk > 0) {
       load_tile(ca, 0, Ku, smem, wave);
@@ -644,6 +665,222 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   }
 }
 
+// Persistent form of the plain FP32-accumulation GEMM. A launch of whole
+// workgroups lets every tile of a round finish at once, and then every CU
+// waits while the whole round's output (32 MB at 4096 x 4096) drains to HBM
+// and while its next tile's first K steps arrive. Here each workgroup walks
+// its tiles (ids blockIdx.x, blockIdx.x + gridDim.x, ...; gridDim.x is a
+// multiple of 8, so a workgroup stays on its XCD's run of tile ids) and
+// overlaps the two: at the end of a tile it issues the copies of the next
+// tile's steps 0 and 1 into the free stages, turns its BF16 output into
+// row-contiguous chunks in registers through a separate 32 KB of LDS,
+// waits for the copies, and only then issues the output stores, which drain
+// while the next tile runs (its first wait for a copy comes at its step 2).
+constexpr int kBandBytes = 8 * 4096;   // eight waves' 4 KB output slices
+
+// Tile id -> origin and kind (narrow or whole) under the tile plan.
+template <int NARROW>
+__device__ __forceinline__ bool plan_tile(int bid, const TilePlan& plan, int64_t& m0, int64_t& n0) {
+  using G2 = typename NarrowGeom<NARROW>::G;
+  const int n_full = plan.tm * plan.tn;
+  int bm, bn;
+  if (NARROW == kNarrowNone || bid < n_full) {
+    tile_coords(bid, plan.tm, plan.tn, bm, bn);
+    m0 = (int64_t)bm * kBM;
+    n0 = (int64_t)bn * kBN;
+    return false;
+  }
+  tile_coords(bid - n_full, plan.tm2, plan.tn2, bm, bn);
+  m0 = plan.m2_off + (int64_t)bm * G2::BM;
+  n0 = plan.n2_off + (int64_t)bn * G2::BN;
+  return true;
+}
+
+// Column groups of a wave's tile in the persistent epilogue: up to two
+// 32-column MFMA blocks (64 columns, 128 bytes of BF16) each.
+template <class GM> struct OutGroups {
+  static constexpr int G = (GM::PN + 1) / 2;
+  static __device__ __forceinline__ constexpr int blocks(int g) { return GM::PN - 2 * g < 2 ? GM::PN - 2 * g : 2; }
+};
+
+// End of a persistent tile: each wave turns its own accumulators into
+// row-contiguous BF16 chunks in registers, 32 rows x one column group at a
+// time, through a private 4 KB slice of the band: lane l writes the four
+// consecutive columns it holds of row l % 32, then reads back 16-byte
+// chunks, chunk t of the pass being row t / cpr, chunk t % cpr (cpr = 8 or
+// 4 chunks a row). Within a wave LDS accesses are ordered, so no workgroup
+// barrier is needed, and nothing waits for the copies in flight. Chunk slot
+// of (row, c) is c ^ ((row >> 1) & 7) for 8-chunk rows and c ^ ((row >> 2) &
+// 3) for 4-chunk rows, which spreads the 8-byte writes of 32 rows over the
+// banks. Then, with has_next, the next tile's steps 0 and 1 are copied into
+// the stages.
+template <class GM>
+__device__ __forceinline__ void next_copies_and_wave_out(
+    uint8_t* __restrict__ stages, uint8_t* __restrict__ band, bool has_next, const uint8_t* A, int64_t lda,
+    const uint8_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K, int64_t nm0, int64_t nn0, int cap_m, int cap_n,
+    const Acc<GM>& acc, float s1, float s2, int elane, int ewave, uint4 (&out)[GM::PM][OutGroups<GM>::G][4]) {
+  constexpr int kPM = GM::PM, kG = OutGroups<GM>::G;
+  static_assert(8 * 32 * 64 * 2 <= kBandBytes, "eight 4 KB wave slices");
+  const int nk = (int)((K + kBK - 1) / kBK);
+  uint8_t* wbuf = band + ewave * 4096;
+  const int half = elane >> 5, wrow = elane & 31;
+#pragma unroll
+  for (int i = 0; i < kPM; ++i)
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const int nb = OutGroups<GM>::blocks(g), cpr = 4 * nb;
+      const int wsw = cpr == 8 ? (wrow >> 1) & 7 : (wrow >> 2) & 3;
+#pragma unroll
+      for (int jj = 0; jj < nb; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v16f& a = acc.v[i][2 * g + jj];
+          const uint2 v = {pack_bf16((a[4 * q] * s1) * s2, (a[4 * q + 1] * s1) * s2),
+                           pack_bf16((a[4 * q + 2] * s1) * s2, (a[4 * q + 3] * s1) * s2)};
+          *reinterpret_cast<uint2*>(wbuf + wrow * cpr * 16 + (((4 * jj + q) ^ wsw) << 4) + half * 8) = v;
+        }
+#pragma unroll
+      for (int p = 0; p < cpr / 2; ++p) {
+        const int t = p * 64 + elane, row = t / cpr, c = t % cpr;
+        const int rsw = cpr == 8 ? (row >> 1) & 7 : (row >> 2) & 3;
+        out[i][g][p] = *reinterpret_cast<const uint4*>(wbuf + row * cpr * 16 + ((c ^ rsw) << 4));
+      }
+    }
+  // The copies go out after the band reads: the compiler cannot always tell
+  // those reads from the copies' LDS writes and would otherwise wait for the
+  // copies before them.
+  if (has_next) {
+    const TileCopy na = make_copy(A, lda, nm0, M, K, cap_m, ewave, elane);
+    const TileCopy nb = make_copy(B, ldb, nn0, N, K, cap_n, ewave, elane);
+    exact_first_copies(stages, stages + 2 * kTileBytes, nk, na, nb, (uint32_t)K, ewave);
+  }
+}
+
+// One tile of geometry GM at (m0, n0) whose steps 0 and 1 are in the stages
+// and published. With has_next, the next tile's steps 0 and 1 (origin nm0,
+// nn0, heights cap_m x cap_n) are copied in before this tile's output is
+// stored; on return they are published.
+template <class GM, int FA, int FB>
+__device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                                int64_t M, int64_t N, int64_t K, float s1, float s2, uint16_t* C,
+                                                int64_t ldc, uint8_t* smem, uint8_t* band, int64_t m0, int64_t n0,
+                                                bool has_next, int64_t nm0, int64_t nn0, int cap_m, int cap_n) {
+  constexpr int kPM = GM::PM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / GM::WavesN, wn = wave % GM::WavesN;
+  const int nk = (int)((K + kBK - 1) / kBK);
+  const uint32_t Ku = (uint32_t)K;
+  Acc<GM> acc;
+  float* accf = reinterpret_cast<float*>(&acc);
+#pragma unroll
+  for (int e = 0; e < (int)(sizeof(acc) / sizeof(float)); ++e) accf[e] = 0.f;
+  {
+    const TileCopy ca = make_copy(A, lda, m0, M, K, GM::BM, wave, lane);
+    const TileCopy cb = make_copy(B, ldb, n0, N, K, GM::BN, wave, lane);
+    exact_k_steps<GM, FA, FB>(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
+  }
+  // every wave is done reading the stages: the next tile's first steps may land there
+  __syncthreads();
+  // The epilogue's thread indices are taken afresh here (opaque to the
+  // compiler), so that their address arithmetic is not hoisted out of the
+  // tile loop and kept live through the K loop.
+  int etid = (int)threadIdx.x;
+  asm volatile("" : "+v"(etid));
+  const int elane = etid & 63, ewave = __builtin_amdgcn_readfirstlane(etid) >> 6;
+  constexpr int kG = OutGroups<GM>::G;
+  uint4 out[kPM][kG][4];
+  next_copies_and_wave_out<GM>(smem, band, has_next, A, lda, B, ldb, M, N, K, nm0, nn0, cap_m, cap_n, acc, s1, s2,
+                               elane, ewave, out);
+  // The next tile's first copies (and any stores still in flight) have
+  // landed and are published; nothing else is outstanding while the stores
+  // below drain.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  // Chunk p of pass (i, g) of this lane: wave-tile row 32 i + (64 p + lane) / cpr,
+  // columns 64 g + 8 ((64 p + lane) % cpr) .. +7. C is 16-byte aligned with a
+  // 16-byte row pitch (checked by the C-ABI).
+  const int ewm = ewave / GM::WavesN, ewn = ewave % GM::WavesN;
+  const int64_t r0 = m0 + ewm * GM::WM, c0 = n0 + ewn * GM::WN;
+  if (m0 + GM::BM <= M && n0 + GM::BN <= N) {
+#pragma unroll
+    for (int i = 0; i < kPM; ++i)
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        const int cpr = 4 * OutGroups<GM>::blocks(g);
+#pragma unroll
+        for (int p = 0; p < cpr / 2; ++p) {
+          const int t = p * 64 + elane, row = 32 * i + t / cpr, col = 64 * g + 8 * (t % cpr);
+          *reinterpret_cast<uint4*>(C + (r0 + row) * ldc + c0 + col) = out[i][g][p];
+        }
+      }
+  } else {
+    // edge tile: row and column checks, element stores where a chunk straddles N
+#pragma unroll
+    for (int i = 0; i < kPM; ++i)
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        const int cpr = 4 * OutGroups<GM>::blocks(g);
+#pragma unroll
+        for (int p = 0; p < cpr / 2; ++p) {
+          const int t = p * 64 + elane;
+          const int64_t gm = r0 + 32 * i + t / cpr, gn = c0 + 64 * g + 8 * (t % cpr);
+          if (gm >= M || gn >= N) continue;
+          uint16_t* dst = C + gm * ldc + gn;
+          if (gn + 8 <= N) {
+            *reinterpret_cast<uint4*>(dst) = out[i][g][p];
+          } else {
+            const uint32_t w[4] = {out[i][g][p].x, out[i][g][p].y, out[i][g][p].z, out[i][g][p].w};
+            for (int e = 0; e < 8 && gn + e < N; ++e) dst[e] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          }
+        }
+      }
+  }
+}
+
+template <int FA, int FB, int NARROW>
+__global__ __launch_bounds__(kThreads) void gemm_exact_persistent_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M, int64_t N,
+    int64_t K, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ C, int64_t ldc,
+    TilePlan plan) {
+  // Two stages, each an A tile followed by a B tile, and the output band.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t band[kBandBytes];
+  using G2 = typename NarrowGeom<NARROW>::G;
+  const int total = plan.tm * plan.tn + plan.tm2 * plan.tn2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nk = (int)((K + kBK - 1) / kBK);
+  float s1, s2;
+  epilogue_scales(*sa, *sb, s1, s2);
+  int bid = blockIdx.x;
+  int64_t m0, n0;
+  bool narrow = plan_tile<NARROW>(bid, plan, m0, n0);
+  if (nk > 0) {
+    const TileCopy ca = make_copy(A, lda, m0, M, K, narrow ? G2::BM : kBM, wave, lane);
+    const TileCopy cb = make_copy(B, ldb, n0, N, K, narrow ? G2::BN : kBN, wave, lane);
+    exact_first_copies(smem, smem + 2 * kTileBytes, nk, ca, cb, (uint32_t)K, wave);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+  for (;;) {
+    const int next = bid + (int)gridDim.x;
+    const bool has_next = next < total;
+    int64_t nm0 = 0, nn0 = 0;
+    const bool next_narrow = has_next && plan_tile<NARROW>(next, plan, nm0, nn0);
+    const int cap_m = next_narrow ? G2::BM : kBM, cap_n = next_narrow ? G2::BN : kBN;
+    if (NARROW != kNarrowNone && narrow)
+      persistent_tile<G2, FA, FB>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, smem, band, m0, n0, has_next, nm0, nn0,
+                                  cap_m, cap_n);
+    else
+      persistent_tile<GFull, FA, FB>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, smem, band, m0, n0, has_next, nm0,
+                                     nn0, cap_m, cap_n);
+    if (!has_next) break;
+    bid = next;
+    m0 = nm0;
+    n0 = nn0;
+    narrow = next_narrow;
+  }
+}
+
 // Everything a launch needs besides the format templates.
 struct GemmArgs {
   const uint8_t* a; int64_t lda;
@@ -704,22 +941,37 @@ hipError_t launch_plan(const GemmArgs& g, const TilePlan& p, hipStream_t stream)
   return hipGetLastError();
 }
 
-// The plain FP32-accumulation GEMM takes the tile plan. Measured on one MI355X
-// (4096 x 11008 x 4096, 7B backward, 13B projections): 1-3% faster with the
-// exact GEMM; the fast-accumulation GEMM was up to 6% slower (the chip runs at
-// its power limit there, and a full last round lowers the clock), so it and
-// the fused output cast keep whole tiles.
+// The plain FP32-accumulation GEMM takes the tile plan and runs persistent.
+// Measured on one MI355X: the tile plan is 1-3% faster at 4096 x 11008 x 4096
+// (7B backward, 13B projections); the fast-accumulation GEMM was up to 6%
+// slower with it (the chip runs at its power limit there, and a full last
+// round lowers the clock), so it and the fused output cast keep whole tiles
+// in a launch of one workgroup per tile. The persistent walk gains 1.5-7.5%
+// where K is small next to the output (16384 x 16384 x 512 .. 8192 x 8192 x
+// 2048) and is even at K = 4096 and 8192, where the chip sits at its power
+// limit either way.
+template <int FA, int FB, int NARROW>
+hipError_t launch_persistent(const GemmArgs& g, const TilePlan& p, int num_cus, hipStream_t stream) {
+  const int total = p.tm * p.tn + p.tm2 * p.tn2;
+  // one workgroup per CU, a multiple of 8 so that each keeps to its XCD's tile ids
+  const int slots = num_cus >= 8 ? num_cus / 8 * 8 : total;
+  const unsigned grid = (unsigned)(total < slots ? total : slots);
+  hipLaunchKernelGGL((gemm_exact_persistent_kernel<FA, FB, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g.a,
+                     g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, p);
+  return hipGetLastError();
+}
+
 template <int FA, int FB, int YF, int ACC>
 hipError_t launch_one(const GemmArgs& g, int num_cus, hipStream_t stream) {
   TilePlan p;
   const int kind = plan_tiles(g.m, g.n, YF == kNoY && ACC == kAccExact ? num_cus : 0, p);
   if constexpr (YF == kNoY && ACC == kAccExact) {
     switch (kind) {
-      case kNarrowN192: return launch_plan<FA, FB, YF, ACC, kNarrowN192>(g, p, stream);
-      case kNarrowN128: return launch_plan<FA, FB, YF, ACC, kNarrowN128>(g, p, stream);
-      case kNarrowM192: return launch_plan<FA, FB, YF, ACC, kNarrowM192>(g, p, stream);
-      case kNarrowM128: return launch_plan<FA, FB, YF, ACC, kNarrowM128>(g, p, stream);
-      default: break;
+      case kNarrowN192: return launch_persistent<FA, FB, kNarrowN192>(g, p, num_cus, stream);
+      case kNarrowN128: return launch_persistent<FA, FB, kNarrowN128>(g, p, num_cus, stream);
+      case kNarrowM192: return launch_persistent<FA, FB, kNarrowM192>(g, p, num_cus, stream);
+      case kNarrowM128: return launch_persistent<FA, FB, kNarrowM128>(g, p, num_cus, stream);
+      default: return launch_persistent<FA, FB, kNarrowNone>(g, p, num_cus, stream);
     }
   }
   return launch_plan<FA, FB, YF, ACC, kNarrowNone>(g, p, stream);

@@ -284,3 +284,36 @@ def _exact_bits(a, b):
     u = ref.astype(np.float32).view(np.uint32)
     return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16).view(
         np.int16)
+
+
+# Launches with more tiles than CUs, so each workgroup of the FP32-accumulation GEMM walks several tiles
+# (copying the next tile's first K steps while it stores the current one): 1, 2 and 3 K steps per tile
+# (the first waits of the next tile fall inside, at or past its second step), ragged edges in M, N and K,
+# and one shape whose walk switches to 256 x 128 narrow tiles for its last round.
+PERSISTENT_SHAPES = [(4100, 4100, 16), (4100, 4100, 256), (4100, 4100, 368), (8192, 8448, 144)]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT_SHAPES)
+def test_gemm_workgroups_walking_several_tiles(shape):
+    require_gpu()
+    m, n, k = shape
+    rng = np.random.default_rng(m + 5 * n + 11 * k)
+    a = _codes(rng, (m, k), "e4m3", spread=40)
+    b = _codes(rng, (n, k), "e5m2", spread=40)
+    sa, sb = np.float32(0.75), np.float32(1 / 5.0)
+    banner("gemm persistent walk", shape)
+    c, store = pitched(m, n, torch.int16, fill=0x7FC1, pad_bytes=16)
+    fp8.fp8_scaled_gemm(dev(a), "e4m3", dev(b), "e5m2", f32(sa), f32(sb), c)
+    out = host(store)
+    assert (out[:, n:] == 0x7FC1).all(), "wrote past n"
+    _check(a, "e4m3", b, "e5m2", sa, sb, out[:, :n], f"walk {shape}")
+    # exact sums: one magnitude per row of A and of B, so the output is the correctly rounded product
+    e_a = rng.integers(4, 12, m)
+    e_b = rng.integers(4, 12, n)
+    a = ((e_a[:, None] << 3) | (rng.integers(0, 2, (m, k)) << 7)).astype(np.uint8)
+    b = ((e_b[:, None] << 3) | (rng.integers(0, 2, (n, k)) << 7)).astype(np.uint8)
+    c1, store1 = pitched(m, n, torch.int16, fill=0x7FC1)
+    fp8.fp8_scaled_gemm(dev(a), "e4m3", dev(b), "e4m3", f32(1.0), f32(1.0), c1)
+    want = _exact_bits(a, b).view(np.uint16)
+    got = host(store1)[:, :n].view(np.uint16)
+    assert np.array_equal(got, want), first_diff(got, want)
