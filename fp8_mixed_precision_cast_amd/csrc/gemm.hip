@@ -458,13 +458,15 @@ __device__ __forceinline__ void epilogue_scales(float sa_v, float sb_v, float& s
 // No FP8 copy of the output (YF of the plain GEMM).
 constexpr int kNoY = -1;
 
-// One output tile of geometry GM at (m0, n0).
+// One output tile of geometry GM at (m0, n0), on the FP8 MFMA (fast
+// accumulation; the FP32-accumulation GEMM runs in the persistent kernel).
 template <class GM, int FA, int FB, int YF, int ACC>
 __device__ __forceinline__ void tile_body(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, const float* __restrict__ sa, const float* __restrict__ sb,
     uint16_t* __restrict__ C, int64_t ldc, const float* __restrict__ y_scale,
     uint8_t* __restrict__ y_q, int64_t ld_yq, float* __restrict__ y_amax, uint8_t* smem, int64_t m0, int64_t n0) {
+  static_assert(ACC == kAccFast, "the one-tile-per-workgroup launch runs the fast-accumulation GEMM only");
   constexpr int kPM = GM::PM, kPN = GM::PN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / GM::WavesN, wn = wave % GM::WavesN;
@@ -481,32 +483,23 @@ __device__ __forceinline__ void tile_body(
 
   const TileCopy ca = make_copy(A, lda, m0, M, K, GM::BM, wave, lane);
   const TileCopy cb = make_copy(B, ldb, n0, N, K, GM::BN, wave, lane);
-  if constexpr (ACC == kAccExact) {
-    if (nk > 0) {
-      exact_first_copies(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, wave);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-    }
-    exact_k_steps<GM, FA, FB>(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
-  } else {
-    if (nk > 0) {
-      load_tile(ca, 0, Ku, smem, wave);
-      load_tile(cb, 0, Ku, smem + kTileBytes, wave);
-    }
-    // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
-    // step kt + 1. At the top of a step each thread waits for its own copies
-    // into the stage to be read (buffer-to-LDS loads count in vmcnt; the wait
-    // is written out because the compiler does not insert it in every
-    // instantiation of such a loop), and the barrier then both publishes the
-    // stage and retires every read of the stage about to be overwritten.
-    for (int kt = 0; kt < nk; ++kt) {
-      uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
-      uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      pipelined_step_fast<GM, FA, FB>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn,
-                                      wave, lane);
-    }
+  if (nk > 0) {
+    load_tile(ca, 0, Ku, smem, wave);
+    load_tile(cb, 0, Ku, smem + kTileBytes, wave);
+  }
+  // Step kt reads stage kt & 1 and, meanwhile, fills the other stage with
+  // step kt + 1. At the top of a step each thread waits for its own copies
+  // into the stage to be read (buffer-to-LDS loads count in vmcnt; the wait
+  // is written out because the compiler does not insert it in every
+  // instantiation of such a loop), and the barrier then both publishes the
+  // stage and retires every read of the stage about to be overwritten.
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
+    uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    pipelined_step_fast<GM, FA, FB>(cur, nxt, kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, Ku, acc, wm, wn, wave,
+                                    lane);
   }
 
   // Epilogue. Every wave must be done reading the last stage before the
@@ -759,12 +752,15 @@ __device__ __forceinline__ void next_copies_and_wave_out(
 // One tile of geometry GM at (m0, n0) whose steps 0 and 1 are in the stages
 // and published. With has_next, the next tile's steps 0 and 1 (origin nm0,
 // nn0, heights cap_m x cap_n) are copied in before this tile's output is
-// stored; on return they are published.
-template <class GM, int FA, int FB>
+// stored; on return they are published. YF = a format: the output is also
+// cast as fp8_amax_cast would cast C (codes to y_q under the scale ys when
+// y_q is given; the magnitude max folded into am, packed BF16 pairs).
+template <class GM, int FA, int FB, int YF>
 __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                                                 int64_t M, int64_t N, int64_t K, float s1, float s2, uint16_t* C,
-                                                int64_t ldc, uint8_t* smem, uint8_t* band, int64_t m0, int64_t n0,
-                                                bool has_next, int64_t nm0, int64_t nn0, int cap_m, int cap_n) {
+                                                int64_t ldc, uint8_t* y_q, int64_t ld_yq, float ys, uint32_t& am,
+                                                uint8_t* smem, uint8_t* band, int64_t m0, int64_t n0, bool has_next,
+                                                int64_t nm0, int64_t nn0, int cap_m, int cap_n) {
   constexpr int kPM = GM::PM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / GM::WavesN, wn = wave % GM::WavesN;
@@ -797,11 +793,30 @@ __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, c
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   // Chunk p of pass (i, g) of this lane: wave-tile row 32 i + (64 p + lane) / cpr,
-  // columns 64 g + 8 ((64 p + lane) % cpr) .. +7. C is 16-byte aligned with a
-  // 16-byte row pitch (checked by the C-ABI).
+  // columns 64 g + 8 ((64 p + lane) % cpr) .. +7. C and y_q are 16-byte
+  // aligned with 16-byte row pitches (checked by the C-ABI).
   const int ewm = ewave / GM::WavesN, ewn = ewave % GM::WavesN;
   const int64_t r0 = m0 + ewm * GM::WM, c0 = n0 + ewn * GM::WN;
+  const bool do_c = C != nullptr, do_q = YF != kNoY && y_q != nullptr;
   if (m0 + GM::BM <= M && n0 + GM::BN <= N) {
+    // interior tile: 16-byte C stores; with the cast, the magnitude max of
+    // this thread's values also tells whether any is NaN (the two encoders
+    // agree on every other value)
+    uint32_t mx = 0;
+    if constexpr (YF != kNoY) {
+#pragma unroll
+      for (int i = 0; i < kPM; ++i)
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+#pragma unroll
+          for (int p = 0; p < 2 * OutGroups<GM>::blocks(g); ++p) {
+            const uint4 v = out[i][g][p];
+            mx = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(mx, v.x), v.y), v.z), v.w);
+          }
+      am = amax_bf16x2(am, mx);
+    }
+    const uint32_t sb = __float_as_uint(ys) & 0x7FFFFFFFu;
+    const bool no_nan = (mx & 0xFFFFu) <= 0x7F80u && (mx >> 16) <= 0x7F80u && sb != 0u && sb < 0x7F800000u;
 #pragma unroll
     for (int i = 0; i < kPM; ++i)
 #pragma unroll
@@ -810,7 +825,15 @@ __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, c
 #pragma unroll
         for (int p = 0; p < cpr / 2; ++p) {
           const int t = p * 64 + elane, row = 32 * i + t / cpr, col = 64 * g + 8 * (t % cpr);
-          *reinterpret_cast<uint4*>(C + (r0 + row) * ldc + c0 + col) = out[i][g][p];
+          const uint4 v = out[i][g][p];
+          if (do_c) *reinterpret_cast<uint4*>(C + (r0 + row) * ldc + c0 + col) = v;
+          if constexpr (YF != kNoY) {
+            if (do_q) {
+              const uint2 qq = no_nan ? uint2{enc4_bf16_nonan<YF>(v.x, v.y, ys), enc4_bf16_nonan<YF>(v.z, v.w, ys)}
+                                      : uint2{enc4_bf16_sel<YF>(v.x, v.y, ys), enc4_bf16_sel<YF>(v.z, v.w, ys)};
+              *reinterpret_cast<uint2*>(y_q + (r0 + row) * ld_yq + c0 + col) = qq;
+            }
+          }
         }
       }
   } else {
@@ -825,23 +848,55 @@ __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, c
           const int t = p * 64 + elane;
           const int64_t gm = r0 + 32 * i + t / cpr, gn = c0 + 64 * g + 8 * (t % cpr);
           if (gm >= M || gn >= N) continue;
-          uint16_t* dst = C + gm * ldc + gn;
+          const uint4 v = out[i][g][p];
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
           if (gn + 8 <= N) {
-            *reinterpret_cast<uint4*>(dst) = out[i][g][p];
+            if (do_c) *reinterpret_cast<uint4*>(C + gm * ldc + gn) = v;
+            if constexpr (YF != kNoY) {
+              am = amax_bf16x2(amax_bf16x2(amax_bf16x2(amax_bf16x2(am, w[0]), w[1]), w[2]), w[3]);
+              if (do_q)
+                *reinterpret_cast<uint2*>(y_q + gm * ld_yq + gn) =
+                    uint2{enc4_bf16_sel<YF>(w[0], w[1], ys), enc4_bf16_sel<YF>(w[2], w[3], ys)};
+            }
           } else {
-            const uint32_t w[4] = {out[i][g][p].x, out[i][g][p].y, out[i][g][p].z, out[i][g][p].w};
-            for (int e = 0; e < 8 && gn + e < N; ++e) dst[e] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            for (int e = 0; e < 8 && gn + e < N; ++e) {
+              const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+              if (do_c) C[gm * ldc + gn + e] = (uint16_t)h;
+              if constexpr (YF != kNoY) {
+                am = amax_bf16x2(am, h);
+                if (do_q) y_q[gm * ld_yq + gn + e] = enc1<YF>(__uint_as_float(h << 16), ys);
+              }
+            }
           }
         }
       }
   }
 }
 
-template <int FA, int FB, int NARROW>
+// Wave-level amax commit: the same skip-or-atomic rule as block_amax_commit,
+// once per wave (the persistent kernel has no LDS left for a block reduction).
+__device__ __forceinline__ void wave_amax_commit(uint32_t m, float* amax) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(m, off, 64);
+    m = m > o ? m : o;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    const uint32_t r = canonical_nan(m);
+    unsigned int* a = reinterpret_cast<unsigned int*>(amax);
+    if (r != 0u && r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
+  }
+}
+
+// YF = kNoY: the plain GEMM. YF = a format: the epilogue also runs the cast
+// of the BF16 output C on the fly, exactly as fp8_amax_cast would on C:
+// *y_amax = max(*y_amax, max|C|) (if y_amax) and y_q = enc_YF(C * *y_scale)
+// (if y_q); C may then be null.
+template <int FA, int FB, int YF, int NARROW>
 __global__ __launch_bounds__(kThreads) void gemm_exact_persistent_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M, int64_t N,
     int64_t K, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ C, int64_t ldc,
-    TilePlan plan) {
+    TilePlan plan, const float* __restrict__ y_scale, uint8_t* __restrict__ y_q, int64_t ld_yq,
+    float* __restrict__ y_amax) {
   // Two stages, each an A tile followed by a B tile, and the output band.
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t band[kBandBytes];
@@ -851,6 +906,8 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_persistent_kernel(
   const int nk = (int)((K + kBK - 1) / kBK);
   float s1, s2;
   epilogue_scales(*sa, *sb, s1, s2);
+  const float ys = YF != kNoY && y_q != nullptr ? *y_scale : 0.f;
+  uint32_t am = 0;   // packed BF16 magnitudes of this thread's outputs, over all its tiles
   int bid = blockIdx.x;
   int64_t m0, n0;
   bool narrow = plan_tile<NARROW>(bid, plan, m0, n0);
@@ -868,16 +925,19 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_persistent_kernel(
     const bool next_narrow = has_next && plan_tile<NARROW>(next, plan, nm0, nn0);
     const int cap_m = next_narrow ? G2::BM : kBM, cap_n = next_narrow ? G2::BN : kBN;
     if (NARROW != kNarrowNone && narrow)
-      persistent_tile<G2, FA, FB>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, smem, band, m0, n0, has_next, nm0, nn0,
-                                  cap_m, cap_n);
+      persistent_tile<G2, FA, FB, YF>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, y_q, ld_yq, ys, am, smem, band, m0,
+                                      n0, has_next, nm0, nn0, cap_m, cap_n);
     else
-      persistent_tile<GFull, FA, FB>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, smem, band, m0, n0, has_next, nm0,
-                                     nn0, cap_m, cap_n);
+      persistent_tile<GFull, FA, FB, YF>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, y_q, ld_yq, ys, am, smem, band,
+                                         m0, n0, has_next, nm0, nn0, cap_m, cap_n);
     if (!has_next) break;
     bid = next;
     m0 = nm0;
     n0 = nn0;
     narrow = next_narrow;
+  }
+  if constexpr (YF != kNoY) {
+    if (y_amax != nullptr) wave_amax_commit(bf16x2_acc_to_f32_bits(am), y_amax);
   }
 }
 
@@ -941,40 +1001,44 @@ hipError_t launch_plan(const GemmArgs& g, const TilePlan& p, hipStream_t stream)
   return hipGetLastError();
 }
 
-// The plain FP32-accumulation GEMM takes the tile plan and runs persistent.
-// Measured on one MI355X: the tile plan is 1-3% faster at 4096 x 11008 x 4096
-// (7B backward, 13B projections); the fast-accumulation GEMM was up to 6%
-// slower with it (the chip runs at its power limit there, and a full last
-// round lowers the clock), so it and the fused output cast keep whole tiles
-// in a launch of one workgroup per tile. The persistent walk gains 1.5-7.5%
-// where K is small next to the output (16384 x 16384 x 512 .. 8192 x 8192 x
-// 2048) and is even at K = 4096 and 8192, where the chip sits at its power
-// limit either way.
-template <int FA, int FB, int NARROW>
+// The FP32-accumulation GEMM, plain or with the fused output cast, takes the
+// tile plan and runs persistent. Measured on one MI355X: the tile plan is
+// 1-3% faster at 4096 x 11008 x 4096 (7B backward, 13B projections); the
+// fast-accumulation GEMM was up to 6% slower with it (the chip runs at its
+// power limit there, and a full last round lowers the clock), so it keeps
+// whole tiles in a launch of one workgroup per tile. The persistent walk
+// gains 1.5-7.5% where K is small next to the output (16384 x 16384 x 512 ..
+// 8192 x 8192 x 2048) and is even at K = 4096 and 8192 for the plain GEMM,
+// where the chip sits at its power limit either way; with the fused output
+// cast, whose code stores now also drain under the next tile, the 7B GEMM
+// took 265 instead of 272 us.
+template <int FA, int FB, int YF, int NARROW>
 hipError_t launch_persistent(const GemmArgs& g, const TilePlan& p, int num_cus, hipStream_t stream) {
   const int total = p.tm * p.tn + p.tm2 * p.tn2;
   // one workgroup per CU, a multiple of 8 so that each keeps to its XCD's tile ids
   const int slots = num_cus >= 8 ? num_cus / 8 * 8 : total;
   const unsigned grid = (unsigned)(total < slots ? total : slots);
-  hipLaunchKernelGGL((gemm_exact_persistent_kernel<FA, FB, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g.a,
-                     g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, p);
+  hipLaunchKernelGGL((gemm_exact_persistent_kernel<FA, FB, YF, NARROW>), dim3(grid), dim3(kThreads), 0, stream,
+                     g.a, g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, p, g.y_scale, g.y_q, g.ld_yq,
+                     g.y_amax);
   return hipGetLastError();
 }
 
 template <int FA, int FB, int YF, int ACC>
 hipError_t launch_one(const GemmArgs& g, int num_cus, hipStream_t stream) {
   TilePlan p;
-  const int kind = plan_tiles(g.m, g.n, YF == kNoY && ACC == kAccExact ? num_cus : 0, p);
-  if constexpr (YF == kNoY && ACC == kAccExact) {
+  const int kind = plan_tiles(g.m, g.n, ACC == kAccExact ? num_cus : 0, p);
+  if constexpr (ACC == kAccExact) {
     switch (kind) {
-      case kNarrowN192: return launch_persistent<FA, FB, kNarrowN192>(g, p, num_cus, stream);
-      case kNarrowN128: return launch_persistent<FA, FB, kNarrowN128>(g, p, num_cus, stream);
-      case kNarrowM192: return launch_persistent<FA, FB, kNarrowM192>(g, p, num_cus, stream);
-      case kNarrowM128: return launch_persistent<FA, FB, kNarrowM128>(g, p, num_cus, stream);
-      default: return launch_persistent<FA, FB, kNarrowNone>(g, p, num_cus, stream);
+      case kNarrowN192: return launch_persistent<FA, FB, YF, kNarrowN192>(g, p, num_cus, stream);
+      case kNarrowN128: return launch_persistent<FA, FB, YF, kNarrowN128>(g, p, num_cus, stream);
+      case kNarrowM192: return launch_persistent<FA, FB, YF, kNarrowM192>(g, p, num_cus, stream);
+      case kNarrowM128: return launch_persistent<FA, FB, YF, kNarrowM128>(g, p, num_cus, stream);
+      default: return launch_persistent<FA, FB, YF, kNarrowNone>(g, p, num_cus, stream);
     }
+  } else {
+    return launch_plan<FA, FB, YF, ACC, kNarrowNone>(g, p, stream);
   }
-  return launch_plan<FA, FB, YF, ACC, kNarrowNone>(g, p, stream);
 }
 
 template <int FA, int FB, int ACC>
