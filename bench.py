@@ -72,11 +72,18 @@ def parse():
     return ap.parse_args()
 
 
+GEMM_SOURCES = ("gemm_kernels.h", "gemm_parts.h", "gemm.hip", "gemm_exact_a4.hip", "gemm_exact_a5.hip", "gemm_fast.hip")
+
+
 def source_digest() -> str:
-    """Digest of the GEMM kernel source; counter readings are valid only for the source they were taken on."""
+    """Digest of the GEMM sources (in this order); counter readings are valid only for the sources they were taken
+    on."""
     import hashlib
-    with open(os.path.join(ROOT, "fp8_mixed_precision_cast_amd", "csrc", "gemm.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "fp8_mixed_precision_cast_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def copy_reference(nbytes: int) -> None:
