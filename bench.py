@@ -614,10 +614,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
                      "traffic": traffic,
-                     "kernel": ("gemm_fp8_kernel (fp8 MFMA, fast accumulation)" if fast else
-                                "gemm_fp8_kernel (bf16 MFMA on widened FP8, fused output cast)"
-                                if args.output_cast.startswith("fused") else
-                                "gemm_exact_persistent_kernel (bf16 MFMA on widened FP8)"),
+                     "kernel": (("gemm_fp8_kernel" if args.output_cast.startswith("fused") else
+                                 "gemm_persistent_kernel") + " (fp8 MFMA, fast accumulation)" if fast else
+                                "gemm_persistent_kernel (bf16 MFMA on widened FP8)"),
                      "instruction_peak": PEAK_FP8_MFMA_TFLOPS if fast else PEAK_BF16_MFMA_TFLOPS,
                      "frac_of_instruction_peak": round(gemm_tflops / (PEAK_FP8_MFMA_TFLOPS if fast else
                                                                       PEAK_BF16_MFMA_TFLOPS), 4)},

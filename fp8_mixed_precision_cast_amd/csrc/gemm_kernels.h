@@ -757,16 +757,52 @@ __device__ __forceinline__ void next_copies_and_wave_out(
   }
 }
 
+// Wave-level amax commit: the same skip-or-atomic rule as block_amax_commit,
+// once per wave (the persistent kernel has no LDS left for a block reduction).
+__device__ __forceinline__ void wave_amax_commit(uint32_t m, float* amax) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(m, off, 64);
+    m = m > o ? m : o;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    const uint32_t r = canonical_nan(m);
+    unsigned int* a = reinterpret_cast<unsigned int*>(amax);
+    if (r != 0u && r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
+  }
+}
+
+// K loop of the fast-accumulation GEMM (FP8 MFMA) from published stages:
+// steps 0 and 1 are in the two stages (exact_first_copies, waited for, then
+// a barrier). Step kt reads stage kt & 1 and, from inside it, copies step
+// kt + 1 into the other stage (from step 1 on: step 1 is already there).
+template <class GM, int FA, int FB>
+__device__ __forceinline__ void fast_k_steps(uint8_t* smem, int nk, const TileCopy& ca, const TileCopy& cb,
+                                             uint32_t K, Acc<GM>& acc, int wm, int wn, int wave, int lane) {
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = smem + (kt & 1) * 2 * kTileBytes;
+    uint8_t* nxt = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+    // Steps 0 and 1 were waited for before the loop; a later step's copy was
+    // issued by the step before it. The barrier publishes step kt and retires
+    // every read of the stage the next copy overwrites (step 0 is published).
+    if (kt > 1) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (kt > 0) __syncthreads();
+    pipelined_step_fast<GM, FA, FB>(cur, nxt, kt >= 1 && kt + 1 < nk, ca, cb, (uint32_t)(kt + 1) * kBK, K, acc, wm,
+                                    wn, wave, lane);
+  }
+}
+
 // One tile of geometry GM at (m0, n0) whose steps 0 and 1 are in the stages
 // and published. With has_next, the next tile's steps 0 and 1 (origin nm0,
 // nn0, heights cap_m x cap_n) are copied in before this tile's output is
 // stored; on return they are published. YF = a format: the output is also
 // cast as fp8_amax_cast would cast C (codes to y_q under the scale ys when
-// y_q is given; the magnitude max folded into am, packed BF16 pairs).
-template <class GM, int FA, int FB, int YF>
+// y_q is given; the tile's magnitude max committed to *y_amax, one atomic per
+// wave at most, when y_amax is given). ACC picks the K loop: BF16 MFMA on
+// widened codes, or the FP8 MFMA.
+template <class GM, int FA, int FB, int YF, int ACC>
 __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                                                 int64_t M, int64_t N, int64_t K, float s1, float s2, uint16_t* C,
-                                                int64_t ldc, uint8_t* y_q, int64_t ld_yq, float ys, uint32_t& am,
+                                                int64_t ldc, uint8_t* y_q, int64_t ld_yq, float ys, float* y_amax,
                                                 uint8_t* smem, uint8_t* band, int64_t m0, int64_t n0, bool has_next,
                                                 int64_t nm0, int64_t nn0, int cap_m, int cap_n) {
   constexpr int kPM = GM::PM;
@@ -781,7 +817,10 @@ __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, c
   {
     const TileCopy ca = make_copy(A, lda, m0, M, K, GM::BM, wave, lane);
     const TileCopy cb = make_copy(B, ldb, n0, N, K, GM::BN, wave, lane);
-    exact_k_steps<GM, FA, FB>(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
+    if constexpr (ACC == kAccExact)
+      exact_k_steps<GM, FA, FB>(smem, smem + 2 * kTileBytes, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
+    else
+      fast_k_steps<GM, FA, FB>(smem, nk, ca, cb, Ku, acc, wm, wn, wave, lane);
   }
   // every wave is done reading the stages: the next tile's first steps may land there
   __syncthreads();
@@ -806,6 +845,7 @@ __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, c
   const int ewm = ewave / GM::WavesN, ewn = ewave % GM::WavesN;
   const int64_t r0 = m0 + ewm * GM::WM, c0 = n0 + ewn * GM::WN;
   const bool do_c = C != nullptr, do_q = YF != kNoY && y_q != nullptr;
+  uint32_t am = 0;   // packed BF16 magnitudes of this thread's outputs in the tile
   if (m0 + GM::BM <= M && n0 + GM::BN <= N) {
     // interior tile: 16-byte C stores; with the cast, the magnitude max of
     // this thread's values also tells whether any is NaN (the two encoders
@@ -879,19 +919,8 @@ __device__ __forceinline__ void persistent_tile(const uint8_t* A, int64_t lda, c
         }
       }
   }
-}
-
-// Wave-level amax commit: the same skip-or-atomic rule as block_amax_commit,
-// once per wave (the persistent kernel has no LDS left for a block reduction).
-__device__ __forceinline__ void wave_amax_commit(uint32_t m, float* amax) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(m, off, 64);
-    m = m > o ? m : o;
-  }
-  if ((threadIdx.x & 63) == 0) {
-    const uint32_t r = canonical_nan(m);
-    unsigned int* a = reinterpret_cast<unsigned int*>(amax);
-    if (r != 0u && r > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, r);
+  if constexpr (YF != kNoY) {
+    if (y_amax != nullptr) wave_amax_commit(bf16x2_acc_to_f32_bits(am), y_amax);
   }
 }
 
@@ -899,8 +928,8 @@ __device__ __forceinline__ void wave_amax_commit(uint32_t m, float* amax) {
 // of the BF16 output C on the fly, exactly as fp8_amax_cast would on C:
 // *y_amax = max(*y_amax, max|C|) (if y_amax) and y_q = enc_YF(C * *y_scale)
 // (if y_q); C may then be null.
-template <int FA, int FB, int YF, int NARROW>
-__global__ __launch_bounds__(kThreads) void gemm_exact_persistent_kernel(
+template <int FA, int FB, int YF, int ACC, int NARROW>
+__global__ __launch_bounds__(kThreads) void gemm_persistent_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M, int64_t N,
     int64_t K, const float* __restrict__ sa, const float* __restrict__ sb, uint16_t* __restrict__ C, int64_t ldc,
     TilePlan plan, const float* __restrict__ y_scale, uint8_t* __restrict__ y_q, int64_t ld_yq,
@@ -915,7 +944,6 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_persistent_kernel(
   float s1, s2;
   epilogue_scales(*sa, *sb, s1, s2);
   const float ys = YF != kNoY && y_q != nullptr ? *y_scale : 0.f;
-  uint32_t am = 0;   // packed BF16 magnitudes of this thread's outputs, over all its tiles
   int bid = blockIdx.x;
   int64_t m0, n0;
   bool narrow = plan_tile<NARROW>(bid, plan, m0, n0);
@@ -933,19 +961,16 @@ __global__ __launch_bounds__(kThreads) void gemm_exact_persistent_kernel(
     const bool next_narrow = has_next && plan_tile<NARROW>(next, plan, nm0, nn0);
     const int cap_m = next_narrow ? G2::BM : kBM, cap_n = next_narrow ? G2::BN : kBN;
     if (NARROW != kNarrowNone && narrow)
-      persistent_tile<G2, FA, FB, YF>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, y_q, ld_yq, ys, am, smem, band, m0,
-                                      n0, has_next, nm0, nn0, cap_m, cap_n);
+      persistent_tile<G2, FA, FB, YF, ACC>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, y_q, ld_yq, ys, y_amax, smem, band,
+                                           m0, n0, has_next, nm0, nn0, cap_m, cap_n);
     else
-      persistent_tile<GFull, FA, FB, YF>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, y_q, ld_yq, ys, am, smem, band,
-                                         m0, n0, has_next, nm0, nn0, cap_m, cap_n);
+      persistent_tile<GFull, FA, FB, YF, ACC>(A, lda, B, ldb, M, N, K, s1, s2, C, ldc, y_q, ld_yq, ys, y_amax, smem,
+                                              band, m0, n0, has_next, nm0, nn0, cap_m, cap_n);
     if (!has_next) break;
     bid = next;
     m0 = nm0;
     n0 = nn0;
     narrow = next_narrow;
-  }
-  if constexpr (YF != kNoY) {
-    if (y_amax != nullptr) wave_amax_commit(bf16x2_acc_to_f32_bits(am), y_amax);
   }
 }
 
@@ -1000,24 +1025,29 @@ hipError_t launch_plan(const GemmArgs& g, const TilePlan& p, hipStream_t stream)
   return hipGetLastError();
 }
 
-// The FP32-accumulation GEMM, plain or with the fused output cast, takes the
-// tile plan and runs persistent. Measured on one MI355X: the tile plan is
-// 1-3% faster at 4096 x 11008 x 4096 (7B backward, 13B projections); the
-// fast-accumulation GEMM was up to 6% slower with it (the chip runs at its
-// power limit there, and a full last round lowers the clock), so it keeps
-// whole tiles in a launch of one workgroup per tile. The persistent walk
-// gains 1.5-7.5% where K is small next to the output (16384 x 16384 x 512 ..
-// 8192 x 8192 x 2048) and is even at K = 4096 and 8192 for the plain GEMM,
-// where the chip sits at its power limit either way; with the fused output
-// cast, whose code stores now also drain under the next tile, the 7B GEMM
-// took 265 instead of 272 us.
-template <int FA, int FB, int YF, int NARROW>
+// Launch choice. The FP32-accumulation GEMM, plain or with the fused output
+// cast, takes the tile plan and runs persistent. The plain fast-accumulation
+// GEMM runs persistent on whole tiles; its fused-cast form keeps one
+// workgroup per tile (in the persistent kernel its K loop spills registers).
+// Measured on one MI355X:
+// - the tile plan is 1-3% faster for the exact GEMM at 4096 x 11008 x 4096
+//   (7B backward, 13B projections) and up to 6% slower for the fast one (the
+//   chip runs at its power limit there, and a full last round lowers the
+//   clock);
+// - the persistent walk gains 1.5-7.5% for the exact GEMM where K is small
+//   next to the output (16384 x 16384 x 512 .. 8192 x 8192 x 2048) and is
+//   even at K = 4096 and 8192, where the chip sits at its power limit either
+//   way; with the fused output cast, whose code stores also drain under the
+//   next tile, the 7B GEMM took 265 instead of 272 us;
+// - for the fast GEMM it gains 2-3% at 4096 x 11008 x 4096 and at the 70B
+//   slice and 4-13% at the small-K shapes.
+template <int FA, int FB, int YF, int ACC, int NARROW>
 hipError_t launch_persistent(const GemmArgs& g, const TilePlan& p, int num_cus, hipStream_t stream) {
   const int total = p.tm * p.tn + p.tm2 * p.tn2;
   // one workgroup per CU, a multiple of 8 so that each keeps to its XCD's tile ids
   const int slots = num_cus >= 8 ? num_cus / 8 * 8 : total;
   const unsigned grid = (unsigned)(total < slots ? total : slots);
-  hipLaunchKernelGGL((gemm_exact_persistent_kernel<FA, FB, YF, NARROW>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_persistent_kernel<FA, FB, YF, ACC, NARROW>), dim3(grid), dim3(kThreads), 0, stream,
                      g.a, g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, p, g.y_scale, g.y_q, g.ld_yq,
                      g.y_amax);
   return hipGetLastError();
@@ -1029,12 +1059,14 @@ hipError_t launch_one(const GemmArgs& g, int num_cus, hipStream_t stream) {
   const int kind = plan_tiles(g.m, g.n, ACC == kAccExact ? num_cus : 0, p);
   if constexpr (ACC == kAccExact) {
     switch (kind) {
-      case kNarrowN192: return launch_persistent<FA, FB, YF, kNarrowN192>(g, p, num_cus, stream);
-      case kNarrowN128: return launch_persistent<FA, FB, YF, kNarrowN128>(g, p, num_cus, stream);
-      case kNarrowM192: return launch_persistent<FA, FB, YF, kNarrowM192>(g, p, num_cus, stream);
-      case kNarrowM128: return launch_persistent<FA, FB, YF, kNarrowM128>(g, p, num_cus, stream);
-      default: return launch_persistent<FA, FB, YF, kNarrowNone>(g, p, num_cus, stream);
+      case kNarrowN192: return launch_persistent<FA, FB, YF, ACC, kNarrowN192>(g, p, num_cus, stream);
+      case kNarrowN128: return launch_persistent<FA, FB, YF, ACC, kNarrowN128>(g, p, num_cus, stream);
+      case kNarrowM192: return launch_persistent<FA, FB, YF, ACC, kNarrowM192>(g, p, num_cus, stream);
+      case kNarrowM128: return launch_persistent<FA, FB, YF, ACC, kNarrowM128>(g, p, num_cus, stream);
+      default: return launch_persistent<FA, FB, YF, ACC, kNarrowNone>(g, p, num_cus, stream);
     }
+  } else if constexpr (YF == kNoY) {
+    return launch_persistent<FA, FB, YF, ACC, kNarrowNone>(g, p, num_cus, stream);
   } else {
     return launch_plan<FA, FB, YF, ACC, kNarrowNone>(g, p, stream);
   }

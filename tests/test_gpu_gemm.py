@@ -294,26 +294,34 @@ PERSISTENT_SHAPES = [(4100, 4100, 16), (4100, 4100, 256), (4100, 4100, 368), (81
 
 
 @pytest.mark.parametrize("shape", PERSISTENT_SHAPES)
-def test_gemm_workgroups_walking_several_tiles(shape):
+@pytest.mark.parametrize("call", ["exact", "fast"])
+def test_gemm_workgroups_walking_several_tiles(shape, call):
+    """Every output against the oracle (the FP32 bound for the exact GEMM, the fast bound for the FP8
+    instruction), and the correctly rounded product on exact sums, in both modes."""
     require_gpu()
+    from oracle.gemm import FAST_ACCUM_SUM_COEF
     m, n, k = shape
+    f = fp8.fp8_scaled_gemm if call == "exact" else fp8.fp8_scaled_gemm_fast_accum
+    coef = oracle.gemm.SUM_COEF if call == "exact" else FAST_ACCUM_SUM_COEF
     rng = np.random.default_rng(m + 5 * n + 11 * k)
     a = _codes(rng, (m, k), "e4m3", spread=40)
     b = _codes(rng, (n, k), "e5m2", spread=40)
     sa, sb = np.float32(0.75), np.float32(1 / 5.0)
-    banner("gemm persistent walk", shape)
+    banner("gemm persistent walk", call, shape)
     c, store = pitched(m, n, torch.int16, fill=0x7FC1, pad_bytes=16)
-    fp8.fp8_scaled_gemm(dev(a), "e4m3", dev(b), "e5m2", f32(sa), f32(sb), c)
+    f(dev(a), "e4m3", dev(b), "e5m2", f32(sa), f32(sb), c)
     out = host(store)
     assert (out[:, n:] == 0x7FC1).all(), "wrote past n"
-    _check(a, "e4m3", b, "e5m2", sa, sb, out[:, :n], f"walk {shape}")
+    ok, worst = oracle.gemm_check(out[:, :n], oracle.gemm_ref(a, "e4m3", b, "e5m2", sa, sb),
+                                  oracle.gemm_abs_ref(a, "e4m3", b, "e5m2", sa, sb), coef)
+    assert ok, f"{call} walk {shape}: worst |err|/bound {worst}"
     # exact sums: one magnitude per row of A and of B, so the output is the correctly rounded product
     e_a = rng.integers(4, 12, m)
     e_b = rng.integers(4, 12, n)
     a = ((e_a[:, None] << 3) | (rng.integers(0, 2, (m, k)) << 7)).astype(np.uint8)
     b = ((e_b[:, None] << 3) | (rng.integers(0, 2, (n, k)) << 7)).astype(np.uint8)
     c1, store1 = pitched(m, n, torch.int16, fill=0x7FC1)
-    fp8.fp8_scaled_gemm(dev(a), "e4m3", dev(b), "e4m3", f32(1.0), f32(1.0), c1)
+    f(dev(a), "e4m3", dev(b), "e4m3", f32(1.0), f32(1.0), c1)
     want = _exact_bits(a, b).view(np.uint16)
     got = host(store1)[:, :n].view(np.uint16)
     assert np.array_equal(got, want), first_diff(got, want)

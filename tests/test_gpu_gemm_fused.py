@@ -201,3 +201,20 @@ def test_fused_refuses_misaligned_code_outputs():
             fp8.fp8_scaled_gemm_amax_cast(a, "e4m3", a, "e4m3", f32(1.0), f32(1.0), c, "e4m3", f32(1.0), yq, None)
         assert ei.value.status == 1, name
     assert (host(store) == 0x5A).all()
+
+
+# The FP32-accumulation GEMM with the fused cast walks several tiles per workgroup here (more tiles than CUs),
+# storing each tile's BF16 output and codes while the next one runs; one shape switches to narrow tiles for
+# its last round. The amax is folded over all of a workgroup's tiles before it is committed.
+WALK_SHAPES = [(4100, 4100, 256), (8192, 8448, 144)]
+
+
+@pytest.mark.parametrize("shape", WALK_SHAPES)
+def test_fused_on_workgroups_walking_several_tiles(shape):
+    require_gpu()
+    m, n, k = shape
+    rng = np.random.default_rng(m + 7 * n + 3 * k)
+    a, b = _codes(rng, (m, k), "e4m3"), _codes(rng, (n, k), "e5m2")
+    for yf, ys, pad in (("e4m3", 1.0, 0), ("e5m2", 1e6, 16)):
+        banner("fused walk", shape, yf, ys)
+        _fused(a, "e4m3", b, "e5m2", 0.5, 1 / 3.0, yf, ys, amax0=0.0, ldq_pad=pad)
