@@ -137,7 +137,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
 __device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4); }
 
 // Tile id -> (tile row, tile column); a bijection on [0, tm * tn).
-__device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& bm, int& bn) {
+__host__ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& bm, int& bn) {
   const int ntiles = tm * tn;
   const int per = ntiles / kXcds, rem = ntiles % kXcds;
   const int xcd = bid % kXcds, local = bid / kXcds;
@@ -681,7 +681,7 @@ constexpr int kBandBytes = 8 * 4096;   // eight waves' 4 KB output slices
 
 // Tile id -> origin and kind (narrow or whole) under the tile plan.
 template <int NARROW>
-__device__ __forceinline__ bool plan_tile(int bid, const TilePlan& plan, int64_t& m0, int64_t& n0) {
+__host__ __device__ __forceinline__ bool plan_tile(int bid, const TilePlan& plan, int64_t& m0, int64_t& n0) {
   using G2 = typename NarrowGeom<NARROW>::G;
   const int n_full = plan.tm * plan.tn;
   int bm, bn;
@@ -1041,12 +1041,17 @@ hipError_t launch_plan(const GemmArgs& g, const TilePlan& p, hipStream_t stream)
 //   next tile, the 7B GEMM took 265 instead of 272 us;
 // - for the fast GEMM it gains 2-3% at 4096 x 11008 x 4096 and at the 70B
 //   slice and 4-13% at the small-K shapes.
+// Workgroups of a persistent launch over `total` tiles: one per CU, a
+// multiple of 8 so that each keeps to its XCD's tile ids (all tiles when
+// fewer, or when the device reports fewer than 8 CUs).
+inline int persistent_grid(int total, int num_cus) {
+  const int slots = num_cus >= 8 ? num_cus / 8 * 8 : total;
+  return total < slots ? total : slots;
+}
+
 template <int FA, int FB, int YF, int ACC, int NARROW>
 hipError_t launch_persistent(const GemmArgs& g, const TilePlan& p, int num_cus, hipStream_t stream) {
-  const int total = p.tm * p.tn + p.tm2 * p.tn2;
-  // one workgroup per CU, a multiple of 8 so that each keeps to its XCD's tile ids
-  const int slots = num_cus >= 8 ? num_cus / 8 * 8 : total;
-  const unsigned grid = (unsigned)(total < slots ? total : slots);
+  const unsigned grid = (unsigned)persistent_grid(p.tm * p.tn + p.tm2 * p.tn2, num_cus);
   hipLaunchKernelGGL((gemm_persistent_kernel<FA, FB, YF, ACC, NARROW>), dim3(grid), dim3(kThreads), 0, stream,
                      g.a, g.lda, g.b, g.ldb, g.m, g.n, g.k, g.sa, g.sb, g.c, g.ldc, p, g.y_scale, g.y_q, g.ld_yq,
                      g.y_amax);
