@@ -12,11 +12,12 @@
 // MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4 and the older fp8 forms) run twice
 // as fast but reduce each dot product with only about 17 bits relative to its
 // largest product (measured: up to 7e-5 of sum|a*b| per instruction), which
-// exceeds the tolerance on outputs that cancel; they are not used. (The
-// 16x16x32 BF16 form issues at half the 32x32x16 rate on gfx950.)
+// exceeds the tolerance on outputs that cancel, so the FP32-accumulation GEMM
+// does not use them. (The 16x16x32 BF16 form issues at half the 32x32x16
+// rate on gfx950.)
 //
 // Fast accumulation (ACC = kAccFast) is the opt-in alternative: the same
-// tiles, copies and epilogue, but the FP8 fragments go unwidened into
+// tiles, copies and epilogues, but the FP8 fragments go unwidened into
 // v_mfma_f32_32x32x64_f8f6f4 at twice the MAC rate. Each such instruction
 // aligns its 64 products to the largest one and keeps about 16 bits below it
 // (measured on gfx950: errors up to 2^-10.9 of the largest product), so the
@@ -28,7 +29,10 @@
 // whole rounds of 256 x 256 tiles and re-tiles the remaining columns (or rows)
 // into exactly one round of narrower tiles (256 x 192 or 256 x 128 as 4 x 2
 // waves, or 192 x 256 or 128 x 256 as 2 x 4 waves): at 4096 x 11008 every CU
-// then does 2.75 tiles' work instead of 3 rounds of whole tiles. Tiles of A
+// then does 2.75 tiles' work instead of 3 rounds of whole tiles. One
+// workgroup per CU walks its tiles (persistent launch) and stores each tile's
+// output while the next one computes; the fast GEMM with the fused output
+// cast instead launches one workgroup per tile. Tiles of A
 // and B are copied global -> LDS directly (buffer_load_dwordx4 ... lds, no
 // VGPR staging) into a double buffer, so the next K step streams in while
 // this one is multiplied; in the FP32-accumulation loop each step's barrier
@@ -45,10 +49,10 @@
 // the tile transposed and each lane ends up holding four consecutive output
 // columns of one output row. The epilogue scales by sa_inv * sb_inv, rounds to
 // BF16 (v_cvt_pk_bf16_f32, round to nearest even), turns the lanes' pieces
-// into row-contiguous 16-byte chunks through LDS (the FP32-accumulation
-// GEMM through a private 4 KB slice per wave, the fast one through the whole
-// 256 x 256 BF16 tile staged in the two stages' 128 KB) and writes them out
-// with 16-byte stores.
+// into row-contiguous 16-byte chunks through LDS (the persistent kernel
+// through a private 4 KB slice per wave, the one-tile kernel through the
+// whole 256 x 256 BF16 tile staged in the two stages' 128 KB) and writes
+// them out with 16-byte stores.
 //
 // This header holds the kernels and their launch templates; gemm_exact_a4.hip,
 // gemm_exact_a5.hip and gemm_fast.hip instantiate them (split so that the
@@ -640,10 +644,10 @@ struct TilePlan {
   int64_t m2_off, n2_off;
 };
 
-// YF = kNoY: the plain GEMM. YF = a format: the epilogue also runs the cast
-// of the BF16 output C on the fly, exactly as fp8_amax_cast would on C:
-// *y_amax = max(*y_amax, max|C|) (if y_amax) and y_q = enc_YF(C * *y_scale)
-// (if y_q).
+// One workgroup per tile (the fast GEMM with the fused output cast). YF = a
+// format: the epilogue also runs the cast of the BF16 output C on the fly,
+// exactly as fp8_amax_cast would on C: *y_amax = max(*y_amax, max|C|) (if
+// y_amax) and y_q = enc_YF(C * *y_scale) (if y_q).
 template <int FA, int FB, int YF, int ACC, int NARROW>
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb, int64_t M,
@@ -666,17 +670,18 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(
   }
 }
 
-// Persistent form of the plain FP32-accumulation GEMM. A launch of whole
-// workgroups lets every tile of a round finish at once, and then every CU
-// waits while the whole round's output (32 MB at 4096 x 4096) drains to HBM
-// and while its next tile's first K steps arrive. Here each workgroup walks
-// its tiles (ids blockIdx.x, blockIdx.x + gridDim.x, ...; gridDim.x is a
-// multiple of 8, so a workgroup stays on its XCD's run of tile ids) and
-// overlaps the two: at the end of a tile it issues the copies of the next
-// tile's steps 0 and 1 into the free stages, turns its BF16 output into
-// row-contiguous chunks in registers through a separate 32 KB of LDS,
-// waits for the copies, and only then issues the output stores, which drain
-// while the next tile runs (its first wait for a copy comes at its step 2).
+// Persistent form of the GEMM (both accumulation modes, and the exact one
+// with the fused output cast). A launch of one workgroup per tile lets every
+// tile of a round finish at once, and then every CU waits while the whole
+// round's output (32 MB at 4096 x 4096) drains to HBM and while its next
+// tile's first K steps arrive. Here each workgroup walks its tiles (ids
+// blockIdx.x, blockIdx.x + gridDim.x, ...; gridDim.x is a multiple of 8, so a
+// workgroup stays on its XCD's run of tile ids): at the end of a tile it
+// turns its BF16 output into row-contiguous chunks in registers through a
+// separate 32 KB of LDS, copies the next tile's steps 0 and 1 into the free
+// stages and waits for them, and only then issues the output stores, which
+// drain while the next tile runs (its first wait for a copy comes at its
+// step 2).
 constexpr int kBandBytes = 8 * 4096;   // eight waves' 4 KB output slices
 
 // Tile id -> origin and kind (narrow or whole) under the tile plan.
