@@ -75,14 +75,38 @@ def parse():
 GEMM_SOURCES = ("gemm_kernels.h", "gemm_parts.h", "gemm.hip", "gemm_exact_a4.hip", "gemm_exact_a5.hip", "gemm_fast.hip")
 
 
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: what the compiler sees."""
+    import re
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src[i] in "\"'":
+            q, j = src[i], i + 1
+            while j < n and src[j] != q:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_digest() -> str:
-    """Digest of the GEMM sources (in this order); counter readings are valid only for the sources they were taken
-    on."""
+    """Digest of the GEMM sources' code (in this order, comments and whitespace left out); counter readings are
+    valid only for the code they were taken on."""
     import hashlib
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "fp8_mixed_precision_cast_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "fp8_mixed_precision_cast_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -20,3 +20,13 @@ def test_help_lists_the_workload_switches():
     for flag in ("--steps", "--warmup", "--workload", "--recipe", "--output-cast", "--layernorm", "--gemm-accum", "--no-graph", "--gemm-data",
                  "--copy-reference"):
         assert flag in r.stdout
+
+
+def test_source_digest_ignores_comments_and_whitespace_only():
+    """The counters' digest follows the GEMM code, not its comments: stripping keeps code and string literals."""
+    import bench
+    a = bench.code_text('int f() { return 1; } // one\n/* block */\nconst char* s = "// kept";')
+    b = bench.code_text('int  f()  {\n  return 1;\n}\nconst char* s = "// kept";   // trailing')
+    assert a == b == 'int f() { return 1; } const char* s = "// kept";'
+    assert bench.code_text("x = 1;") != bench.code_text("x = 2;")
+    assert len(bench.source_digest()) == 16
