@@ -325,3 +325,36 @@ def test_gemm_workgroups_walking_several_tiles(shape, call):
     want = _exact_bits(a, b).view(np.uint16)
     got = host(store1)[:, :n].view(np.uint16)
     assert np.array_equal(got, want), first_diff(got, want)
+
+
+def _seeded_walk_shapes(count=6, seed=20261203):
+    """Ragged shapes with more tiles than CUs (so workgroups walk several tiles, and partly filled last rounds
+    take the narrow plan where it applies), small K to keep the oracle quick; fixed by the seed."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(4097, 9001)), int(rng.integers(4097, 9001)), int(rng.choice([16, 48, 144, 272])))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("shape", _seeded_walk_shapes())
+@pytest.mark.parametrize("call", ["exact", "fast"])
+def test_gemm_seeded_ragged_walks(shape, call):
+    """Every output of seeded ragged multi-round launches against the oracle, in both modes, and no write past
+    the last column."""
+    require_gpu()
+    from oracle.gemm import FAST_ACCUM_SUM_COEF
+    m, n, k = shape
+    f = fp8.fp8_scaled_gemm if call == "exact" else fp8.fp8_scaled_gemm_fast_accum
+    coef = oracle.gemm.SUM_COEF if call == "exact" else FAST_ACCUM_SUM_COEF
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    af, bf = ("e4m3", "e4m3") if (m + n) % 2 else ("e5m2", "e4m3")
+    a = _codes(rng, (m, k), af, spread=40)
+    b = _codes(rng, (n, k), bf, spread=40)
+    sa, sb = np.float32(1.25), np.float32(0.125)
+    banner("gemm seeded walk", call, af, bf, shape)
+    c, store = pitched(m, n, torch.int16, fill=0x7FC1, pad_bytes=32)
+    f(dev(a), af, dev(b), bf, f32(sa), f32(sb), c)
+    out = host(store)
+    assert (out[:, n:] == 0x7FC1).all(), "wrote past n"
+    ok, worst = oracle.gemm_check(out[:, :n], oracle.gemm_ref(a, af, b, bf, sa, sb),
+                                  oracle.gemm_abs_ref(a, af, b, bf, sa, sb), coef)
+    assert ok, f"{call} {af}x{bf} {shape}: worst |err|/bound {worst}"
