@@ -163,6 +163,9 @@ __host__ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, in
 // on odd ones.
 struct TileCopy {
   __amdgpu_buffer_rsrc_t rsrc;   // this tile's rows of the operand; loads past their end return 0
+  uint32_t off[kSlabs];          // this lane's byte offset in slab j at k = 0
+  int here;                      // rows of the tile that exist (wave-uniform)
+  // the same offsets in the per-lane form of load_tile_rows
   uint32_t base;                 // byte offset of row 8 * kSlabs * wave + lane / 8 at k = 0
   uint32_t stride8;              // 8 rows
   uint32_t kc0, kc1;             // c * 16 on even and odd slabs
@@ -179,6 +182,14 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 // their maxima (not waited on).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Byte offset within the K step of the 16-byte chunk that a lane copies in
+// slab j: row group lane / 8 takes chunk c = (lane % 8) ^ (lane / 8 % 8) on
+// even slabs and c ^ 1 on odd ones (the LDS swizzle of the fragment reads).
+__device__ __forceinline__ uint32_t slab_kc(int j, int lane) {
+  const int c = (lane & 7) ^ ((lane >> 3) & 7);
+  return (uint32_t)((j & 1) ? c ^ 1 : c) * 16u;
+}
+
 // The buffer resource starts at the tile's first row, so operands of any size
 // are addressed with 32-bit offsets.
 // cap: the tile's height in rows (256, or a narrow tile's 192 or 128).
@@ -189,6 +200,9 @@ __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int6
   const uint32_t bytes = (uint32_t)((here - 1) * ld + K);
   t.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(G + row0 * ld), (short)0, (int)bytes, 0x00020000);
   const int r = wave * 8 * kSlabs + (lane >> 3);
+#pragma unroll
+  for (int j = 0; j < kSlabs; ++j) t.off[j] = (uint32_t)((r + 8 * j) * ld) + slab_kc(j, lane);
+  t.here = (int)here;
   const int c = (lane & 7) ^ ((lane >> 3) & 7);
   t.kc0 = (uint32_t)c * 16u;
   t.kc1 = (uint32_t)(c ^ 1) * 16u;
@@ -200,13 +214,50 @@ __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int6
   return t;
 }
 
-// Copies K step [k0, k0 + 128) of one operand into an LDS tile. Chunks of
-// missing rows or past K are read out of range, which stores zeros. With
-// SKIP_EMPTY, a lane none of whose rows exists (all of a wave's rows lie
-// beyond a narrow tile's height) issues nothing: those LDS rows are never
-// read. Without it the copy has no branch (such lanes store zeros).
+// Copies K step [k0, k0 + 128) of one operand into an LDS tile. A row
+// beyond the tile's height lies past the end of the buffer resource (its
+// offset is at least here * ld >= (here - 1) * ld + K), so its chunks read
+// zeros. With SKIP_EMPTY, a wave whose rows all lie beyond the tile's height
+// (a narrow tile's unused waves) issues nothing: those LDS rows are never
+// read.
+//
+// load_tile_inner: a step wholly inside K (k0 + kBK <= K). k0 goes in the
+// scalar offset and the LDS slab addresses are wave-uniform, so a load takes
+// no vector arithmetic. Whether or not the hardware's range check counts the
+// scalar offset, it finds the same rows in and out of range here.
+template <bool SKIP_EMPTY = true>
+__device__ __forceinline__ void load_tile_inner(const TileCopy& t, uint32_t k0, uint8_t* lds, int wave) {
+  const int uw = __builtin_amdgcn_readfirstlane(wave);
+  if (SKIP_EMPTY && uw * 8 * kSlabs >= t.here) return;
+  const uint32_t uk = __builtin_amdgcn_readfirstlane(k0);
+#pragma unroll
+  for (int j = 0; j < kSlabs; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        t.rsrc, (__attribute__((address_space(3))) void*)(lds + (uw * kSlabs + j) * 1024), 16, t.off[j], (int)uk, 0,
+        0);
+}
+
+// load_tile: any step. A chunk past K (which would read the next row's
+// bytes) is read at an offset out of range, which stores zeros.
 template <bool SKIP_EMPTY = true>
 __device__ __forceinline__ void load_tile(const TileCopy& t, uint32_t k0, uint32_t K, uint8_t* lds, int wave) {
+  const int uw = __builtin_amdgcn_readfirstlane(wave);
+  if (SKIP_EMPTY && uw * 8 * kSlabs >= t.here) return;
+  const int lane = (int)(threadIdx.x & 63u);
+#pragma unroll
+  for (int j = 0; j < kSlabs; ++j) {
+    const uint32_t off = k0 + slab_kc(j, lane) < K ? t.off[j] + k0 : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        t.rsrc, (__attribute__((address_space(3))) void*)(lds + (uw * kSlabs + j) * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+// load_tile_rows: the copy of the FP8-MFMA K loop, as load_tile with the
+// offsets, row and K masks formed per lane, and a lane none of whose rows
+// exists issuing nothing. That loop measured 3-4% slower with the
+// cheaper copies above (load_tile, or load_tile_inner for inner steps).
+template <bool SKIP_EMPTY = true>
+__device__ __forceinline__ void load_tile_rows(const TileCopy& t, uint32_t k0, uint32_t K, uint8_t* lds, int wave) {
   if (SKIP_EMPTY && t.row_ok == 0) return;
   // all-ones where the chunk exists: a branch-free choice between its offset and out of range
   const uint32_t km0 = 0u - (uint32_t)(k0 + t.kc0 < K), km1 = 0u - (uint32_t)(k0 + t.kc1 < K);
@@ -279,8 +330,8 @@ __device__ __forceinline__ void pipelined_step_fast(const uint8_t* __restrict__ 
                                                     int wave, int lane) {
   auto issue = [&]() {
     if (more) {
-      load_tile(ca, k_next, K, nxt, wave);
-      load_tile(cb, k_next, K, nxt + kTileBytes, wave);
+      load_tile_rows(ca, k_next, K, nxt, wave);
+      load_tile_rows(cb, k_next, K, nxt + kTileBytes, wave);
     }
   };
   mma_step_fast<GM, FA, FB>(cur, cur + kTileBytes, acc, wm, wn, lane, issue);
@@ -377,8 +428,9 @@ __device__ __forceinline__ void exact_chunks012(const uint8_t* rd, ExactRegs<GM>
 //
 // rd and wr never overlap; saying so (restrict) lets the compiler keep the
 // copy into wr in flight while rd is read, here and in the next body (whose
-// reads are of this body's wr, after its own wait and barrier).
-template <class GM, int FA, int FB>
+// reads are of this body's wr, after its own wait and barrier). INNER: step
+// k + 1 lies wholly inside K, and its copy takes the scalar-offset form.
+template <class GM, int FA, int FB, bool INNER>
 __device__ __forceinline__ void exact_body(const uint8_t* __restrict__ rd, uint8_t* __restrict__ wr, int k,
                                            const TileCopy& ca, const TileCopy& cb, uint32_t K, ExactRegs<GM>& r,
                                            Acc<GM>& acc, int ra, int rb, int G, int wave) {
@@ -389,9 +441,15 @@ __device__ __forceinline__ void exact_body(const uint8_t* __restrict__ rd, uint8
   read_frags<GM>(rd, ra, rb, G, 0, r.aq[0], r.bq[0]);
   __builtin_amdgcn_sched_barrier(0);
   exact_chunk<GM, FA, FB, false>(r, acc, 3, [&] {
-    // copy of step k + 1; for k + 1 = nk every chunk lies past K and only zeros are stored
-    load_tile<false>(ca, (uint32_t)(k + 1) * kBK, K, wr, wave);
-    load_tile<false>(cb, (uint32_t)(k + 1) * kBK, K, wr + kTileBytes, wave);
+    // copy of step k + 1 (none for k + 1 = nk: every chunk would lie past K)
+    const uint32_t k0 = (uint32_t)(k + 1) * kBK;
+    if constexpr (INNER) {
+      load_tile_inner<false>(ca, k0, wr, wave);
+      load_tile_inner<false>(cb, k0, wr + kTileBytes, wave);
+    } else if (k0 < K) {
+      load_tile<false>(ca, k0, K, wr, wave);
+      load_tile<false>(cb, k0, K, wr + kTileBytes, wave);
+    }
   });
   exact_chunks012<GM, FA, FB>(rd, r, acc, ra, rb, G);
 }
@@ -436,8 +494,17 @@ __device__ __forceinline__ void exact_k_steps(uint8_t* s0, uint8_t* s1, int nk, 
   exact_chunks012<GM, FA, FB>(s0, r, acc, ra, rb, G);
   uint8_t* rd = s1;
   uint8_t* wr = s0;
-  for (int k = 1; k < nk; ++k) {
-    exact_body<GM, FA, FB>(rd, wr, k, ca, cb, K, r, acc, ra, rb, G, wave);
+  // bodies whose copy (of step k + 1) lies wholly inside K, then the rest
+  const int n_inner = (int)(K / kBK) - 1 < nk ? (int)(K / kBK) - 1 : nk;
+  int k = 1;
+  for (; k < n_inner; ++k) {
+    exact_body<GM, FA, FB, true>(rd, wr, k, ca, cb, K, r, acc, ra, rb, G, wave);
+    uint8_t* t = rd;
+    rd = wr;
+    wr = t;
+  }
+  for (; k < nk; ++k) {
+    exact_body<GM, FA, FB, false>(rd, wr, k, ca, cb, K, r, acc, ra, rb, G, wave);
     uint8_t* t = rd;
     rd = wr;
     wr = t;
