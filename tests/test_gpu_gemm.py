@@ -287,10 +287,11 @@ def _exact_bits(a, b):
 
 
 # Launches with more tiles than CUs, so each workgroup of the FP32-accumulation GEMM walks several tiles
-# (copying the next tile's first K steps while it stores the current one): 1, 2 and 3 K steps per tile
+# (copying the next tile's first K steps while it stores the current one): 1, 2, 3 and 4 K steps per tile
 # (the first waits of the next tile fall inside, at or past its second step), ragged edges in M, N and K,
-# and one shape whose walk switches to 256 x 128 narrow tiles for its last round.
-PERSISTENT_SHAPES = [(4100, 4100, 16), (4100, 4100, 256), (4100, 4100, 368), (8192, 8448, 144)]
+# and one shape whose walk switches to 256 x 128 narrow tiles for its last round. At K = 400 the K loop
+# copies one step wholly inside K (the scalar-offset copy), then the ragged last step (masked).
+PERSISTENT_SHAPES = [(4100, 4100, 16), (4100, 4100, 256), (4100, 4100, 368), (4100, 4100, 400), (8192, 8448, 144)]
 
 
 @pytest.mark.parametrize("shape", PERSISTENT_SHAPES)
