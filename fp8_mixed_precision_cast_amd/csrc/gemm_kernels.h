@@ -221,14 +221,13 @@ __device__ __forceinline__ TileCopy make_copy(const uint8_t* G, int64_t ld, int6
 // (a narrow tile's unused waves) issues nothing: those LDS rows are never
 // read.
 //
-// load_tile_inner: a step wholly inside K (k0 + kBK <= K). k0 goes in the
-// scalar offset and the LDS slab addresses are wave-uniform, so a load takes
-// no vector arithmetic. Whether or not the hardware's range check counts the
-// scalar offset, it finds the same rows in and out of range here.
-template <bool SKIP_EMPTY = true>
+// load_tile_inner: a step wholly inside K (k0 + kBK <= K), every wave
+// copying. k0 goes in the scalar offset and the LDS slab addresses are
+// wave-uniform, so a load takes no vector arithmetic. Whether or not the
+// hardware's range check counts the scalar offset, it finds the same rows in
+// and out of range here.
 __device__ __forceinline__ void load_tile_inner(const TileCopy& t, uint32_t k0, uint8_t* lds, int wave) {
   const int uw = __builtin_amdgcn_readfirstlane(wave);
-  if (SKIP_EMPTY && uw * 8 * kSlabs >= t.here) return;
   const uint32_t uk = __builtin_amdgcn_readfirstlane(k0);
 #pragma unroll
   for (int j = 0; j < kSlabs; ++j)
@@ -444,8 +443,8 @@ __device__ __forceinline__ void exact_body(const uint8_t* __restrict__ rd, uint8
     // copy of step k + 1 (none for k + 1 = nk: every chunk would lie past K)
     const uint32_t k0 = (uint32_t)(k + 1) * kBK;
     if constexpr (INNER) {
-      load_tile_inner<false>(ca, k0, wr, wave);
-      load_tile_inner<false>(cb, k0, wr + kTileBytes, wave);
+      load_tile_inner(ca, k0, wr, wave);
+      load_tile_inner(cb, k0, wr + kTileBytes, wave);
     } else if (k0 < K) {
       load_tile<false>(ca, k0, K, wr, wave);
       load_tile<false>(cb, k0, K, wr + kTileBytes, wave);
