@@ -359,3 +359,43 @@ def test_gemm_seeded_ragged_walks(shape, call):
     ok, worst = oracle.gemm_check(out[:, :n], oracle.gemm_ref(a, af, b, bf, sa, sb),
                                   oracle.gemm_abs_ref(a, af, b, bf, sa, sb), coef)
     assert ok, f"{call} {af}x{bf} {shape}: worst |err|/bound {worst}"
+
+
+def _sweep_cases(count=40, seed=20261204):
+    """Seeded small shapes for a sweep of both GEMM modes: M, N in [1, 700), K a multiple of 16 up to
+    1024 (so one- and several-step K loops, whole and ragged last steps), a random format pair, and
+    operand and output rows padded by random multiples of 16 bytes; fixed by the seed."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        m, n = int(rng.integers(1, 700)), int(rng.integers(1, 700))
+        k = 16 * int(rng.integers(1, 65))
+        af, bf = PAIRS[int(rng.integers(0, len(PAIRS)))]
+        pads = tuple(16 * int(v) for v in rng.integers(0, 4, 3))
+        cases.append((m, n, k, af, bf) + pads)
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases())
+@pytest.mark.parametrize("call", ["exact", "fast"])
+def test_gemm_seeded_sweep(case, call):
+    """Every output against the oracle: the FP32 bound for the exact GEMM, the fast bound for the FP8
+    instruction; strided operands and output; nothing written past N."""
+    require_gpu()
+    from oracle.gemm import FAST_ACCUM_SUM_COEF
+    m, n, k, af, bf, pad_a, pad_b, pad_c = case
+    rng = np.random.default_rng([m, n, k, pad_a, pad_b, pad_c])
+    a_full = _codes(rng, (m, k + pad_a), af, spread=40)
+    b_full = _codes(rng, (n, k + pad_b), bf, spread=40)
+    sa, sb = np.float32(rng.uniform(0.25, 4.0)), np.float32(rng.uniform(0.25, 4.0))
+    f = fp8.fp8_scaled_gemm if call == "exact" else fp8.fp8_scaled_gemm_fast_accum
+    coef = oracle.gemm.SUM_COEF if call == "exact" else FAST_ACCUM_SUM_COEF
+    banner("gemm sweep", call, case)
+    c, store = pitched(m, n, torch.int16, fill=0x7FC1, pad_bytes=pad_c)
+    f(dev(a_full)[:, :k], af, dev(b_full)[:, :k], bf, f32(sa), f32(sb), c)
+    out = host(store)
+    assert (out[:, n:] == 0x7FC1).all(), "wrote past n"
+    a, b = a_full[:, :k], b_full[:, :k]
+    ok, worst = oracle.gemm_check(out[:, :n], oracle.gemm_ref(a, af, b, bf, sa, sb),
+                                  oracle.gemm_abs_ref(a, af, b, bf, sa, sb), coef)
+    assert ok, f"{call} sweep {case}: worst |err|/bound {worst}"
