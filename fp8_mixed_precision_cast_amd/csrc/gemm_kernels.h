@@ -509,7 +509,8 @@ __device__ __forceinline__ void exact_k_steps(uint8_t* s0, uint8_t* s1, int nk, 
     wr = t;
   }
   exact_chunk<GM, FA, FB, true>(r, acc, 3, [] {});
-  // the copy issued by the last body (of a step past K) may still be landing
+  // no copy of this tile is still in flight (each was waited for at the top of
+  // the body that reads it); the wait keeps the tile's end free of them
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 }
 
