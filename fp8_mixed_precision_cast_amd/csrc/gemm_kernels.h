@@ -9,12 +9,13 @@
 // registers (v_cvt_scalef32_pk_bf16_{fp8,bf8} with scale 1, exact for every
 // code) and runs v_mfma_f32_32x32x16_bf16, whose products are exact and whose
 // sums carry about 22 bits relative to sum|a*b| per instruction. gfx950's FP8
-// MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4 and the older fp8 forms) run twice
-// as fast but reduce each dot product with only about 17 bits relative to its
-// largest product (measured: up to 7e-5 of sum|a*b| per instruction), which
-// exceeds the tolerance on outputs that cancel, so the FP32-accumulation GEMM
-// does not use them. (The 16x16x32 BF16 form issues at half the 32x32x16
-// rate on gfx950.)
+// MFMAs reduce each dot product with only about 17 bits relative to its
+// largest product (measured: up to 7e-5 of sum|a*b| per instruction for the
+// f8f6f4 forms, which run at twice the MAC rate, and up to 3e-4 for the older
+// K = 16 fp8 forms, which run at this BF16 instruction's rate). That exceeds
+// the tolerance on outputs that cancel, so the FP32-accumulation GEMM does not
+// use them. (The 16x16x32 BF16 form issues at half the 32x32x16 rate on
+// gfx950.)
 //
 // Fast accumulation (ACC = kAccFast) is the opt-in alternative: the same
 // tiles, copies and epilogues, but the FP8 fragments go unwidened into
