@@ -15,9 +15,11 @@
 // K = 16 fp8 forms, which run at this BF16 instruction's rate). That exceeds
 // the tolerance on outputs that cancel, so the FP32-accumulation GEMM does not
 // use them. (The 16x16x32 BF16 form draws less power per product: in a
-// register-only loop it ran 14-23% faster than 32x32x16. With its lane layout
-// the operands of a 128 x 64 wave tile no longer fit next to the accumulators
-// at two waves per SIMD.)
+// register-only loop it ran 14-23% faster than 32x32x16. In this kernel its
+// lane layout costs more than that: read from LDS in 8-byte pieces, 16 rows
+// of one column share eight bank pairs; read in 16-byte pieces, or regrouped
+// from the 32 x 32 reads across lanes, the operands of a 128 x 64 wave tile
+// no longer fit beside the accumulators at two waves per SIMD.)
 //
 // Fast accumulation (ACC = kAccFast) is the opt-in alternative: the same
 // tiles, copies and epilogues, but the FP8 fragments go unwidened into
