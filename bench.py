@@ -10,10 +10,12 @@ K=4096; amax history 1024, margin 0).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload mlp7b_up_fwd]
 
-Prints one JSON line. After W warm-up steps the step is captured once as a HIP
-graph and replayed untimed for --settle-seconds (the GPU's power management
-dips a few milliseconds into a burst and settles within a second or two); then
-K replays are timed, synchronized on both sides: `value` is the step's GEMM
+Prints one JSON line. After W warm-up steps, --steps-per-graph consecutive
+steps (10 by default, fewer when that does not divide K) are captured as one
+HIP graph, as a training loop captures an iteration of many layers, and
+replayed untimed for --settle-seconds (the GPU's power management dips a few
+milliseconds into a burst and settles within a second or two); then K steps of
+replays are timed, synchronized on both sides: `value` is the step's GEMM
 FLOPs divided by that step time (TFLOP/s, higher is better; `--no-graph` times
 eager steps instead). K eager steps follow directly, with HIP events around
 every phase on the launch stream: they give `roofline` (the dominant kernel,
@@ -55,6 +57,9 @@ def parse():
     ap.add_argument("--gemm-accum", default="exact", choices=["exact", "fast"],
                     help="exact: FP32 accumulation (BF16 MFMA on exactly widened FP8); fast: the FP8 MFMA's own "
                          "reduced-precision accumulation (within 2^-9 of sum|a*b|)")
+    ap.add_argument("--steps-per-graph", type=int, default=10,
+                    help="consecutive steps captured in one HIP graph (the largest divisor of --steps up to this "
+                         "is used; 1 replays a one-step graph per step)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager steps only (by default the timed steps are replays of the step captured "
                          "as a HIP graph, after the eager steps that give the per-kernel figures)")
@@ -261,24 +266,30 @@ def cold_cast_gbps(plan, dinp, reps: int = 5):
     return plan.cast_bytes(dinp) / (ms * 1e-3) / 1e9, ms
 
 
-def settle(run_ten, seconds: float) -> int:
-    """Repeats the step (ten at a time) untimed for `seconds`; returns the number of steps run. A few
+def settle(run, steps_per_run: int, seconds: float) -> int:
+    """Calls run() (steps_per_run steps) untimed for `seconds`; returns the number of steps run. A few
     milliseconds into a burst of work the power controller lowers the clock below where it ends up
     after a second or two (per-dispatch traces show it), so the timed steps follow this directly."""
     import torch
     n = 0
     torch.cuda.synchronize()
     s0 = time.perf_counter()
-    while True:   # at least ten, so a captured graph has been replayed before it is timed
-        run_ten()
-        n += 10
+    while True:   # at least once, so a captured graph has been replayed before it is timed
+        run()
+        n += steps_per_run
         torch.cuda.synchronize()
         if time.perf_counter() - s0 >= seconds:
             return n
 
 
+def steps_per_graph(k: int, wanted: int) -> int:
+    """The largest divisor of k that is at most `wanted` (at least 1): the timed region then replays
+    whole graphs for exactly k steps."""
+    return max(d for d in range(1, max(1, min(k, wanted)) + 1) if k % d == 0)
+
+
 def graph_steps(g, steps: int):
-    """Replays the captured step `steps` times, synchronized on both sides. Returns (wall seconds per
+    """Replays the captured graph `steps` times, synchronized on both sides. Returns (wall seconds per
     replay, per-replay milliseconds from HIP events recorded between the replays on the launch
     stream)."""
     import torch
@@ -517,13 +528,17 @@ def main():
     # The timed steps: K replays of the step captured as a HIP graph (value, ms_per_step), right after
     # the settle replays; with --no-graph, K eager steps after eager settle steps. The K eager steps
     # with HIP events around every phase (roofline, components) follow directly.
+    spg = steps_per_graph(K, args.steps_per_graph)
     if args.no_graph:
         graph = None
-        settle_steps = settle(lambda: [plan.step(dinp) for _ in range(10)], args.settle_seconds)
+        settle_steps = settle(lambda: [plan.step(dinp) for _ in range(10)], 10, args.settle_seconds)
     else:
-        graph = plan.capture(dinp)
-        settle_steps = settle(lambda: [graph.replay() for _ in range(10)], args.settle_seconds)
-        graph_step_s, graph_ms = graph_steps(graph, K)
+        graph = plan.capture(dinp, steps=spg)
+        reps = max(1, 10 // spg)
+        settle_steps = settle(lambda: [graph.replay() for _ in range(reps)], reps * spg, args.settle_seconds)
+        graph_replay_s, graph_replay_ms = graph_steps(graph, K // spg)
+        graph_step_s = graph_replay_s / spg
+        graph_ms = [t / spg for t in graph_replay_ms]
     n_updates += settle_steps + (0 if args.no_graph else K)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
@@ -633,6 +648,7 @@ def main():
                    "recipe": args.recipe, "output_cast": args.output_cast, "layernorm_x": bool(args.layernorm),
                    "gemm_accum": args.gemm_accum,
                    "step_launch": "eager" if args.no_graph else "hip_graph",
+                   "steps_per_graph": None if args.no_graph else spg,
                    "settle_s": args.settle_seconds, "settle_steps": settle_steps,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,

@@ -223,16 +223,20 @@ class LayerPlan:
         self.output_cast_all(stream)
         self.update_all(stream)
 
-    def capture(self, inputs: Dict[str, torch.Tensor]) -> "torch.cuda.CUDAGraph":
-        """One step captured as a HIP graph (through torch's graph API): replaying it runs the step's
-        launches without host launch overhead or gaps between kernels. The graph reads `inputs` and
-        writes the plan's buffers at the addresses they have now; every replay advances the recipe by
-        one step, like step(). The step issues only kernel launches (no memset or copy nodes). Call
-        prime() (and, for the batched cast, one eager step) first, so nothing is allocated during
-        capture."""
+    def capture(self, inputs: Dict[str, torch.Tensor], steps: int = 1) -> "torch.cuda.CUDAGraph":
+        """`steps` consecutive steps captured as one HIP graph (through torch's graph API): replaying it
+        runs their launches without host launch overhead or gaps between kernels. The graph reads
+        `inputs` and writes the plan's buffers at the addresses they have now; every replay advances the
+        recipe by `steps` steps, like that many calls of step(). A training loop captures a whole
+        iteration (many layers) the same way, so the cost of launching a graph is spread over them.
+        The step issues only kernel launches (no memset or copy nodes). Call prime() (and, for the
+        batched cast, one eager step) first, so nothing is allocated during capture."""
+        if steps < 1:
+            raise ValueError("steps must be at least 1")
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step(inputs)
+            for _ in range(steps):
+                self.step(inputs)
         return g
 
     def gemm_operands(self) -> List[tuple]:

@@ -18,8 +18,20 @@ def test_help_lists_the_workload_switches():
                        timeout=120)
     assert r.returncode == 0
     for flag in ("--steps", "--warmup", "--workload", "--recipe", "--output-cast", "--layernorm", "--gemm-accum", "--no-graph", "--gemm-data",
-                 "--copy-reference"):
+                 "--copy-reference", "--steps-per-graph"):
         assert flag in r.stdout
+
+
+def test_steps_per_graph_divides_the_timed_steps():
+    """The timed region replays whole graphs: the steps per graph is the largest divisor of --steps not above
+    the request, so exactly --steps steps are timed."""
+    import bench
+    assert [bench.steps_per_graph(k, 10) for k in (1, 2, 3, 7, 12, 20, 50, 97, 100)] == [1, 2, 3, 7, 6, 10, 10, 1, 10]
+    assert bench.steps_per_graph(20, 1) == 1 and bench.steps_per_graph(20, 0) == 1
+    for k in range(1, 60):
+        for want in range(1, 15):
+            d = bench.steps_per_graph(k, want)
+            assert k % d == 0 and 1 <= d <= max(1, want)
 
 
 def test_source_digest_ignores_comments_and_whitespace_only():

@@ -40,7 +40,7 @@ def test_bench_line_contract(monkeypatch, capsys):
     assert par["checked"][-1]["fp32_bound_ok"]
     clk = line["clocks"]
     assert clk is not None and ("sclk_mhz" in clk or "error" in clk)
-    assert line["config"]["step_launch"] == "hip_graph"
+    assert line["config"]["step_launch"] == "hip_graph" and line["config"]["steps_per_graph"] == 2
     assert 0 < line["ms_per_step"] and 0 < line["components"]["eager_ms_per_step"]
     (eager,) = _run(monkeypatch, capsys, "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--no-graph")
     assert eager["config"]["step_launch"] == "eager"
