@@ -46,11 +46,17 @@ __device__ __forceinline__ uint32_t flat_tail(const void* __restrict__ x, uint8_
 // Contiguous BF16 source: each thread converts kFlatUnroll chunks of 16
 // elements per iteration (two 16-byte loads -> one 16-byte store per chunk);
 // all loads of an iteration are issued before any conversion. The source is
-// read non-temporally; the codes are cached for the GEMM that follows.
+// read non-temporally; the codes are cached for the GEMM that follows. The
+// magnitude max of an iteration's sources also tells whether any is NaN: when
+// no lane of the wave has one (and s is finite and nonzero), no product can
+// be NaN and the codes skip the NaN checks.
 template <int FMT, bool HAS_Q>
 __device__ __forceinline__ uint32_t flat_bf16_body(const uint4* __restrict__ x, uint4* __restrict__ q,
                                                    int64_t nchunk, float s, int64_t block, int64_t nblocks) {
   uint32_t acc = 0;
+  // no product x * s can be NaN when no source is NaN and s is finite and nonzero
+  const uint32_t sbits = __float_as_uint(s) & 0x7FFFFFFFu;
+  const bool s_ok = sbits != 0u && sbits < 0x7F800000u;
   const int64_t stride = nblocks * kFlatBlock;
   for (int64_t base = block * kFlatBlock + threadIdx.x; base < nchunk; base += kFlatUnroll * stride) {
     u32x4 a[kFlatUnroll], b[kFlatUnroll];
@@ -73,19 +79,37 @@ __device__ __forceinline__ uint32_t flat_bf16_body(const uint4* __restrict__ x, 
         b[u] = a[u];
       }
     }
+    uint32_t m = 0;
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
-      acc = amax_bf16x2(acc, a[u].x); acc = amax_bf16x2(acc, a[u].y);
-      acc = amax_bf16x2(acc, a[u].z); acc = amax_bf16x2(acc, a[u].w);
-      acc = amax_bf16x2(acc, b[u].x); acc = amax_bf16x2(acc, b[u].y);
-      acc = amax_bf16x2(acc, b[u].z); acc = amax_bf16x2(acc, b[u].w);
-      if constexpr (HAS_Q) {
-        const int64_t i = base + u * stride;
-        if (i < nchunk) {
-          u32x4 o;
-          o.x = enc4_bf16<FMT>(a[u].x, a[u].y, s); o.y = enc4_bf16<FMT>(a[u].z, a[u].w, s);
-          o.z = enc4_bf16<FMT>(b[u].x, b[u].y, s); o.w = enc4_bf16<FMT>(b[u].z, b[u].w, s);
-          *(reinterpret_cast<u32x4*>(q) + i) = o;
+      m = amax_bf16x2(m, a[u].x); m = amax_bf16x2(m, a[u].y);
+      m = amax_bf16x2(m, a[u].z); m = amax_bf16x2(m, a[u].w);
+      m = amax_bf16x2(m, b[u].x); m = amax_bf16x2(m, b[u].y);
+      m = amax_bf16x2(m, b[u].z); m = amax_bf16x2(m, b[u].w);
+    }
+    acc = amax_bf16x2(acc, m);
+    if constexpr (HAS_Q) {
+      if (__all(s_ok && (m & 0xFFFFu) <= 0x7F80u && (m >> 16) <= 0x7F80u)) {
+#pragma unroll
+        for (int u = 0; u < kFlatUnroll; ++u) {
+          const int64_t i = base + u * stride;
+          if (i < nchunk) {
+            u32x4 o;
+            o.x = enc4_bf16_nonan<FMT>(a[u].x, a[u].y, s); o.y = enc4_bf16_nonan<FMT>(a[u].z, a[u].w, s);
+            o.z = enc4_bf16_nonan<FMT>(b[u].x, b[u].y, s); o.w = enc4_bf16_nonan<FMT>(b[u].z, b[u].w, s);
+            *(reinterpret_cast<u32x4*>(q) + i) = o;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kFlatUnroll; ++u) {
+          const int64_t i = base + u * stride;
+          if (i < nchunk) {
+            u32x4 o;
+            o.x = enc4_bf16<FMT>(a[u].x, a[u].y, s); o.y = enc4_bf16<FMT>(a[u].z, a[u].w, s);
+            o.z = enc4_bf16<FMT>(b[u].x, b[u].y, s); o.w = enc4_bf16<FMT>(b[u].z, b[u].w, s);
+            *(reinterpret_cast<u32x4*>(q) + i) = o;
+          }
         }
       }
     }
