@@ -60,6 +60,26 @@ def test_all_bf16_patterns_at_many_scales(fmt):
         assert am == 0x7FC00000   # the patterns include NaNs
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_zero_infinite_and_nan_scales_without_nan_sources(fmt):
+    """Every BF16 pattern except the NaNs (so no source forces the NaN checks), at scales for which
+    0 * Inf or a NaN scale makes some products NaN: 0 * Inf and Inf * 0 give the NaN code with the
+    product's sign, and a NaN scale gives it for every element. The cast may skip its NaN checks only
+    when the scale is finite and nonzero; here every product has to take them."""
+    require_gpu()
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[(pats & 0x7FFF) <= 0x7F80]                       # no NaN sources
+    x = np.zeros(256 * 256, dtype=np.uint16)
+    x[: pats.size] = pats
+    x = x.reshape(256, 256)
+    for s in (0.0, -0.0, float("inf"), float("-inf"), float("nan"), 1.5):
+        banner("no-NaN sources", fmt, s)
+        q, _, am = _run_cast(x, "bf16", fmt, s)
+        want = oracle.cast(x, np.float32(s), fmt, "bf16")
+        assert np.array_equal(q, want), f"scale {s}: {first_diff(q, want)}"
+        assert am == 0x7F800000   # the sources' magnitude max is Inf
+
+
 def _boundary_f32(fmt):
     """fp32 values at, just above and just below every rounding boundary of the format."""
     t = decode_table(fmt)
